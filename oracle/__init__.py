@@ -1,0 +1,159 @@
+"""CPU oracle of the SageAttention 8-bit attention forward (ctypes over oracle.c).
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this package; the GPU product path never does.
+
+Every function works on numpy arrays.  Tensors are [B, H, N, d] fp16 (numpy
+float16), as the GPU path takes them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared", "-pthread"]
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile oracle.c with gcc (no fast-math, no contraction)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, src, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load an oracle library (the default build, or another path for tests)."""
+    if path is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        path = _LIB
+    lib = ctypes.CDLL(path)
+    p, i, d, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+    lib.oracle_attn_rows.argtypes = [p, p, p, i, i, i, i, i, d, i, i, i, i, i, i, i, p, p, i, p, i, p]
+    lib.oracle_attn_rows.restype = i
+    lib.oracle_quant.argtypes = [p, p, p, i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p]
+    lib.oracle_quant.restype = i
+    lib.oracle_qk_int32.argtypes = [p, p, i, i, i, i, i, i, p]
+    lib.oracle_qk_int32.restype = i
+    lib.oracle_pad_len.argtypes = [i]
+    lib.oracle_pad_len.restype = i
+    for name in ("oracle_f16_decode_n", "oracle_f16_encode_n", "oracle_e4m3_decode_n",
+                 "oracle_e4m3_encode_n"):
+        getattr(lib, name).argtypes = [p, sz, p]
+        getattr(lib, name).restype = None
+    return lib
+
+
+class Oracle:
+    """Thin numpy front end of one oracle library."""
+
+    def __init__(self, path: str | None = None):
+        self.lib = load(path)
+
+    # ---- number formats
+    def f16_decode(self, codes: np.ndarray) -> np.ndarray:
+        c = np.ascontiguousarray(codes, dtype=np.uint16)
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_f16_decode_n(c.ctypes.data, c.size, out.ctypes.data)
+        return out
+
+    def f16_encode(self, x: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.oracle_f16_encode_n(a.ctypes.data, a.size, out.ctypes.data)
+        return out
+
+    def e4m3_decode(self, codes: np.ndarray) -> np.ndarray:
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_e4m3_decode_n(c.ctypes.data, c.size, out.ctypes.data)
+        return out
+
+    def e4m3_encode(self, x: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint8)
+        self.lib.oracle_e4m3_encode_n(a.ctypes.data, a.size, out.ctypes.data)
+        return out
+
+    def pad_len(self, N: int) -> int:
+        return self.lib.oracle_pad_len(N)
+
+    # ---- steps 1-3
+    def quant(self, q, k, v=None, blk_q=128, blk_k=64, smooth_k=1, smooth_q=0, with_v=False) -> dict:
+        q = _f16(q)
+        k = _f16(k)
+        B, H, N, d = q.shape
+        G, Np = B * H, self.pad_len(N)
+        nqb, nkb = -(-N // blk_q), -(-N // blk_k)
+        r = dict(q_i8=np.empty((B, H, Np, d), np.int8), k_i8=np.empty((B, H, Np, d), np.int8),
+                 q_scale=np.empty((B, H, nqb), np.float32), k_scale=np.empty((B, H, nkb), np.float32),
+                 k_mean=np.empty((B, H, d), np.float32), q_mean=np.empty((B, H, nqb, d), np.float32))
+        vp = 0
+        if with_v:
+            v = _f16(v)
+            r["v_f8"] = np.empty((B, H, d, Np), np.uint8)
+            r["v_scale"] = np.empty((B, H, d), np.float32)
+            vp = v.ctypes.data
+        rc = self.lib.oracle_quant(
+            q.ctypes.data, k.ctypes.data, vp, B, H, N, d, blk_q, blk_k, smooth_k, smooth_q,
+            r["q_i8"].ctypes.data, r["k_i8"].ctypes.data, r["q_scale"].ctypes.data,
+            r["k_scale"].ctypes.data, r["k_mean"].ctypes.data, r["q_mean"].ctypes.data,
+            r["v_f8"].ctypes.data if with_v else None, r["v_scale"].ctypes.data if with_v else None)
+        if rc:
+            raise ValueError("oracle_quant: bad arguments")
+        return r
+
+    # ---- step 4
+    def qk_int32(self, q_i8_head, k_i8_head, r0, nr, c0, nc) -> np.ndarray:
+        a = np.ascontiguousarray(q_i8_head, dtype=np.int8)
+        b = np.ascontiguousarray(k_i8_head, dtype=np.int8)
+        Np, d = a.shape
+        out = np.empty((nr, nc), np.int32)
+        if self.lib.oracle_qk_int32(a.ctypes.data, b.ctypes.data, Np, d, r0, nr, c0, nc, out.ctypes.data):
+            raise ValueError("oracle_qk_int32: bad arguments")
+        return out
+
+    # ---- steps 1-9 for chosen rows
+    def attn_rows(self, q, k, v, heads, rows, causal=0, sm_scale=None, variant=0, blk_q=128,
+                  blk_k=64, bkv=64, smooth_k=1, smooth_q=None, exact=0, nthreads=0):
+        """O (fp64, before the fp16 rounding) for rows[i] of flat head heads[i]."""
+        q, k, v = _f16(q), _f16(k), _f16(v)
+        B, H, N, d = q.shape
+        if sm_scale is None:
+            sm_scale = 1.0 / np.sqrt(d)
+        if smooth_q is None:
+            smooth_q = 1 if variant == 1 else 0
+        heads = np.ascontiguousarray(heads, dtype=np.int32)
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        out = np.empty((heads.size, d), np.float64)
+        used = ctypes.c_int(0)
+        rc = self.lib.oracle_attn_rows(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d, causal, float(sm_scale), variant,
+            blk_q, blk_k, bkv, smooth_k, smooth_q, exact, heads.ctypes.data, rows.ctypes.data,
+            heads.size, out.ctypes.data, nthreads, ctypes.byref(used))
+        if rc:
+            raise ValueError("oracle_attn_rows: bad arguments")
+        self.threads_used = used.value
+        return out
+
+    def attn(self, q, k, v, **kw) -> np.ndarray:
+        """O for every row, [B, H, N, d] fp64."""
+        B, H, N, d = q.shape
+        heads = np.repeat(np.arange(B * H, dtype=np.int32), N)
+        rows = np.tile(np.arange(N, dtype=np.int32), B * H)
+        return self.attn_rows(q, k, v, heads, rows, **kw).reshape(B, H, N, d)
+
+
+def _f16(x) -> np.ndarray:
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.float16:
+        raise TypeError(f"expected float16, got {a.dtype}")
+    return a

@@ -1,0 +1,529 @@
+/*
+ * oracle.c -- plain, slow CPU oracle of the SageAttention 8-bit attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this library.  The GPU product
+ * path never links, imports or calls it, and shares no code with it.
+ *
+ * Sources (titles of the pages this follows):
+ *  [SA-sum]  "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+ *            Acceleration" (research summary page): sections "Summary",
+ *            "Key points", "Interesting ideas" I1-I5.
+ *  [SA2]     "SageAttention2: Efficient Attention with Thorough Outlier Smoothing
+ *            and Per-thread INT4 Quantization" (ICML 2025 abstract), and the
+ *            arXiv 2411.10958 abstract of SageAttention2.
+ *  [FA]      FlashAttention / FlashAttention-2 and "Online normalizer calculation
+ *            for softmax", entries of the reference list on the [SA-sum] page.
+ *
+ * What it computes, per (batch b, head h), in the order of the method:
+ *   1. k_mean[c] = mean over the N tokens of K[:, c]          ([SA-sum] I1)
+ *   2. K' = K - k_mean (fp32); Q' = Q - q_mean(block) when Q smoothing is on ([SA2])
+ *   3. per-block symmetric INT8 quantisation of Q', K' with one fp32 scale per block
+ *   4. S = Qhat Khat^T with exact integer accumulation
+ *   5. s = sm_scale * dQ * dK * S  (+ sm_scale * dK * (q_mean . Khat_j) with Q smoothing)
+ *   6. causal / sequence-end mask
+ *   7. online softmax over key tiles of `bkv` keys in ascending order ([FA])
+ *   8. P~ V: P~ rounded to fp16 (variant 0) or P~*448 to FP8 E4M3 with V in
+ *      per-channel-scaled FP8 and a fresh accumulator per tile (variant 1, [SA2]
+ *      "two-level accumulation")
+ *   9. O / l (variant 1 also * dV / 448)
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - means are exact: fp16 inputs are integer multiples of 2^-24, so the token
+ *    sum is an exact int64; the mean is (float)((double)sum / (N * 2^24)).
+ *  - scale = absmax / 127 (fp32), codes = rint(x' * (127 / absmax)) clamped to
+ *    [-127, 127] (round half to even); an all-zero block gets scale 0 and codes 0.
+ *  - sm_scale is applied at dequantisation, never folded into Q before quantising.
+ *  - the Q-smoothing term is dK_j * (q_mean . Khat_j), i.e. it uses the
+ *    dequantised smoothed K.
+ *  - l sums the unrounded P~ (fp64 here).
+ *  - P~ in FP8 uses the static scale 448 (P~ <= 1 after max subtraction).
+ *  - V in FP8: per channel, scale = absmax_t |V[t, c]| / 448, codes =
+ *    E4M3FN(V * (448 / absmax)) rounded to nearest even after clamping to +-448.
+ *
+ * Floating-point decisions that produce integer codes (int8 Q/K codes, fp8 V
+ * codes) are taken in fp32, the precision the GPU kernels use.  Everything else
+ * (scores, exponentials, sums, O) is fp64.
+ *
+ * Build: gcc -O2 -ffp-contract=off -std=c11 -fPIC -shared -pthread (no fast-math).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* IEEE binary16 -> double (exact). */
+double oracle_f16_decode(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+/* double -> IEEE binary16, round to nearest, ties to even. */
+uint16_t oracle_f16_encode(double x) {
+  uint16_t s = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return (uint16_t)(s | 0x7e00);
+  double a = fabs(x);
+  if (a >= 65520.0) return (uint16_t)(s | 0x7c00); /* rounds to infinity */
+  if (a < 0x1.0p-14) {                              /* subnormal range, quantum 2^-24 */
+    double q = nearbyint(ldexp(a, 24));             /* 0..1024; 1024 encodes 2^-14 */
+    return (uint16_t)(s | (uint16_t)q);
+  }
+  int e;
+  frexp(a, &e);                                     /* a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  double q = nearbyint(ldexp(a, 10 - E));           /* 1024..2048 */
+  if (q == 2048.0) { q = 1024.0; E += 1; }
+  if (E > 15) return (uint16_t)(s | 0x7c00);
+  return (uint16_t)(s | ((E + 15) << 10) | ((int)q - 1024));
+}
+
+/* OCP FP8 E4M3FN: bias 7, no infinities, S.1111.111 is NaN, max 448. */
+double oracle_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/* double -> E4M3FN, round to nearest even, saturating at +-448, sign of zero kept. */
+uint8_t oracle_e4m3_encode(double x) {
+  uint8_t s = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return (uint8_t)(s | 0x7f);
+  double a = fabs(x);
+  if (a >= 448.0) return (uint8_t)(s | 0x7e);
+  if (a < 0x1.0p-6) {                 /* subnormals: quantum 2^-9 */
+    double q = nearbyint(ldexp(a, 9)); /* 0..8; 8 encodes 2^-6 */
+    return (uint8_t)(s | (uint8_t)q);
+  }
+  int e;
+  frexp(a, &e);
+  int E = e - 1;                      /* a in [2^E, 2^(E+1)), -6 <= E <= 8 */
+  double q = nearbyint(ldexp(a, 3 - E)); /* 8..16 */
+  if (q == 16.0) { q = 8.0; E += 1; }
+  /* a < 448 keeps the result at or below 448 = code 0x7e */
+  return (uint8_t)(s | ((E + 7) << 3) | ((int)q - 8));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 1-3: means, smoothing, per-block INT8 quantisation                  */
+/* ------------------------------------------------------------------------ */
+
+/* Exact mean over rows [r0, r1) of channel c of one head x[N][d] (fp16 bits).
+ * Every fp16 value times 2^24 is an integer, so the int64 sum is exact and
+ * independent of order; one rounding to double, one to float. */
+static float exact_mean(const uint16_t* x, int d, int r0, int r1, int c) {
+  int64_t acc = 0;
+  for (int t = r0; t < r1; ++t) acc += (int64_t)ldexp(oracle_f16_decode(x[(size_t)t * d + c]), 24);
+  return (float)((double)acc / ((double)(r1 - r0) * 16777216.0));
+}
+
+/* Symmetric INT8 quantisation of one block of n fp32 values (the values are
+ * already smoothed).  Returns the scale; writes codes. */
+static float quant_block_i8(const float* xs, size_t n, int8_t* out) {
+  float a = 0.0f;
+  for (size_t i = 0; i < n; ++i) a = fmaxf(a, fabsf(xs[i]));
+  if (a == 0.0f) {
+    memset(out, 0, n);
+    return 0.0f;
+  }
+  float r = 127.0f / a;
+  for (size_t i = 0; i < n; ++i) {
+    float t = rintf(xs[i] * r);
+    if (t > 127.0f) t = 127.0f;
+    if (t < -127.0f) t = -127.0f;
+    out[i] = (int8_t)t;
+  }
+  return a / 127.0f;
+}
+
+/* Quantise one head's [N][d] tensor in blocks of `blk` rows.
+ *  mean_mode 0: no smoothing; 1: subtract the mean over all N tokens
+ *  (k_mean[d] written); 2: subtract the mean of each block (blk_mean
+ *  [nblk][d] written).  out is [Np][d] with rows >= N zero.  scale[nblk]. */
+static void quant_head(const uint16_t* x, int N, int Np, int d, int blk, int mean_mode,
+                       int8_t* out, float* scale, float* k_mean, float* blk_mean) {
+  int nblk = (N + blk - 1) / blk;
+  float* mean = (float*)malloc(sizeof(float) * (size_t)d);
+  float* buf = (float*)malloc(sizeof(float) * (size_t)blk * d);
+  if (mean_mode == 1) {
+    for (int c = 0; c < d; ++c) mean[c] = exact_mean(x, d, 0, N, c);
+    if (k_mean) memcpy(k_mean, mean, sizeof(float) * (size_t)d);
+  }
+  for (int b = 0; b < nblk; ++b) {
+    int r0 = b * blk, r1 = r0 + blk < N ? r0 + blk : N;
+    if (mean_mode == 2) {
+      for (int c = 0; c < d; ++c) mean[c] = exact_mean(x, d, r0, r1, c);
+      if (blk_mean) memcpy(blk_mean + (size_t)b * d, mean, sizeof(float) * (size_t)d);
+    }
+    for (int t = r0; t < r1; ++t)
+      for (int c = 0; c < d; ++c) {
+        float v = (float)oracle_f16_decode(x[(size_t)t * d + c]);
+        buf[(size_t)(t - r0) * d + c] = mean_mode ? v - mean[c] : v;
+      }
+    scale[b] = quant_block_i8(buf, (size_t)(r1 - r0) * d, out + (size_t)r0 * d);
+  }
+  memset(out + (size_t)N * d, 0, (size_t)(Np - N) * d);
+  free(mean);
+  free(buf);
+}
+
+/* V in FP8 for one head: per-channel scale absmax / 448, codes transposed to
+ * vt[d][Np] (columns >= N zero). */
+static void quant_v_head(const uint16_t* v, int N, int Np, int d, uint8_t* vt, float* vscale) {
+  for (int c = 0; c < d; ++c) {
+    float a = 0.0f;
+    for (int t = 0; t < N; ++t) a = fmaxf(a, fabsf((float)oracle_f16_decode(v[(size_t)t * d + c])));
+    uint8_t* row = vt + (size_t)c * Np;
+    memset(row, 0, (size_t)Np);
+    if (a == 0.0f) {
+      vscale[c] = 0.0f;
+      continue;
+    }
+    float r = 448.0f / a;
+    for (int t = 0; t < N; ++t) {
+      float y = (float)oracle_f16_decode(v[(size_t)t * d + c]) * r;
+      if (y > 448.0f) y = 448.0f;
+      if (y < -448.0f) y = -448.0f;
+      row[t] = oracle_e4m3_encode((double)y);
+    }
+    vscale[c] = a / 448.0f;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Parameters and per-head preparation                                      */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int B, H, N, d, causal, variant;
+  int blk_q, blk_k, bkv;
+  int smooth_k, smooth_q;
+  int exact;      /* 1: no quantisation at all, fp64 everywhere (pins the online softmax) */
+  double sm_scale;
+} params_t;
+
+int oracle_pad_len(int N) { return (N + 127) / 128 * 128; }
+
+typedef struct {
+  int8_t *qi, *ki;   /* [Np][d] */
+  float *qs, *ks;    /* per block */
+  float *kmean;      /* [d] */
+  float *qmean;      /* [nqb][d] (only with smooth_q) */
+  uint8_t* vt;       /* [d][Np] (variant 1) */
+  float* vs;         /* [d] (variant 1) */
+} prep_t;
+
+static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      prep_t* h) {
+  int N = P->N, d = P->d, Np = oracle_pad_len(N);
+  int nqb = (N + P->blk_q - 1) / P->blk_q, nkb = (N + P->blk_k - 1) / P->blk_k;
+  memset(h, 0, sizeof(*h));
+  if (P->exact) return;
+  h->qi = (int8_t*)malloc((size_t)Np * d);
+  h->ki = (int8_t*)malloc((size_t)Np * d);
+  h->qs = (float*)malloc(sizeof(float) * (size_t)nqb);
+  h->ks = (float*)malloc(sizeof(float) * (size_t)nkb);
+  h->kmean = (float*)calloc((size_t)d, sizeof(float));
+  h->qmean = (float*)calloc((size_t)nqb * d, sizeof(float));
+  quant_head(k, N, Np, d, P->blk_k, P->smooth_k ? 1 : 0, h->ki, h->ks, h->kmean, NULL);
+  quant_head(q, N, Np, d, P->blk_q, P->smooth_q ? 2 : 0, h->qi, h->qs, NULL, h->qmean);
+  if (P->variant == 1) {
+    h->vt = (uint8_t*)malloc((size_t)d * Np);
+    h->vs = (float*)malloc(sizeof(float) * (size_t)d);
+    quant_v_head(v, N, Np, d, h->vt, h->vs);
+  }
+}
+
+static void free_prep(prep_t* h) {
+  free(h->qi); free(h->ki); free(h->qs); free(h->ks); free(h->kmean); free(h->qmean);
+  free(h->vt); free(h->vs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Steps 4-9 for one query row                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Exact integer dot product of two int8 rows. */
+static int32_t dot_i8(const int8_t* a, const int8_t* b, int d) {
+  int32_t s = 0;
+  for (int c = 0; c < d; ++c) s += (int32_t)a[c] * (int32_t)b[c];
+  return s;
+}
+
+/* O row i of one head (fp64, before the final fp16 rounding).
+ * work: 3 * bkv doubles of scratch. */
+static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, int i, double* o, double* work) {
+  const int N = P->N, d = P->d, bkv = P->bkv, Np = oracle_pad_len(N);
+  double* s = work;            /* scores of the tile */
+  double* p = work + bkv;      /* P~ of the tile */
+  double* inner = work + 2 * bkv; /* variant 1: the per-tile accumulator, d entries */
+  const int qb = i / P->blk_q;
+  double m = -INFINITY, l = 0.0;
+  for (int c = 0; c < d; ++c) o[c] = 0.0;
+
+  /* Q-smoothing term depends on the key only (per query block). */
+  const float* qm = (P->smooth_q && !P->exact) ? h->qmean + (size_t)qb * d : NULL;
+
+  for (int j0 = 0; j0 < N; j0 += bkv) {
+    if (P->causal && j0 > i) break; /* every key of this and later tiles is masked */
+    int j1 = j0 + bkv < N ? j0 + bkv : N;
+    double tmax = -INFINITY;
+    for (int j = j0; j < j1; ++j) {
+      double sj;
+      if (P->causal && j > i) {
+        sj = -INFINITY;
+      } else if (P->exact) {
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c)
+          acc += oracle_f16_decode(q[(size_t)i * d + c]) * oracle_f16_decode(k[(size_t)j * d + c]);
+        sj = P->sm_scale * acc;
+      } else {
+        int32_t S = dot_i8(h->qi + (size_t)i * d, h->ki + (size_t)j * d, d);
+        double dk = (double)h->ks[j / P->blk_k];
+        sj = P->sm_scale * (double)h->qs[qb] * dk * (double)S;
+        if (qm) {
+          double ds = 0.0;
+          for (int c = 0; c < d; ++c) ds += (double)qm[c] * (double)h->ki[(size_t)j * d + c];
+          sj += P->sm_scale * dk * ds;
+        }
+      }
+      s[j - j0] = sj;
+      if (sj > tmax) tmax = sj;
+    }
+    double mnew = m > tmax ? m : tmax;
+    double alpha;
+    if (mnew == -INFINITY) {
+      alpha = 1.0;
+      for (int j = j0; j < j1; ++j) p[j - j0] = 0.0;
+    } else {
+      alpha = exp(m - mnew); /* m = -inf gives 0 */
+      for (int j = j0; j < j1; ++j) p[j - j0] = exp(s[j - j0] - mnew);
+    }
+    double psum = 0.0;
+    for (int j = j0; j < j1; ++j) psum += p[j - j0];
+    l = alpha * l + psum;
+
+    if (P->exact) {
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_f16_decode(v[(size_t)j * d + c]);
+        o[c] = alpha * o[c] + acc;
+      }
+    } else if (P->variant == 0) {
+      /* P~ rounded to fp16, V in fp16, wide accumulation */
+      for (int j = j0; j < j1; ++j) p[j - j0] = oracle_f16_decode(oracle_f16_encode(p[j - j0]));
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_f16_decode(v[(size_t)j * d + c]);
+        o[c] = alpha * o[c] + acc;
+      }
+    } else {
+      /* P~ * 448 in FP8, V in FP8; fresh accumulator for the tile, then the
+       * outer buffer is rescaled and the tile's sum added (two-level). */
+      for (int j = j0; j < j1; ++j) p[j - j0] = oracle_e4m3_decode(oracle_e4m3_encode(p[j - j0] * 448.0));
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        const uint8_t* vrow = h->vt + (size_t)c * Np;
+        for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_e4m3_decode(vrow[j]);
+        inner[c] = acc;
+      }
+      for (int c = 0; c < d; ++c) o[c] = alpha * o[c] + inner[c];
+    }
+    m = mnew;
+  }
+  if (P->exact || P->variant == 0) {
+    for (int c = 0; c < d; ++c) o[c] = o[c] / l;
+  } else {
+    for (int c = 0; c < d; ++c) o[c] = o[c] * (double)h->vs[c] / (448.0 * l);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Threading over work items                                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const params_t* P;
+  const uint16_t *q, *k, *v;
+  prep_t* preps;        /* one per head slot */
+  const int* head_slot; /* item -> prep index */
+  const int* heads;     /* item -> b*H+h */
+  const int* rows;      /* item -> row */
+  int n_items;
+  double* out;          /* [n_items][d] */
+  int next;
+  pthread_mutex_t mu;
+} job_t;
+
+static void* worker(void* arg) {
+  job_t* J = (job_t*)arg;
+  const params_t* P = J->P;
+  size_t hs = (size_t)P->N * P->d;
+  double* work = (double*)malloc(sizeof(double) * (size_t)(2 * P->bkv + P->d));
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int it = J->next;
+    J->next += 16;
+    pthread_mutex_unlock(&J->mu);
+    if (it >= J->n_items) break;
+    int end = it + 16 < J->n_items ? it + 16 : J->n_items;
+    for (; it < end; ++it) {
+      size_t g = (size_t)J->heads[it];
+      attn_row(P, &J->preps[J->head_slot[it]], J->q + g * hs, J->k + g * hs, J->v + g * hs,
+               J->rows[it], J->out + (size_t)it * P->d, work);
+    }
+  }
+  free(work);
+  return NULL;
+}
+
+typedef struct {
+  const params_t* P;
+  const uint16_t *q, *k, *v;
+  prep_t* preps;
+  const int* uheads;
+  int n;
+  int next;
+  pthread_mutex_t mu;
+} prepjob_t;
+
+static void* prep_worker(void* arg) {
+  prepjob_t* J = (prepjob_t*)arg;
+  size_t hs = (size_t)J->P->N * J->P->d;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int it = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (it >= J->n) break;
+    size_t g = (size_t)J->uheads[it];
+    prep_head(J->P, J->q + g * hs, J->k + g * hs, J->v + g * hs, &J->preps[it]);
+  }
+  return NULL;
+}
+
+static int pick_threads(int want) {
+  if (want > 0) return want;
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+static int check_params(const params_t* P) {
+  if (P->B < 1 || P->H < 1 || P->N < 1 || P->d < 1) return -1;
+  if (P->blk_q < 1 || P->blk_k < 1 || P->bkv < 1) return -1;
+  if (P->causal != 0 && P->causal != 1) return -1;
+  if (P->variant != 0 && P->variant != 1) return -1;
+  if (!(P->sm_scale > 0.0) || !isfinite(P->sm_scale)) return -1;
+  if ((int64_t)P->d * 127 * 127 > 2147483647LL) return -1; /* int32 bound of S */
+  return 0;
+}
+
+/*
+ * O for a list of (head, row) items.
+ *  q, k, v: [B*H][N][d] fp16 bits.  heads[i] in [0, B*H), rows[i] in [0, N).
+ *  out: [n_items][d] fp64 (before rounding to fp16).
+ *  Returns 0, or -1 on bad arguments.  nthreads <= 0 uses every online core;
+ *  the count actually used is written to *threads_used when non-NULL.
+ */
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N,
+                     int d, int causal, double sm_scale, int variant, int blk_q, int blk_k, int bkv,
+                     int smooth_k, int smooth_q, int exact, const int* heads, const int* rows,
+                     int n_items, double* out, int nthreads, int* threads_used) {
+  params_t P = {B, H, N, d, causal, variant, blk_q, blk_k, bkv, smooth_k, smooth_q, exact, sm_scale};
+  if (check_params(&P)) return -1;
+  for (int i = 0; i < n_items; ++i)
+    if (heads[i] < 0 || heads[i] >= B * H || rows[i] < 0 || rows[i] >= N) return -1;
+  /* unique heads, in order of first appearance */
+  int G = B * H;
+  int* slot_of = (int*)malloc(sizeof(int) * (size_t)G);
+  int* uheads = (int*)malloc(sizeof(int) * (size_t)(n_items > 0 ? n_items : 1));
+  int* head_slot = (int*)malloc(sizeof(int) * (size_t)(n_items > 0 ? n_items : 1));
+  for (int g = 0; g < G; ++g) slot_of[g] = -1;
+  int nu = 0;
+  for (int i = 0; i < n_items; ++i) {
+    if (slot_of[heads[i]] < 0) { slot_of[heads[i]] = nu; uheads[nu++] = heads[i]; }
+    head_slot[i] = slot_of[heads[i]];
+  }
+  prep_t* preps = (prep_t*)calloc((size_t)(nu > 0 ? nu : 1), sizeof(prep_t));
+  int nt = pick_threads(nthreads);
+  if (threads_used) *threads_used = nt;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+
+  prepjob_t PJ = {&P, q, k, v, preps, uheads, nu, 0, PTHREAD_MUTEX_INITIALIZER};
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, prep_worker, &PJ);
+  for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+
+  job_t J = {&P, q, k, v, preps, head_slot, heads, rows, n_items, out, 0, PTHREAD_MUTEX_INITIALIZER};
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, worker, &J);
+  for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+
+  for (int u = 0; u < nu; ++u) free_prep(&preps[u]);
+  free(preps); free(th); free(slot_of); free(uheads); free(head_slot);
+  return 0;
+}
+
+/*
+ * Quantised tensors of steps 1-3 (and the FP8 V of variant 1) for all heads.
+ *  q_i8, k_i8: [G][Np][d];  q_scale [G][nqb], k_scale [G][nkb];  k_mean [G][d];
+ *  q_mean [G][nqb][d] (zeros unless smooth_q);  v_f8 [G][d][Np], v_scale [G][d]
+ *  (only when v_f8 != NULL).  Np = oracle_pad_len(N).
+ */
+int oracle_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N, int d,
+                 int blk_q, int blk_k, int smooth_k, int smooth_q, int8_t* q_i8, int8_t* k_i8,
+                 float* q_scale, float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
+                 float* v_scale) {
+  if (B < 1 || H < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1) return -1;
+  int Np = oracle_pad_len(N), G = B * H;
+  int nqb = (N + blk_q - 1) / blk_q, nkb = (N + blk_k - 1) / blk_k;
+  size_t hs = (size_t)N * d, hp = (size_t)Np * d;
+  for (int g = 0; g < G; ++g) {
+    if (k_mean) memset(k_mean + (size_t)g * d, 0, sizeof(float) * (size_t)d);
+    if (q_mean) memset(q_mean + (size_t)g * nqb * d, 0, sizeof(float) * (size_t)nqb * d);
+    quant_head(k + g * hs, N, Np, d, blk_k, smooth_k ? 1 : 0, k_i8 + g * hp, k_scale + (size_t)g * nkb,
+               k_mean ? k_mean + (size_t)g * d : NULL, NULL);
+    quant_head(q + g * hs, N, Np, d, blk_q, smooth_q ? 2 : 0, q_i8 + g * hp, q_scale + (size_t)g * nqb,
+               NULL, q_mean ? q_mean + (size_t)g * nqb * d : NULL);
+    if (v_f8) quant_v_head(v + g * hs, N, Np, d, v_f8 + g * hp, v_scale + (size_t)g * d);
+  }
+  return 0;
+}
+
+/*
+ * S = Qhat Khat^T for one head, rows [r0, r0+nr) x keys [c0, c0+nc), exact int32.
+ *  q_i8, k_i8: [Np][d] of that head.  out: [nr][nc].
+ */
+int oracle_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int Np, int d, int r0, int nr, int c0,
+                    int nc, int32_t* out) {
+  if (r0 < 0 || c0 < 0 || r0 + nr > Np || c0 + nc > Np) return -1;
+  for (int i = 0; i < nr; ++i)
+    for (int j = 0; j < nc; ++j)
+      out[(size_t)i * nc + j] = dot_i8(q_i8 + (size_t)(r0 + i) * d, k_i8 + (size_t)(c0 + j) * d, d);
+  return 0;
+}
+
+/* Array forms of the codecs (for tests). */
+void oracle_f16_decode_n(const uint16_t* h, size_t n, double* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = oracle_f16_decode(h[i]);
+}
+void oracle_f16_encode_n(const double* x, size_t n, uint16_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = oracle_f16_encode(x[i]);
+}
+void oracle_e4m3_decode_n(const uint8_t* c, size_t n, double* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+void oracle_e4m3_encode_n(const double* x, size_t n, uint8_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}

@@ -1,0 +1,96 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case copies oracle.c, plants one mistake by text substitution (a dropped
+term, a wrong sign, index or constant, a transposed operand), builds the copy on
+the CPU, and runs the pin battery against it: at least one pin must fail.
+The real oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle as oracle_pkg
+from oracle import Oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
+
+MUTANTS = {
+    "v0 rescale dropped": ("o[c] = alpha * o[c] + acc;", "o[c] = o[c] + acc;"),
+    "v1 outer rescale dropped": ("o[c] = alpha * o[c] + inner[c];", "o[c] = o[c] + inner[c];"),
+    "l rescale dropped": ("l = alpha * l + psum;", "l = l + psum;"),
+    "mean divisor off by one": ("((double)(r1 - r0) * 16777216.0)", "((double)(r1 - r0 + 1) * 16777216.0)"),
+    "smoothing not applied": ("mean_mode ? v - mean[c] : v", "v"),
+    "q-smoothing term sign": ("sj += P->sm_scale * dk * ds;", "sj -= P->sm_scale * dk * ds;"),
+    "int8 range 128": ("float r = 127.0f / a;", "float r = 128.0f / a;"),
+    "truncation instead of rne": ("float t = rintf(xs[i] * r);", "float t = truncf(xs[i] * r);"),
+    "scale not divided": ("return a / 127.0f;", "return a / 128.0f;"),
+    "causal includes diagonal wrongly": ("if (P->causal && j > i) {", "if (P->causal && j >= i + 1 && j != i + 1) {"),
+    "k scale indexed by q block": ("h->ks[j / P->blk_k]", "h->ks[j / P->blk_q]"),
+    "q block index from k blocks": ("const int qb = i / P->blk_q;", "const int qb = i / P->blk_k;"),
+    "v fp8 operand transposed": ("acc += p[j - j0] * oracle_e4m3_decode(vrow[j]);",
+                                 "acc += p[j - j0] * oracle_e4m3_decode(h->vt[(size_t)j * d + c % d]);"),
+    "fp8 epilogue 448 dropped": ("o[c] * (double)h->vs[c] / (448.0 * l)", "o[c] * (double)h->vs[c] / l"),
+    "e4m3 rounding floors": ("double q = nearbyint(ldexp(a, 3 - E));", "double q = floor(ldexp(a, 3 - E));"),
+    "f16 encode exponent bias": ("((E + 15) << 10)", "((E + 14) << 10)"),
+    "dequant drops q scale": ("sj = P->sm_scale * (double)h->qs[qb] * dk * (double)S;",
+                              "sj = P->sm_scale * dk * (double)S;"),
+    "p~ fp8 scale dropped": ("oracle_e4m3_encode(p[j - j0] * 448.0)", "oracle_e4m3_encode(p[j - j0])"),
+}
+
+
+def _battery(orc):
+    """The pins, as (name, thunk) pairs."""
+    yield "f16 decode", lambda: pins.test_f16_decode_all_codes_match_numpy(orc)
+    yield "f16 encode", lambda: pins.test_f16_encode_matches_numpy_rne(orc)
+    yield "e4m3 decode", lambda: pins.test_e4m3_decode_all_codes_match_torch(orc)
+    yield "e4m3 encode", lambda: pins.test_e4m3_encode_rne_and_saturation(orc)
+    for a in [(7, 3, 4, 3), (10, 5, 10, 4), (5, 8, 2, 5)]:
+        yield f"fraction quant {a}", lambda a=a: pins.test_quant_matches_fraction_bruteforce(orc, *a)
+    yield "roundtrip", lambda: pins.test_quant_roundtrip_bound_and_absmax(orc)
+    yield "smoothing shift", lambda: pins.test_smoothing_subtracts_exact_token_mean(orc)
+    yield "qk int32", lambda: pins.test_qk_int32_matches_numpy_int64(orc)
+    for a in [(37, 0, 16), (37, 1, 16)]:
+        yield f"online {a}", lambda a=a: pins.test_online_softmax_equals_textbook(orc, *a)
+    for var in (0, 1):
+        yield f"q zero v{var}", lambda var=var: pins.test_closed_form_q_zero_gives_mean_of_visible_v(orc, var)
+        for causal in (0, 1):
+            yield f"lossless v{var} c{causal}", (
+                lambda var=var, causal=causal: pins.test_lossless_inputs_match_exact_attention(orc, var, causal))
+    yield "single token", lambda: pins.test_closed_form_single_token_and_causal_row0(orc)
+    yield "q smoothing term", lambda: pins.test_q_smoothing_term_restores_scores(orc)
+    yield "vs fp64 cfg1", lambda: pins.test_oracle_vs_fp64_attention_config1(orc)
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def test_battery_passes_on_real_oracle():
+    orc = Oracle()
+    for name, fn in _battery(orc):
+        fn()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site not found: {old}"
+    mut_src = os.path.join(mutant_dir, f"m_{abs(hash(name))}.c")
+    with open(mut_src, "w") as f:
+        f.write(src.replace(old, new))
+    so = mut_src[:-2] + ".so"
+    subprocess.check_call(["gcc", *oracle_pkg.CFLAGS, mut_src, "-o", so, "-lm"])
+    orc = Oracle(so)
+    caught = []
+    for pin, fn in _battery(orc):
+        try:
+            fn()
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin)
+            break
+    assert caught, f"no pin caught mutant '{name}'"
