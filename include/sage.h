@@ -1,0 +1,149 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) 8-bit attention forward.
+ *
+ * The operation is SageAttention's plug-and-play quantised attention forward:
+ *   "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+ *    Acceleration" (research summary page, sections "Summary" and
+ *    "Interesting ideas" I1, I3): K is smoothed by subtracting its mean over
+ *    tokens, Q and K are quantised to INT8, Q K^T runs on 8-bit matrix units,
+ *    the online (FlashAttention-style) softmax follows, P~ V stays in FP16;
+ *   "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and
+ *    Per-thread INT4 Quantization" (abstract): Q is smoothed as well, P~ and V
+ *    are quantised to FP8, and P~ V uses two-level accumulation.  Here Q/K stay
+ *    INT8 (one fp32 scale per block of tokens) in both variants.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *    The library never allocates, frees or keeps caller memory, and keeps no
+ *    state between calls.
+ *  - q, k, v, o are [B, H, N, d] contiguous IEEE fp16, 16-byte aligned.
+ *  - d must be 64 or 128 (SAGE_ERR_UNSUPPORTED otherwise); N >= 1;
+ *    B*H*pad_len(N)*d < 2^31.
+ *  - Quantised Q/K tensors are [B, H, Np, d] int8 with Np = sage_pad_len(N);
+ *    rows >= N are zero.  Q scales are [B, H, ceil(N / blk_q)] fp32, K scales
+ *    [B, H, ceil(N / blk_k)] fp32.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work and returns without waiting.
+ *  - Arguments are checked before anything is launched; a bad argument returns a
+ *    negative status and launches nothing.  No exception crosses the ABI.
+ *    sage_last_error() gives a message for the calling thread's last failure.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or flag */
+  SAGE_ERR_UNSUPPORTED = -2, /* head dim other than 64/128, bad block sizes */
+  SAGE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  SAGE_ERR_HIP = -4          /* a HIP launch failed (message in sage_last_error) */
+};
+
+enum {
+  SAGE_VARIANT_INT8QK_FP16PV = 0, /* SageAttention: INT8 Q K^T, FP16 P~ V (fp32 accumulation) */
+  SAGE_VARIANT_INT8QK_FP8PV = 1   /* SageAttention2-style: + Q smoothing, FP8 P~ and V, two-level accumulation */
+};
+
+/* Optional knobs.  Pass NULL for the defaults; set struct_size = sizeof(sage_params). */
+typedef struct {
+  int struct_size;
+  int blk_q;    /* tokens per Q scale block: 32, 64 or 128 (default 128) */
+  int blk_k;    /* tokens per K scale block: 16, 32, 64 or 128 (default 64) */
+  int smooth_k; /* subtract the token mean of K (default 1) */
+  int smooth_q; /* subtract the block mean of Q and add its term back (default: variant == 1) */
+} sage_params;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sage_version(void);
+
+/* Rows of the padded int8 / fp8 tensors: N rounded up to a multiple of 128. */
+int sage_pad_len(int N);
+
+/* Keys per online-softmax tile (the tile over which the running max advances and,
+ * in variant 1, the span of one fresh FP8 accumulator).  Ascending tiles of this
+ * size define the exact schedule of the softmax.  Returns < 0 for bad arguments. */
+int sage_kv_tile(int variant, int d);
+
+/* Bytes of device workspace sage_attn_fwd / sage_attn_fwd_ex / sage_quant_qk /
+ * sage_quant_v need for this shape (0 for bad arguments).  p may be NULL. */
+size_t sage_workspace_bytes(int B, int H, int N, int d, int variant, const sage_params* p);
+
+/*
+ * Smoothing and per-block INT8 quantisation of Q and K ([SA summary page]
+ * "Summary", I1; Q smoothing from the SageAttention2 abstract).
+ *   k_mean[B,H,d] = exact mean of K over the N tokens (fp32; exact integer sum of the
+ *     fp16 values, one rounding to fp64 by the division, one to fp32);
+ *   K' = K - k_mean (fp32); per block of blk_k tokens: scale = max|K'| / 127,
+ *     code = rint(K' * (127 / max|K'|)) in [-127, 127] (ties to even); a block of
+ *     zeros gets scale 0 and codes 0;
+ *   Q: the same per block of blk_q tokens; with smooth_q, the block's exact mean is
+ *     subtracted first and written to q_mean[B,H,ceil(N/blk_q),d].
+ * q_mean may be NULL unless smooth_q is on; k_mean may be NULL.
+ */
+int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const sage_params* p,
+                  int8_t* q_i8, int8_t* k_i8, float* q_scale, float* k_scale, float* k_mean,
+                  float* q_mean, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * FP8 E4M3 (OCP E4M3FN: bias 7, max 448) quantisation of V with one scale per
+ * channel (SageAttention2 abstract: P~ and V in FP8):
+ *   v_scale[B,H,d] = max_t |V[t,c]| / 448;
+ *   v_f8[B,H,d,Np] = E4M3(clamp(V[t,c] * (448 / max_t|V[t,c]|), +-448)), round to
+ *   nearest even, stored transposed (keys contiguous); columns >= N are 0; a
+ *   channel of zeros gets scale 0 and codes 0.
+ */
+int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float* v_scale,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * o = SageAttention(q, k, v): the whole plug-and-play forward (quantisation kernels
+ * plus the attention kernel).  causal: key j is visible to query i iff j <= i.
+ * sm_scale: softmax scale (finite, > 0; normally 1/sqrt(d)), applied when the int32
+ * scores are dequantised.  variant: SAGE_VARIANT_*.  ws: device workspace of at
+ * least sage_workspace_bytes(...) bytes.
+ */
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                  int causal, float sm_scale, int variant, void* ws, size_t ws_bytes, void* stream);
+
+/* sage_attn_fwd with explicit sage_params (block sizes, smoothing switches). */
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
+                     int d, int causal, float sm_scale, int variant, const sage_params* p, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * The attention kernel alone, on tensors sage_quant_qk / sage_quant_v produced
+ * (same p).  Variant 0 reads v (fp16); variant 1 reads v_f8 / v_scale and, with
+ * smooth_q, q_mean.  Used to time the attention kernel by itself.
+ */
+int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* q_scale,
+                           const float* k_scale, const float* q_mean, const void* v,
+                           const uint8_t* v_f8, const float* v_scale, void* o, int B, int H, int N,
+                           int d, int causal, float sm_scale, int variant, const sage_params* p,
+                           void* stream);
+
+/*
+ * Test surface: the int32 products S = Qhat Khat^T that the attention kernel forms,
+ * for chosen 128 x 64 tiles.  tiles[3*i + 0..2] = (flat head b*H+h, query tile, key
+ * tile) with query rows [128*qt, 128*qt+128) and keys [64*kt, 64*kt+64) of the padded
+ * tensors; tiles is a device array.  s_out: device [n_tiles][128][64] int32.
+ * blk_q is only used for validation and may be 0.
+ */
+int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
+                        const int* tiles, int n_tiles, int32_t* s_out, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* sage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H_ */

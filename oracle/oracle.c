@@ -479,25 +479,53 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
  * Quantised tensors of steps 1-3 (and the FP8 V of variant 1) for all heads.
  *  q_i8, k_i8: [G][Np][d];  q_scale [G][nqb], k_scale [G][nkb];  k_mean [G][d];
  *  q_mean [G][nqb][d] (zeros unless smooth_q);  v_f8 [G][d][Np], v_scale [G][d]
- *  (only when v_f8 != NULL).  Np = oracle_pad_len(N).
+ *  (only when v_f8 != NULL).  Np = oracle_pad_len(N).  Heads run on a thread pool;
+ *  each head is computed sequentially, so the result does not depend on threading.
  */
+typedef struct {
+  const uint16_t *q, *k, *v;
+  int N, d, Np, blk_q, blk_k, smooth_k, smooth_q, nqb, nkb;
+  int8_t *q_i8, *k_i8;
+  float *q_scale, *k_scale, *k_mean, *q_mean, *v_scale;
+  uint8_t* v_f8;
+  int G, next;
+  pthread_mutex_t mu;
+} quantjob_t;
+
+static void* quant_worker(void* arg) {
+  quantjob_t* J = (quantjob_t*)arg;
+  size_t hs = (size_t)J->N * J->d, hp = (size_t)J->Np * J->d;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int g = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (g >= J->G) break;
+    int d = J->d;
+    if (J->k_mean) memset(J->k_mean + (size_t)g * d, 0, sizeof(float) * (size_t)d);
+    if (J->q_mean) memset(J->q_mean + (size_t)g * J->nqb * d, 0, sizeof(float) * (size_t)J->nqb * d);
+    quant_head(J->k + g * hs, J->N, J->Np, d, J->blk_k, J->smooth_k ? 1 : 0, J->k_i8 + g * hp,
+               J->k_scale + (size_t)g * J->nkb, J->k_mean ? J->k_mean + (size_t)g * d : NULL, NULL);
+    quant_head(J->q + g * hs, J->N, J->Np, d, J->blk_q, J->smooth_q ? 2 : 0, J->q_i8 + g * hp,
+               J->q_scale + (size_t)g * J->nqb, NULL, J->q_mean ? J->q_mean + (size_t)g * J->nqb * d : NULL);
+    if (J->v_f8) quant_v_head(J->v + g * hs, J->N, J->Np, d, J->v_f8 + g * hp, J->v_scale + (size_t)g * d);
+  }
+  return NULL;
+}
+
 int oracle_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N, int d,
                  int blk_q, int blk_k, int smooth_k, int smooth_q, int8_t* q_i8, int8_t* k_i8,
                  float* q_scale, float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
                  float* v_scale) {
   if (B < 1 || H < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1) return -1;
-  int Np = oracle_pad_len(N), G = B * H;
-  int nqb = (N + blk_q - 1) / blk_q, nkb = (N + blk_k - 1) / blk_k;
-  size_t hs = (size_t)N * d, hp = (size_t)Np * d;
-  for (int g = 0; g < G; ++g) {
-    if (k_mean) memset(k_mean + (size_t)g * d, 0, sizeof(float) * (size_t)d);
-    if (q_mean) memset(q_mean + (size_t)g * nqb * d, 0, sizeof(float) * (size_t)nqb * d);
-    quant_head(k + g * hs, N, Np, d, blk_k, smooth_k ? 1 : 0, k_i8 + g * hp, k_scale + (size_t)g * nkb,
-               k_mean ? k_mean + (size_t)g * d : NULL, NULL);
-    quant_head(q + g * hs, N, Np, d, blk_q, smooth_q ? 2 : 0, q_i8 + g * hp, q_scale + (size_t)g * nqb,
-               NULL, q_mean ? q_mean + (size_t)g * nqb * d : NULL);
-    if (v_f8) quant_v_head(v + g * hs, N, Np, d, v_f8 + g * hp, v_scale + (size_t)g * d);
-  }
+  quantjob_t J = {q, k, v, N, d, oracle_pad_len(N), blk_q, blk_k, smooth_k, smooth_q,
+                  (N + blk_q - 1) / blk_q, (N + blk_k - 1) / blk_k, q_i8, k_i8, q_scale, k_scale,
+                  k_mean, q_mean, v_scale, v_f8, B * H, 0, PTHREAD_MUTEX_INITIALIZER};
+  int nt = pick_threads(0);
+  if (nt > J.G) nt = J.G;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, quant_worker, &J);
+  for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+  free(th);
   return 0;
 }
 

@@ -1,0 +1,221 @@
+"""SageAttention-style 8-bit attention forward for the MI355X (gfx950).
+
+Thin Python binding over the C ABI of libsage.so (include/sage.h): it checks
+dtypes, shapes and devices, allocates outputs and the workspace with torch, and
+passes raw device pointers and the current HIP stream.  Every step of the
+computation runs in the HIP kernels of libsage.so; there is no other path.
+
+Method (pages): "SageAttention: Accurate 8-Bit Attention for Plug-and-play
+Inference Acceleration" (summary page, "Summary", "Interesting ideas" I1/I3) and
+"SageAttention2 ..." (abstract: Q smoothing, FP8 P~/V, two-level accumulation).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "debug_qk_int32", "workspace_bytes",
+           "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV"]
+
+VARIANT_FP16PV = 0
+VARIANT_FP8PV = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsage.so")
+_lib = None
+
+
+class SageError(RuntimeError):
+    pass
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int), ("blk_q", ctypes.c_int), ("blk_k", ctypes.c_int),
+                ("smooth_k", ctypes.c_int), ("smooth_q", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise SageError(f"{_LIB_PATH} is missing: build it first "
+                        "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    PP = ctypes.POINTER(_Params)
+    sig = {
+        "sage_version": ([], I),
+        "sage_pad_len": ([I], I),
+        "sage_kv_tile": ([I, I], I),
+        "sage_workspace_bytes": ([I, I, I, I, I, PP], S),
+        "sage_quant_qk": ([P, P, I, I, I, I, PP, P, P, P, P, P, P, P, S, P], I),
+        "sage_quant_v": ([P, I, I, I, I, P, P, P, S, P], I),
+        "sage_attn_fwd": ([P, P, P, P, I, I, I, I, I, F, I, P, S, P], I),
+        "sage_attn_fwd_ex": ([P, P, P, P, I, I, I, I, I, F, I, PP, P, S, P], I),
+        "sage_attn_fwd_prequant": ([P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
+        "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
+        "sage_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = _load().sage_last_error().decode()
+        raise SageError(f"{what} failed ({rc}): {msg}")
+
+
+def _params(blk_q=128, blk_k=64, smooth_k=True, smooth_q=False) -> _Params:
+    return _Params(ctypes.sizeof(_Params), int(blk_q), int(blk_k), int(bool(smooth_k)), int(bool(smooth_q)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(*ts):
+    ref = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16:
+            raise TypeError("q, k, v must be float16 tensors")
+        if not t.is_cuda:
+            raise ValueError("q, k, v must be on a GPU")
+        if t.dim() != 4 or t.shape != ref.shape or t.device != ref.device:
+            raise ValueError("q, k, v must share one [B, H, N, d] shape and device")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    return ref.shape
+
+
+def pad_len(N: int) -> int:
+    return _load().sage_pad_len(N)
+
+
+def kv_tile(variant: int, d: int) -> int:
+    return _load().sage_kv_tile(variant, d)
+
+
+def workspace_bytes(B, H, N, d, variant=0, blk_q=128, blk_k=64, smooth_k=True, smooth_q=None) -> int:
+    if smooth_q is None:
+        smooth_q = variant == VARIANT_FP8PV
+    p = _params(blk_q, blk_k, smooth_k, smooth_q)
+    return _load().sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128, blk_k=64,
+         smooth_k=True, smooth_q=None, out=None, workspace=None):
+    """o = SageAttention(q, k, v) for [B, H, N, d] fp16 tensors on the GPU."""
+    B, H, N, d = _check_qkv(q, k, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if smooth_q is None:
+        smooth_q = variant == VARIANT_FP8PV
+    if out is None:
+        out = torch.empty_like(q)
+    p = _params(blk_q, blk_k, smooth_k, smooth_q)
+    lib = _load()
+    nbytes = lib.sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))
+    if nbytes == 0:
+        _check(-1, "sage_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.sage_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, int(bool(causal)),
+                              float(sm_scale), int(variant), ctypes.byref(p), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(q.device))
+    _check(rc, "sage_attn_fwd_ex")
+    return out
+
+
+def quant_qk(q, k, blk_q=128, blk_k=64, smooth_k=True, smooth_q=False) -> dict:
+    """Smoothing + per-block INT8 of Q and K.  Returns the int8 tensors, scales and means."""
+    B, H, N, d = _check_qkv(q, k)
+    dev = q.device
+    Np = pad_len(N)
+    nqb, nkb = -(-N // blk_q), -(-N // blk_k)
+    r = dict(q_i8=torch.empty((B, H, Np, d), dtype=torch.int8, device=dev),
+             k_i8=torch.empty((B, H, Np, d), dtype=torch.int8, device=dev),
+             q_scale=torch.empty((B, H, nqb), dtype=torch.float32, device=dev),
+             k_scale=torch.empty((B, H, nkb), dtype=torch.float32, device=dev),
+             k_mean=torch.zeros((B, H, d), dtype=torch.float32, device=dev),
+             q_mean=torch.zeros((B, H, nqb, d), dtype=torch.float32, device=dev))
+    p = _params(blk_q, blk_k, smooth_k, smooth_q)
+    lib = _load()
+    ws = _workspace(lib.sage_workspace_bytes(B, H, N, d, 0, ctypes.byref(p)), dev, None)
+    rc = lib.sage_quant_qk(_ptr(q), _ptr(k), B, H, N, d, ctypes.byref(p), _ptr(r["q_i8"]), _ptr(r["k_i8"]),
+                           _ptr(r["q_scale"]), _ptr(r["k_scale"]), _ptr(r["k_mean"]),
+                           _ptr(r["q_mean"]) if smooth_q else None, _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "sage_quant_qk")
+    return r
+
+
+def quant_v(v) -> dict:
+    """FP8 E4M3 V with per-channel scales: v_f8 [B, H, d, Np] (uint8 codes), v_scale [B, H, d]."""
+    B, H, N, d = _check_qkv(v)
+    dev = v.device
+    Np = pad_len(N)
+    r = dict(v_f8=torch.empty((B, H, d, Np), dtype=torch.uint8, device=dev),
+             v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev))
+    lib = _load()
+    ws = _workspace(lib.sage_workspace_bytes(B, H, N, d, 1, None), dev, None)
+    rc = lib.sage_quant_v(_ptr(v), B, H, N, d, _ptr(r["v_f8"]), _ptr(r["v_scale"]), _ptr(ws), ws.numel(),
+                          _stream(dev))
+    _check(rc, "sage_quant_v")
+    return r
+
+
+def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_FP16PV, vq: dict | None = None,
+                  blk_q=128, blk_k=64, smooth_q=None, out=None):
+    """The attention kernel alone, on quant_qk() / quant_v() outputs."""
+    B, H, Np, d = qk["q_i8"].shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if smooth_q is None:
+        smooth_q = variant == VARIANT_FP8PV
+    dev = qk["q_i8"].device
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
+    p = _params(blk_q, blk_k, True, smooth_q)
+    rc = _load().sage_attn_fwd_prequant(
+        _ptr(qk["q_i8"]), _ptr(qk["k_i8"]), _ptr(qk["q_scale"]), _ptr(qk["k_scale"]),
+        _ptr(qk["q_mean"]) if smooth_q else None, _ptr(v) if variant == 0 else None,
+        _ptr(vq["v_f8"]) if variant == 1 else None, _ptr(vq["v_scale"]) if variant == 1 else None,
+        _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale), int(variant), ctypes.byref(p), _stream(dev))
+    _check(rc, "sage_attn_fwd_prequant")
+    return out
+
+
+def debug_qk_int32(q_i8, k_i8, N, tiles) -> torch.Tensor:
+    """int32 S = Qhat Khat^T tiles (128 queries x 64 keys) as the attention kernel forms them.
+    tiles: list of (flat head, query tile, key tile)."""
+    B, H, Np, d = q_i8.shape
+    dev = q_i8.device
+    t = torch.tensor(list(tiles), dtype=torch.int32, device=dev).reshape(-1, 3).contiguous()
+    out = torch.empty((t.shape[0], 128, 64), dtype=torch.int32, device=dev)
+    rc = _load().sage_debug_qk_int32(_ptr(q_i8), _ptr(k_i8), B, H, N, d, _ptr(t), t.shape[0], _ptr(out),
+                                     _stream(dev))
+    _check(rc, "sage_debug_qk_int32")
+    return out

@@ -1,0 +1,347 @@
+// sage_api.cpp -- the C ABI declared in include/sage.h: argument checks, workspace
+// layout, dispatch to the gfx950 kernels.  Every check runs before any HIP call, so a
+// rejected call touches neither the GPU nor the HIP runtime.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sage.h"
+#include "sage_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SAGE_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SAGE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kPad = 128;
+constexpr int kStatRows = 512;
+
+int pad_len(int N) { return (N + kPad - 1) / kPad * kPad; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+struct Params {
+  int blk_q = 128, blk_k = 64, smooth_k = 1, smooth_q = 0;
+};
+
+int read_params(const sage_params* p, int variant, Params* out) {
+  Params r;
+  r.smooth_q = variant == SAGE_VARIANT_INT8QK_FP8PV ? 1 : 0;
+  if (p) {
+    if (p->struct_size != (int)sizeof(sage_params))
+      return fail(SAGE_ERR_INVALID_ARG, "sage_params.struct_size must be %d", (int)sizeof(sage_params));
+    r.blk_q = p->blk_q;
+    r.blk_k = p->blk_k;
+    r.smooth_k = p->smooth_k;
+    r.smooth_q = p->smooth_q;
+  }
+  if (r.blk_q != 32 && r.blk_q != 64 && r.blk_q != 128)
+    return fail(SAGE_ERR_UNSUPPORTED, "blk_q must be 32, 64 or 128 (got %d)", r.blk_q);
+  if (r.blk_k != 16 && r.blk_k != 32 && r.blk_k != 64 && r.blk_k != 128)
+    return fail(SAGE_ERR_UNSUPPORTED, "blk_k must be 16, 32, 64 or 128 (got %d)", r.blk_k);
+  if ((r.smooth_k != 0 && r.smooth_k != 1) || (r.smooth_q != 0 && r.smooth_q != 1))
+    return fail(SAGE_ERR_INVALID_ARG, "smooth_k / smooth_q must be 0 or 1");
+  *out = r;
+  return SAGE_OK;
+}
+
+int check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return fail(SAGE_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (d != 64 && d != 128) return fail(SAGE_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", d);
+  const long long elems = (long long)B * H * pad_len(N) * d;
+  if (elems >= (1LL << 31)) return fail(SAGE_ERR_INVALID_ARG, "B*H*pad_len(N)*d must be < 2^31");
+  return SAGE_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(SAGE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(SAGE_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return SAGE_OK;
+}
+
+// Workspace layout (each piece 256-byte aligned).
+struct Layout {
+  size_t ksum, vmax, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, total;
+};
+
+size_t up(size_t x) { return (x + 255) / 256 * 256; }
+
+Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
+  const size_t G = (size_t)B * H, Np = pad_len(N), ns = ceil_div(N, kStatRows);
+  const size_t nqb = ceil_div(N, p.blk_q), nkb = ceil_div(N, p.blk_k);
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  L.ksum = take(G * ns * d * sizeof(long long));
+  L.vmax = take(variant == 1 ? G * ns * d * sizeof(float) : 0);
+  L.q_i8 = take(G * Np * d);
+  L.k_i8 = take(G * Np * d);
+  L.q_scale = take(G * nqb * sizeof(float));
+  L.k_scale = take(G * nkb * sizeof(float));
+  L.k_mean = take(G * d * sizeof(float));
+  L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
+  L.v_f8 = take(variant == 1 ? G * d * Np : 0);
+  L.v_scale = take(variant == 1 ? G * d * sizeof(float) : 0);
+  L.total = off;
+  return L;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SAGE_OK;
+  if (!ws) return fail(SAGE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 256)) return fail(SAGE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return SAGE_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+sage::QuantArgs quant_args(const void* q, const void* k, int B, int H, int N, int d, const Params& p, int8_t* q_i8,
+                           int8_t* k_i8, float* q_scale, float* k_scale, float* k_mean, float* q_mean,
+                           const long long* ksum) {
+  (void)d;
+  sage::QuantArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.q_i8 = q_i8;
+  a.k_i8 = k_i8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.k_mean = k_mean;
+  a.q_mean = q_mean;
+  a.ksum_part = ksum;
+  a.G = B * H;
+  a.N = N;
+  a.Np = pad_len(N);
+  a.blk_q = p.blk_q;
+  a.blk_k = p.blk_k;
+  a.nqb = ceil_div(N, p.blk_q);
+  a.nkb = ceil_div(N, p.blk_k);
+  a.nsplit = ceil_div(N, kStatRows);
+  a.smooth_k = p.smooth_k;
+  a.smooth_q = p.smooth_q;
+  return a;
+}
+
+int run_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const Params& p, int8_t* q_i8,
+                 int8_t* k_i8, float* q_scale, float* k_scale, float* k_mean, float* q_mean, long long* ksum,
+                 hipStream_t st) {
+  hipError_t e;
+  if (p.smooth_k) {
+    e = sage::launch_stats(d, k, nullptr, B * H, N, ksum, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "statistics kernel");
+  }
+  e = sage::launch_quant(d, quant_args(q, k, B, H, N, d, p, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, ksum), st);
+  if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
+  return SAGE_OK;
+}
+
+int attn_common(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
+                float sm_scale, int variant, const sage_params* pp, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (variant != 0 && variant != 1) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, variant, &p))) return rc;
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k, 16, "k")) || (rc = check_ptr(v, 16, "v")) ||
+      (rc = check_ptr(o, 16, "o")))
+    return rc;
+  const Layout L = layout(B, H, N, d, variant, p);
+  if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int G = B * H, Np = pad_len(N);
+  hipError_t e;
+  if (p.smooth_k || variant == 1) {
+    e = sage::launch_stats(d, k, variant == 1 ? v : nullptr, G, N, at<long long>(ws, L.ksum),
+                           variant == 1 ? at<float>(ws, L.vmax) : nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "statistics kernel");
+  }
+  e = sage::launch_quant(d,
+                         quant_args(q, k, B, H, N, d, p, at<int8_t>(ws, L.q_i8), at<int8_t>(ws, L.k_i8),
+                                    at<float>(ws, L.q_scale), at<float>(ws, L.k_scale), at<float>(ws, L.k_mean),
+                                    p.smooth_q ? at<float>(ws, L.q_mean) : nullptr, at<long long>(ws, L.ksum)),
+                         st);
+  if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
+  if (variant == 1) {
+    e = sage::launch_quant_v(d, v, G, N, Np, at<float>(ws, L.vmax), at<uint8_t>(ws, L.v_f8),
+                             at<float>(ws, L.v_scale), st);
+    if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
+  }
+  sage::AttnArgs a{};
+  a.q_i8 = at<int8_t>(ws, L.q_i8);
+  a.k_i8 = at<int8_t>(ws, L.k_i8);
+  a.q_scale = at<float>(ws, L.q_scale);
+  a.k_scale = at<float>(ws, L.k_scale);
+  a.q_mean = p.smooth_q ? at<float>(ws, L.q_mean) : nullptr;
+  a.v = (const uint16_t*)v;
+  a.v_f8 = variant == 1 ? at<uint8_t>(ws, L.v_f8) : nullptr;
+  a.v_scale = variant == 1 ? at<float>(ws, L.v_scale) : nullptr;
+  a.o = (uint16_t*)o;
+  a.G = G;
+  a.N = N;
+  a.Np = Np;
+  a.blk_q = p.blk_q;
+  a.blk_k = p.blk_k;
+  a.nqb = ceil_div(N, p.blk_q);
+  a.nkb = ceil_div(N, p.blk_k);
+  a.kscale = sm_scale * 1.4426950408889634f;
+  e = sage::launch_attn(d, variant, causal, p.smooth_q, a, st);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_version(void) { return 100; }
+
+int sage_pad_len(int N) { return N < 1 ? -1 : pad_len(N); }
+
+int sage_kv_tile(int variant, int d) {
+  if ((variant != 0 && variant != 1) || (d != 64 && d != 128)) return -1;
+  return 64;
+}
+
+size_t sage_workspace_bytes(int B, int H, int N, int d, int variant, const sage_params* pp) {
+  if (check_shape(B, H, N, d) || (variant != 0 && variant != 1)) return 0;
+  Params p;
+  if (read_params(pp, variant, &p)) return 0;
+  return layout(B, H, N, d, variant, p).total;
+}
+
+int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const sage_params* pp, int8_t* q_i8,
+                  int8_t* k_i8, float* q_scale, float* k_scale, float* k_mean, float* q_mean, void* ws,
+                  size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  Params p;
+  if ((rc = read_params(pp, 0, &p))) return rc;
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k, 16, "k")) || (rc = check_ptr(q_i8, 16, "q_i8")) ||
+      (rc = check_ptr(k_i8, 16, "k_i8")) || (rc = check_ptr(q_scale, 4, "q_scale")) ||
+      (rc = check_ptr(k_scale, 4, "k_scale")))
+    return rc;
+  if (k_mean && !aligned(k_mean, 4)) return fail(SAGE_ERR_INVALID_ARG, "k_mean must be 4-byte aligned");
+  if (p.smooth_q && (rc = check_ptr(q_mean, 4, "q_mean (required with smooth_q)"))) return rc;
+  const size_t need = p.smooth_k ? up((size_t)B * H * ceil_div(N, kStatRows) * d * sizeof(long long)) : 0;
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  rc = run_quant_qk(q, k, B, H, N, d, p, q_i8, k_i8, q_scale, k_scale, k_mean, p.smooth_q ? q_mean : nullptr,
+                    (long long*)ws, (hipStream_t)stream);
+  return rc ? rc : ok();
+}
+
+int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float* v_scale, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if ((rc = check_ptr(v, 16, "v")) || (rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")))
+    return rc;
+  const size_t G = (size_t)B * H, ns = ceil_div(N, kStatRows);
+  const size_t off_v = up(G * ns * d * sizeof(long long));
+  const size_t need = off_v + up(G * ns * d * sizeof(float));
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  long long* ksum = (long long*)ws;
+  float* vmax = at<float>(ws, off_v);
+  // the statistics pass reads K and V together; with V as "K" too the K sums are unused
+  hipError_t e = sage::launch_stats(d, v, v, (int)G, N, ksum, vmax, st);
+  if (e != hipSuccess) return hip_fail(e, "statistics kernel");
+  e = sage::launch_quant_v(d, v, (int)G, N, pad_len(N), vmax, v_f8, v_scale, st);
+  if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
+  return ok();
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
+                  float sm_scale, int variant, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common(q, k, v, o, B, H, N, d, causal, sm_scale, variant, nullptr, ws, ws_bytes, stream);
+}
+
+int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
+                     float sm_scale, int variant, const sage_params* p, void* ws, size_t ws_bytes, void* stream) {
+  return attn_common(q, k, v, o, B, H, N, d, causal, sm_scale, variant, p, ws, ws_bytes, stream);
+}
+
+int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* q_scale, const float* k_scale,
+                           const float* q_mean, const void* v, const uint8_t* v_f8, const float* v_scale, void* o,
+                           int B, int H, int N, int d, int causal, float sm_scale, int variant,
+                           const sage_params* pp, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (variant != 0 && variant != 1) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, variant, &p))) return rc;
+  if ((rc = check_ptr(q_i8, 16, "q_i8")) || (rc = check_ptr(k_i8, 16, "k_i8")) ||
+      (rc = check_ptr(q_scale, 4, "q_scale")) || (rc = check_ptr(k_scale, 4, "k_scale")) ||
+      (rc = check_ptr(o, 16, "o")))
+    return rc;
+  if (variant == 0 && (rc = check_ptr(v, 16, "v"))) return rc;
+  if (variant == 1 && ((rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")))) return rc;
+  if (p.smooth_q && (rc = check_ptr(q_mean, 4, "q_mean (required with smooth_q)"))) return rc;
+  sage::AttnArgs a{};
+  a.q_i8 = q_i8;
+  a.k_i8 = k_i8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.q_mean = q_mean;
+  a.v = (const uint16_t*)v;
+  a.v_f8 = v_f8;
+  a.v_scale = v_scale;
+  a.o = (uint16_t*)o;
+  a.G = B * H;
+  a.N = N;
+  a.Np = pad_len(N);
+  a.blk_q = p.blk_q;
+  a.blk_k = p.blk_k;
+  a.nqb = ceil_div(N, p.blk_q);
+  a.nkb = ceil_div(N, p.blk_k);
+  a.kscale = sm_scale * 1.4426950408889634f;
+  hipError_t e = sage::launch_attn(d, variant, causal, p.smooth_q, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d, const int* tiles,
+                        int n_tiles, int32_t* s_out, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (n_tiles < 1) return fail(SAGE_ERR_INVALID_ARG, "n_tiles must be >= 1");
+  if ((rc = check_ptr(q_i8, 16, "q_i8")) || (rc = check_ptr(k_i8, 16, "k_i8")) || (rc = check_ptr(tiles, 4, "tiles")) ||
+      (rc = check_ptr(s_out, 16, "s_out")))
+    return rc;
+  hipError_t e = sage::launch_debug_qk(d, q_i8, k_i8, B * H, pad_len(N), tiles, n_tiles, s_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug QK kernel");
+  return ok();
+}
+
+const char* sage_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// sage_device.h -- gfx950 device helpers shared by the quantisation and attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kBlockQ = 128;    // query rows per attention workgroup (32 per wave)
+constexpr int kTileKV = 64;     // keys per online-softmax tile
+constexpr int kPad = 128;       // the int8 / fp8 tensors are padded to a multiple of this
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2_448 = 8.807354922057604f;  // log2(448): P~ * 448 is exp2(x + log2 448)
+
+// ---- MFMA (gfx950).  32x32 output tile: lane l, register i holds row
+// 8*(i/4) + 4*(l/32) + i%4, column l%32.  Operand A: lane l holds row l%32 and the
+// k-slots of half l/32; operand B: column l%32, the same k-slots.
+__device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// FP8 E4M3 (OCP) x FP8 E4M3, fp32 accumulation; unit scales select the plain instruction.
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Value of the same register in lane l ^ 32.  v_permlane32_swap exchanges the upper
+// half of the first operand with the lower half of the second; with both equal to x,
+// result[0] = (x[0..31], x[0..31]) and result[1] = (x[32..63], x[32..63]).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS transpose read of 16-bit data: inside each group of 16 lanes, lane i receives
+// element i%4 of the 4-element rows addressed by lanes 4e + i/4 (e = 0..3).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_ptr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+}
+
+// fp16 bits -> value * 2^24 as an exact integer (every fp16 is a multiple of 2^-24).
+__device__ __forceinline__ long long f16_bits_to_fixed24(uint32_t h) {
+  uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+  long long mag = e ? ((long long)(1024u + m) << (e - 1)) : (long long)m;
+  return (h & 0x8000u) ? -mag : mag;
+}
+
+// Exact fixed-point sum (units of 2^-24) divided by count: one correctly rounded fp64
+// division, then round to fp32.
+__device__ __forceinline__ float fixed24_mean(long long sum, int count) {
+  return (float)((double)sum / ((double)count * 16777216.0));
+}
+
+// Round to nearest even and pack two floats as OCP E4M3 into the low (hi = false) or
+// high half of `old`.  Inputs must already lie in [-448, 448].
+__device__ __forceinline__ uint32_t cvt_pk_fp8(float a, float b, uint32_t old, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true)
+            : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f32x2 v = {a, b};
+  f16x2 h = __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+}  // namespace sage

@@ -1,0 +1,46 @@
+// sage_internal.h -- launcher interface between the C ABI (sage_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+struct QuantArgs {
+  const uint16_t* q;  // [G][N][D] fp16
+  const uint16_t* k;
+  int8_t* q_i8;       // [G][Np][D]
+  int8_t* k_i8;
+  float* q_scale;     // [G][nqb]
+  float* k_scale;     // [G][nkb]
+  float* k_mean;      // [G][D] or null
+  float* q_mean;      // [G][nqb][D] or null
+  const long long* ksum_part;  // [G][nsplit][D] from the statistics pass
+  int G, N, Np, blk_q, blk_k, nqb, nkb, nsplit, smooth_k, smooth_q;
+};
+
+struct AttnArgs {
+  const int8_t* q_i8;     // [G][Np][D]
+  const int8_t* k_i8;     // [G][Np][D]
+  const float* q_scale;   // [G][nqb]
+  const float* k_scale;   // [G][nkb]
+  const float* q_mean;    // [G][nqb][D] (variant 1 with Q smoothing)
+  const uint16_t* v;      // [G][N][D] fp16 (variant 0)
+  const uint8_t* v_f8;    // [G][D][Np] (variant 1)
+  const float* v_scale;   // [G][D] (variant 1)
+  uint16_t* o;            // [G][N][D] fp16
+  int G, N, Np, blk_q, blk_k, nqb, nkb;
+  float kscale;           // sm_scale * log2(e)
+};
+
+int stat_splits(int N);
+hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long long* ksum_part,
+                        float* vmax_part, hipStream_t st);
+hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st);
+hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const float* vmax_part,
+                          uint8_t* v_f8, float* v_scale, hipStream_t st);
+hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st);
+hipError_t launch_debug_qk(int d, const int8_t* q_i8, const int8_t* k_i8, int G, int Np, const int* tiles,
+                           int n_tiles, int32_t* s_out, hipStream_t st);
+
+}  // namespace sage

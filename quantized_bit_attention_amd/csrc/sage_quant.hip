@@ -1,0 +1,314 @@
+// sage_quant.hip -- smoothing and quantisation kernels (gfx950).
+//
+// Method: "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+// Acceleration" (summary page, "Summary" and "Interesting ideas" I1): K loses its
+// token mean, then Q and K become INT8 with one fp32 scale per block of tokens.
+// "SageAttention2 ..." (abstract): Q loses its block mean; V becomes FP8 with one
+// scale per channel.
+//
+// All three passes are bound by HBM bandwidth: they read fp16 rows with 16-byte
+// loads (8 channels per thread, d/8 threads per row) and write int8 / fp8 codes.
+//
+// Exactness: token sums are exact int64 sums of the fp16 values in units of 2^-24,
+// so means do not depend on summation order; every fp32 step (subtract, multiply by
+// the reciprocal, divide) is a single IEEE operation, with contraction off.
+#include "sage_device.h"
+#include "sage_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace sage {
+
+constexpr int kStatRows = 512;  // token rows per workgroup of the statistics pass
+
+// Pass 1: per (head, split of kStatRows tokens) partial sums of K (exact, int64) and,
+// when v != nullptr, partial max |V| per channel.
+//   ksum_part [G][nsplit][D] int64, vmax_part [G][nsplit][D] fp32.
+template <int D>
+__global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int N,
+                                                         int nsplit, long long* __restrict__ ksum_part,
+                                                         float* __restrict__ vmax_part) {
+  constexpr int TPR = D / 8;            // threads per row
+  constexpr int RPI = kThreads / TPR;   // rows per iteration
+  const int split = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, cg = tid % TPR, r0 = tid / TPR;
+  const size_t head = (size_t)g * N * D;
+  const int t0 = split * kStatRows, t1 = min(N, t0 + kStatRows);
+
+  long long acc[8];
+  float vm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { acc[j] = 0; vm[j] = 0.0f; }
+
+  for (int t = t0 + r0; t < t1; t += RPI) {
+    const uint4 kk = *reinterpret_cast<const uint4*>(k + head + (size_t)t * D + cg * 8);
+    const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += f16_bits_to_fixed24(w[j] & 0xffffu);
+      acc[2 * j + 1] += f16_bits_to_fixed24(w[j] >> 16);
+    }
+    if (v) {
+      const uint4 vv = *reinterpret_cast<const uint4*>(v + head + (size_t)t * D + cg * 8);
+      const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f16x2 h = __builtin_bit_cast(f16x2, u[j]);
+        vm[2 * j] = fmaxf(vm[2 * j], fabsf((float)h[0]));
+        vm[2 * j + 1] = fmaxf(vm[2 * j + 1], fabsf((float)h[1]));
+      }
+    }
+  }
+
+  __shared__ long long s_sum[kThreads][8];
+  __shared__ float s_max[kThreads][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { s_sum[tid][j] = acc[j]; s_max[tid][j] = vm[j]; }
+  __syncthreads();
+  if (tid < D) {
+    const int c = tid, cgc = c / 8, jj = c % 8;
+    long long s = 0;
+    float m = 0.0f;
+    for (int r = 0; r < RPI; ++r) {
+      s += s_sum[r * TPR + cgc][jj];
+      m = fmaxf(m, s_max[r * TPR + cgc][jj]);
+    }
+    const size_t o = ((size_t)g * nsplit + split) * D + c;
+    ksum_part[o] = s;
+    if (v) vmax_part[o] = m;
+  }
+}
+
+// Block reduction of a non-negative float max over the workgroup.
+__device__ __forceinline__ float block_max(float x, float* red) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  const int wave = threadIdx.x / 64;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Pass 2: smooth + quantise one block of rows (a K block or a Q block) per workgroup.
+//   blockIdx.x < G * nkb: K block (mean from the pass-1 partial sums when smooth_k);
+//   otherwise a Q block (its own exact block mean when smooth_q).
+// MAXR: rows per block rounded up to a multiple of kThreads / (D/8).
+template <int D, int MAXR>
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
+  constexpr int TPR = D / 8;
+  constexpr int RPI = kThreads / TPR;
+  constexpr int NIT = MAXR / RPI;
+  __shared__ float s_mean[D];
+  __shared__ long long s_sum[kThreads][8];
+  __shared__ float s_red[4];
+
+  const int tid = threadIdx.x, cg = tid % TPR, r0 = tid / TPR;
+  const int nk_blocks = a.G * a.nkb;
+  const bool is_k = (int)blockIdx.x < nk_blocks;
+  const int idx = is_k ? (int)blockIdx.x : (int)blockIdx.x - nk_blocks;
+  const int nb = is_k ? a.nkb : a.nqb;
+  const int blk = is_k ? a.blk_k : a.blk_q;
+  const int g = idx / nb, b = idx % nb;
+  const int t0 = b * blk, t1 = min(a.N, t0 + blk), rows = t1 - t0;
+  const uint16_t* __restrict__ src = (is_k ? a.k : a.q) + (size_t)g * a.N * D;
+  int8_t* __restrict__ dst = (is_k ? a.k_i8 : a.q_i8) + (size_t)g * a.Np * D;
+  const bool smooth = is_k ? a.smooth_k : a.smooth_q;
+
+  // load the block's rows: thread holds rows r0 + RPI*it, channels cg*8 .. cg*8+7
+  uint4 raw[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = r0 + RPI * it;
+    raw[it] = r < rows ? *reinterpret_cast<const uint4*>(src + (size_t)(t0 + r) * D + cg * 8)
+                       : make_uint4(0, 0, 0, 0);
+  }
+
+  if (smooth) {
+    if (is_k) {
+      if (tid < D) {
+        long long s = 0;
+        for (int sp = 0; sp < a.nsplit; ++sp) s += a.ksum_part[((size_t)g * a.nsplit + sp) * D + tid];
+        const float m = fixed24_mean(s, a.N);
+        s_mean[tid] = m;
+        if (b == 0 && a.k_mean) a.k_mean[(size_t)g * D + tid] = m;
+      }
+    } else {
+      long long acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += f16_bits_to_fixed24(w[j] & 0xffffu);
+          acc[2 * j + 1] += f16_bits_to_fixed24(w[j] >> 16);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_sum[tid][j] = acc[j];
+      __syncthreads();
+      if (tid < D) {
+        long long s = 0;
+        for (int r = 0; r < RPI; ++r) s += s_sum[r * TPR + tid / 8][tid % 8];
+        const float m = fixed24_mean(s, rows);
+        s_mean[tid] = m;
+        if (a.q_mean) a.q_mean[((size_t)g * a.nqb + b) * D + tid] = m;
+      }
+    }
+  } else if (tid < D) {
+    s_mean[tid] = 0.0f;
+  }
+  __syncthreads();
+
+  float mean[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mean[j] = s_mean[cg * 8 + j];
+
+  // smoothed values and the block absmax
+  float x[NIT][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+    const bool valid = r0 + RPI * it < rows;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x2 h = __builtin_bit_cast(f16x2, w[j]);
+      float x0 = (float)h[0], x1 = (float)h[1];
+      if (smooth) { x0 = x0 - mean[2 * j]; x1 = x1 - mean[2 * j + 1]; }
+      x[it][2 * j] = valid ? x0 : 0.0f;
+      x[it][2 * j + 1] = valid ? x1 : 0.0f;
+      amax = fmaxf(amax, fmaxf(fabsf(x[it][2 * j]), fabsf(x[it][2 * j + 1])));
+    }
+  }
+  amax = block_max(amax, s_red);
+  const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+  if (tid == 0) (is_k ? a.k_scale : a.q_scale)[(size_t)g * nb + b] = amax / 127.0f;
+
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int row = r0 + RPI * it;
+    if (row < rows) {
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float t = rintf(x[it][j] * r);
+        t = fminf(fmaxf(t, -127.0f), 127.0f);
+        packed[j / 4] |= ((uint32_t)(int)t & 0xffu) << (8 * (j % 4));
+      }
+      *reinterpret_cast<uint2*>(dst + (size_t)(t0 + row) * D + cg * 8) = make_uint2(packed[0], packed[1]);
+    }
+  }
+  // the last block of a head zeroes the pad rows [N, Np)
+  if (b == nb - 1) {
+    const int npad = a.Np - a.N;
+    for (int e = tid; e < npad * (D / 8); e += kThreads) {
+      const int row = a.N + e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<uint2*>(dst + (size_t)row * D + c8 * 8) = make_uint2(0u, 0u);
+    }
+  }
+}
+
+// Pass 3 (variant 1): V -> FP8 E4M3 with per-channel scales, transposed to [G][D][Np].
+// One workgroup per (64-token tile, head); the tile goes through LDS so both the fp16
+// reads and the fp8 writes are contiguous.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __restrict__ v, int N, int Np,
+                                                           int nsplit, const float* __restrict__ vmax_part,
+                                                           uint8_t* __restrict__ v_f8,
+                                                           float* __restrict__ v_scale) {
+  constexpr int TPR = D / 8;
+  constexpr int RPI = kThreads / TPR;
+  constexpr int TT = 64;  // tokens per tile
+  __shared__ float s_r[D];
+  __shared__ uint8_t s_t[D][TT + 4];
+  const int tile = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  if (tid < D) {
+    float m = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, vmax_part[((size_t)g * nsplit + sp) * D + tid]);
+    s_r[tid] = m > 0.0f ? 448.0f / m : 0.0f;
+    if (tile == 0) v_scale[(size_t)g * D + tid] = m / 448.0f;
+  }
+  __syncthreads();
+  const int cg = tid % TPR, r0 = tid / TPR;
+  const size_t head = (size_t)g * N * D;
+  for (int rr = r0; rr < TT; rr += RPI) {
+    const int t = tile * TT + rr;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t < N) raw = *reinterpret_cast<const uint4*>(v + head + (size_t)t * D + cg * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x2 h = __builtin_bit_cast(f16x2, w[j]);
+      const int c = cg * 8 + 2 * j;
+      float y0 = fminf(fmaxf((float)h[0] * s_r[c], -448.0f), 448.0f);
+      float y1 = fminf(fmaxf((float)h[1] * s_r[c + 1], -448.0f), 448.0f);
+      const uint32_t p = cvt_pk_fp8(y0, y1, 0u, false);
+      s_t[c][rr] = (uint8_t)(p & 0xffu);
+      s_t[c + 1][rr] = (uint8_t)((p >> 8) & 0xffu);
+    }
+  }
+  __syncthreads();
+  // write D rows of 64 bytes: 4 threads per row, 16 bytes each
+  uint8_t* out = v_f8 + (size_t)g * D * Np + (size_t)tile * TT;
+  for (int e = tid; e < D * 4; e += kThreads) {
+    const int c = e / 4, part = e % 4;
+    uint32_t wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wv[q] = (uint32_t)s_t[c][part * 16 + 4 * q] | ((uint32_t)s_t[c][part * 16 + 4 * q + 1] << 8) |
+              ((uint32_t)s_t[c][part * 16 + 4 * q + 2] << 16) | ((uint32_t)s_t[c][part * 16 + 4 * q + 3] << 24);
+    *reinterpret_cast<uint4*>(out + (size_t)c * Np + part * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+int stat_splits(int N) { return (N + kStatRows - 1) / kStatRows; }
+
+hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long long* ksum_part,
+                        float* vmax_part, hipStream_t st) {
+  dim3 grid(stat_splits(N), G);
+  if (d == 64)
+    stats_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, stat_splits(N),
+                                                ksum_part, vmax_part);
+  else
+    stats_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, stat_splits(N),
+                                                 ksum_part, vmax_part);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t st) {
+  const int maxblk = a.blk_q > a.blk_k ? a.blk_q : a.blk_k;
+  const int grid = a.G * (a.nkb + a.nqb);
+  constexpr int RPI = kThreads / (D / 8);
+  if (maxblk <= 32 && 32 % RPI == 0)
+    quant_kernel<D, (32 > RPI ? 32 : RPI)><<<grid, kThreads, 0, st>>>(a);
+  else if (maxblk <= 64)
+    quant_kernel<D, 64><<<grid, kThreads, 0, st>>>(a);
+  else
+    quant_kernel<D, 128><<<grid, kThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st) {
+  return d == 64 ? launch_quant_d<64>(a, st) : launch_quant_d<128>(a, st);
+}
+
+hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const float* vmax_part,
+                          uint8_t* v_f8, float* v_scale, hipStream_t st) {
+  dim3 grid(Np / 64, G);
+  if (d == 64)
+    quant_v_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, stat_splits(N), vmax_part, v_f8,
+                                                  v_scale);
+  else
+    quant_v_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, stat_splits(N), vmax_part, v_f8,
+                                                   v_scale);
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (stated for this path): int8 Q/K codes, their scales and means, FP8 V codes and
+scales, and int32 Q K^T tiles bit-exact; O within max-abs 2e-3 and cosine >= 0.9999
+of the oracle's fp64 O.  Shapes: the five workloads at full size (O on sampled
+rows), plus small and ragged cases compared on every row.
+"""
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.ref64 import cos_sim
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_MAX_ABS = 2e-3
+TOL_COS = 0.9999
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sage():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_bit_attention_amd as s
+    s._load()
+    return s
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(cfg, **kw):
+    return workloads.make_inputs(cfg, **kw)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def cfg_kw(c):
+    return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"])
+
+
+def oracle_kw(c, bkv=64):
+    return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"], bkv=bkv,
+                smooth_k=c.get("smooth_k", 1), smooth_q=c.get("smooth_q", 1 if c["variant"] == 1 else 0))
+
+
+def check_o(name, g16, o64):
+    g = g16.astype(np.float64)
+    err = np.abs(g - o64)
+    mx = float(err.max())
+    c = cos_sim(g, o64)
+    say(f"  [{name}] O max_abs={mx:.3e} cos={c:.9f} n={o64.size}")
+    assert np.isfinite(g).all()
+    assert mx <= TOL_MAX_ABS, name
+    assert c >= TOL_COS, name
+
+
+def sample_rows(N, causal, rng, n_rand=24):
+    rows = {0, 1, min(2, N - 1), N - 1, max(0, N - 2)}
+    for r in (31, 32, 63, 64, 65, 127, 128, 129, 255, 256):
+        if r < N:
+            rows.add(r)
+    last_tile = (N - 1) // 128 * 128
+    rows.update(range(last_tile, min(N, last_tile + 4)))
+    rows.update(int(r) for r in rng.integers(0, N, n_rand))
+    return sorted(rows)
+
+
+# --------------------------------------------------------------------------
+# quantisation: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_quant_qk_bitexact(sage, orc, cfg):
+    c = inputs(cfg)
+    sq = 1 if c["variant"] == 1 else 0
+    say(f"quant_qk cfg{cfg} {c['q'].shape}")
+    g = sage.quant_qk(dev(c["q"]), dev(c["k"]), blk_q=c["blk_q"], blk_k=c["blk_k"], smooth_k=True, smooth_q=bool(sq))
+    g = {k: host(v) for k, v in g.items()}
+    r = orc.quant(c["q"], c["k"], blk_q=c["blk_q"], blk_k=c["blk_k"], smooth_k=1, smooth_q=sq)
+    for key in ("q_i8", "k_i8", "q_scale", "k_scale", "k_mean") + (("q_mean",) if sq else ()):
+        same = np.array_equal(g[key].view(np.uint8) if g[key].dtype == np.int8 else g[key].view(np.uint32),
+                              r[key].view(np.uint8) if r[key].dtype == np.int8 else r[key].view(np.uint32))
+        if not same:
+            diff = np.nonzero(g[key] != r[key])
+            say(f"  {key}: {len(diff[0])} mismatches, first at {[d[0] for d in diff]}")
+        assert same, key
+
+
+@pytest.mark.parametrize("case", ["cfg5", "ragged_d64", "ties"])
+def test_quant_v_bitexact(sage, orc, case):
+    if case == "cfg5":
+        v = inputs(5)["v"]
+    elif case == "ragged_d64":
+        v = workloads.make_inputs(1, N=333, B=1, H=3)["v"]
+    else:
+        # every channel's absmax is 448, so the scale is 1 and the codes are E4M3(V):
+        # the values are all E4M3 ties, their fp16 neighbours and the codes themselves
+        codes = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+        pos = np.unique(codes[np.isfinite(codes) & (codes >= 0)])
+        mids = 0.5 * (pos[1:] + pos[:-1])
+        vals = np.concatenate([pos, mids, -mids])
+        vals16 = vals.astype(np.float16)
+        up = np.nextafter(vals16, np.float16(np.inf))
+        dn = np.nextafter(vals16, np.float16(-np.inf))
+        allv = np.concatenate([vals16, up, dn, -vals16])
+        allv = allv[np.abs(allv.astype(np.float64)) <= 448]
+        n = -(-allv.size // 64) * 64
+        col = np.zeros(n, np.float16)
+        col[:allv.size] = allv
+        col[0] = 448
+        v = np.tile(col[:, None], (1, 64))[None, None].copy()
+        v[0, 0, :, 1::2] *= np.float16(-1)
+        v = v.astype(np.float16)
+    say(f"quant_v {case} {v.shape}")
+    g = sage.quant_v(dev(v))
+    r = orc.quant(v, v, v, with_v=True)
+    assert np.array_equal(host(g["v_scale"]).view(np.uint32), r["v_scale"].view(np.uint32))
+    gv = host(g["v_f8"])
+    if not np.array_equal(gv, r["v_f8"]):
+        bad = np.nonzero(gv != r["v_f8"])
+        say(f"  v_f8 mismatches: {len(bad[0])} first {[b[0] for b in bad]}")
+    assert np.array_equal(gv, r["v_f8"])
+
+
+# --------------------------------------------------------------------------
+# int32 Q K^T tiles: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_qk_int32_tiles(sage, orc, cfg):
+    c = inputs(cfg)
+    B, H, N, d = c["q"].shape
+    r = orc.quant(c["q"], c["k"], blk_q=c["blk_q"], blk_k=c["blk_k"], smooth_k=1,
+                  smooth_q=1 if c["variant"] == 1 else 0)
+    Np = r["q_i8"].shape[2]
+    nqt, nkt = Np // 128, Np // 64
+    if cfg == 1:
+        tiles = [(g, qt, kt) for g in range(B * H) for qt in range(nqt) for kt in range(nkt)]
+    else:
+        tiles = []
+        for g in (0, B * H - 1):
+            tiles += [(g, 0, 0), (g, nqt - 1, nkt - 1), (g, nqt - 1, 0), (g, 0, nkt - 1),
+                      (g, nqt // 2, nkt // 2), (g, nqt // 2, nkt // 2 + 1)]
+    say(f"qk_int32 cfg{cfg} {len(tiles)} tiles")
+    qi, ki = r["q_i8"].reshape(B * H, Np, d), r["k_i8"].reshape(B * H, Np, d)
+    got = host(sage.debug_qk_int32(dev(r["q_i8"]), dev(r["k_i8"]), N, tiles))
+    for n, (g, qt, kt) in enumerate(tiles):
+        ref = orc.qk_int32(qi[g], ki[g], qt * 128, 128, kt * 64, 64)
+        assert np.array_equal(got[n], ref), (g, qt, kt)
+    # an entry outside the tensors gives zeros instead of reading past them
+    got = host(sage.debug_qk_int32(dev(r["q_i8"]), dev(r["k_i8"]), N, [(B * H, 0, 0), (0, nqt, 0)]))
+    assert not got.any()
+
+
+# --------------------------------------------------------------------------
+# O: within tolerance
+# --------------------------------------------------------------------------
+
+def run_gpu(sage, c, **over):
+    kw = cfg_kw(c)
+    kw.update(over)
+    o = sage.attn(dev(c["q"]), dev(c["k"]), dev(c["v"]), **kw)
+    return host(o)
+
+
+def test_attn_config1_all_rows(sage, orc):
+    c = inputs(1)
+    say("attn cfg1 all rows")
+    g = run_gpu(sage, c)
+    o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
+    check_o("cfg1", g, o)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_attn_full_size_sampled_rows(sage, orc, cfg):
+    c = inputs(cfg)
+    B, H, N, d = c["q"].shape
+    G = B * H
+    say(f"attn cfg{cfg} full size {c['q'].shape} causal={c['causal']} variant={c['variant']}")
+    g = run_gpu(sage, c).reshape(G, N, d)
+    rng = np.random.default_rng(cfg)
+    heads, rows = [], []
+    for hd in (0, G // 2 + 1, G - 1):
+        for r in sample_rows(N, c["causal"], rng):
+            heads.append(hd)
+            rows.append(r)
+    o = orc.attn_rows(c["q"], c["k"], c["v"], heads, rows, **oracle_kw(c))
+    check_o(f"cfg{cfg} sampled {len(rows)} rows", g[heads, rows], o)
+
+
+EDGE = [
+    # name, recipe cfg, overrides of shape, attention options
+    ("n1_v0", 1, dict(N=1, B=1, H=1), dict(causal=0, variant=0)),
+    ("n1_v1_causal", 5, dict(N=1, B=1, H=1), dict(causal=1, variant=1)),
+    ("n17_causal_d64", 1, dict(N=17, B=1, H=2), dict(causal=1, variant=0)),
+    ("n65_d128", 2, dict(N=65, B=1, H=2), dict(causal=0, variant=0)),
+    ("n129_causal_d128", 2, dict(N=129, B=2, H=1), dict(causal=1, variant=0)),
+    ("n200_v1_d64", 1, dict(N=200, B=1, H=2), dict(causal=0, variant=1)),
+    ("n333_v1_causal", 5, dict(N=333, B=1, H=2), dict(causal=1, variant=1)),
+    ("blk32_16", 2, dict(N=300, B=1, H=2), dict(causal=1, variant=0, blk_q=32, blk_k=16)),
+    ("blk64_128", 3, dict(N=520, B=1, H=2), dict(causal=0, variant=0, blk_q=64, blk_k=128)),
+    ("blk32_v1_smoothq", 5, dict(N=400, B=1, H=2), dict(causal=0, variant=1, blk_q=32, blk_k=32)),
+    ("nosmooth", 1, dict(N=256, B=1, H=2), dict(causal=0, variant=0, smooth_k=0)),
+    ("v0_smoothq", 2, dict(N=256, B=1, H=2), dict(causal=1, variant=0, smooth_q=1)),
+    ("v1_no_smoothq", 5, dict(N=256, B=1, H=2), dict(causal=1, variant=1, smooth_q=0)),
+]
+
+
+@pytest.mark.parametrize("name,cfg,shape,opt", EDGE, ids=[e[0] for e in EDGE])
+def test_attn_edge_cases_all_rows(sage, orc, name, cfg, shape, opt):
+    c = dict(workloads.config(cfg))
+    c.update(workloads.make_inputs(cfg, **shape))
+    c.update(opt)
+    say(f"attn edge {name} {c['q'].shape} {opt}")
+    kw = cfg_kw(c)
+    kw["smooth_k"] = bool(c.get("smooth_k", 1))
+    kw["smooth_q"] = bool(c.get("smooth_q", 1 if c["variant"] == 1 else 0))
+    g = host(sage.attn(dev(c["q"]), dev(c["k"]), dev(c["v"]), **kw))
+    o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
+    check_o(name, g, o)
+
+
+def test_attn_q_offset_stress_variant1(sage, orc):
+    """Q with a large per-channel offset: the Q-smoothing term carries real weight."""
+    c = dict(workloads.config(5))
+    c.update(workloads.make_inputs(5, N=2048, B=1, H=2, q_sigma=4.0))
+    say("attn v1 q-offset stress N=2048")
+    g = run_gpu(sage, c)
+    o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
+    check_o("q_offset_v1", g, o)
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_attn_degenerate_inputs(sage, orc, variant):
+    """Q = 0 (uniform attention) and constant K (zero codes after smoothing)."""
+    rng = np.random.default_rng(5)
+    N, d = 150, 64
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    for name, (qq, kk) in {"q_zero": (np.zeros_like(q), k), "k_const": (q, np.full_like(k, 1.5))}.items():
+        for causal in (0, 1):
+            say(f"attn degenerate {name} variant={variant} causal={causal}")
+            g = host(sage.attn(dev(qq), dev(kk), dev(v), causal=bool(causal), variant=variant))
+            o = orc.attn(qq, kk, v, causal=causal, variant=variant)
+            check_o(f"{name} v{variant} c{causal}", g, o)
+
+
+def test_prequant_matches_whole_call_and_is_deterministic(sage):
+    c = inputs(2)
+    say("prequant vs whole call, determinism (cfg2)")
+    q, k, v = dev(c["q"]), dev(c["k"]), dev(c["v"])
+    a = sage.attn(q, k, v, **cfg_kw(c))
+    b = sage.attn(q, k, v, **cfg_kw(c))
+    qk = sage.quant_qk(q, k, blk_q=c["blk_q"], blk_k=c["blk_k"])
+    p = sage.attn_prequant(qk, v, c["q"].shape[2], causal=True, variant=0, blk_q=c["blk_q"], blk_k=c["blk_k"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, p)
+
+
+def test_api_rejects_bad_arguments_on_gpu(sage):
+    q = torch.zeros((1, 1, 64, 96), dtype=torch.float16, device="cuda")
+    with pytest.raises(sage.SageError, match="head dim"):
+        sage.attn(q, q, q)
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(sage.SageError, match="sm_scale"):
+        sage.attn(q, q, q, sm_scale=-1.0)
+    with pytest.raises(sage.SageError, match="blk_q"):
+        sage.attn(q, q, q, blk_q=48)

@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/sage.h declares, and reject
+bad arguments with the documented status before touching the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_bit_attention_amd as sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+P = ctypes.c_void_p
+A = P(0x10000)          # aligned, never dereferenced: every call below fails validation first
+MIS = P(0x10002)        # misaligned
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sage.library_path()):
+        pytest.skip("libsage.so not built")
+    return sage._load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_header():
+    src = open(HEADER).read()
+    codes = dict(re.findall(r"(SAGE_\w+)\s*=\s*(-?\d+)", src))
+    assert codes["SAGE_OK"] == "0" and codes["SAGE_ERR_INVALID_ARG"] == "-1"
+    assert codes["SAGE_ERR_UNSUPPORTED"] == "-2" and codes["SAGE_ERR_WORKSPACE"] == "-3"
+    assert codes["SAGE_ERR_HIP"] == "-4"
+
+
+def test_pure_helpers(lib):
+    assert lib.sage_pad_len(1) == 128 and lib.sage_pad_len(128) == 128 and lib.sage_pad_len(17776) == 17792
+    assert lib.sage_pad_len(0) == -1
+    assert lib.sage_kv_tile(0, 64) == 64 and lib.sage_kv_tile(1, 128) == 64
+    assert lib.sage_kv_tile(2, 64) < 0 and lib.sage_kv_tile(0, 96) < 0
+    assert lib.sage_version() >= 100
+
+
+def test_workspace_size(lib):
+    # variant 0, config-2 shape: int64 partial sums + int8 Q/K + scales + k_mean (each piece 256-aligned)
+    B, H, N, d = 4, 32, 4096, 128
+    G, Np = B * H, 4096
+    up = lambda x: (x + 255) // 256 * 256
+    expect = (up(G * 8 * d * 8) + up(G * Np * d) * 2 + up(G * 32 * 4) + up(G * 64 * 4) + up(G * d * 4))
+    assert sage.workspace_bytes(B, H, N, d, 0) == expect
+    assert sage.workspace_bytes(B, H, N, d, 1) > expect   # V in FP8 + q means
+    assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
+    assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
+
+
+def attn(lib, q=A, k=A, v=A, o=A, B=1, H=1, N=64, d=64, causal=0, sm=0.125, variant=0, ws=A, wsb=1 << 30,
+         params=None):
+    if params is None:
+        return lib.sage_attn_fwd(q, k, v, o, B, H, N, d, causal, sm, variant, ws, wsb, None)
+    return lib.sage_attn_fwd_ex(q, k, v, o, B, H, N, d, causal, sm, variant, ctypes.byref(params), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(d=96), -2, "head dim"),
+    (dict(d=32), -2, "head dim"),
+    (dict(N=0), -1, "N must be"),
+    (dict(B=0), -1, "B, H, N"),
+    (dict(B=1 << 12, H=1 << 8, N=1 << 10, d=128), -1, "2^31"),
+    (dict(causal=2), -1, "causal"),
+    (dict(variant=2), -1, "variant"),
+    (dict(sm=0.0), -1, "sm_scale"),
+    (dict(sm=float("nan")), -1, "sm_scale"),
+    (dict(sm=float("inf")), -1, "sm_scale"),
+    (dict(q=None), -1, "q is NULL"),
+    (dict(v=MIS), -1, "aligned"),
+    (dict(o=None), -1, "o is NULL"),
+    (dict(ws=None), -3, "workspace"),
+    (dict(wsb=16), -3, "too small"),
+    (dict(ws=P(0x10010)), -3, "256-byte"),
+])
+def test_attn_rejects(lib, kw, code, msg):
+    assert attn(lib, **kw) == code
+    assert msg in lib.sage_last_error().decode()
+
+
+def test_params_rejected(lib):
+    p = sage._params(blk_q=48)
+    assert attn(lib, params=p) == -2 and b"blk_q" in lib.sage_last_error()
+    p = sage._params(blk_k=8)
+    assert attn(lib, params=p) == -2 and b"blk_k" in lib.sage_last_error()
+    p = sage._params()
+    p.struct_size = 4
+    assert attn(lib, params=p) == -1 and b"struct_size" in lib.sage_last_error()
+    p = sage._params()
+    p.smooth_k = 3
+    assert attn(lib, params=p) == -1
+
+
+def test_other_entry_points_reject(lib):
+    I = ctypes.c_int
+    # quant_qk: q_mean required when smooth_q is on
+    p = sage._params(smooth_q=True)
+    rc = lib.sage_quant_qk(A, A, 1, 1, 64, 64, ctypes.byref(p), A, A, A, A, A, None, A, 1 << 20, None)
+    assert rc == -1 and b"q_mean" in lib.sage_last_error()
+    rc = lib.sage_quant_qk(A, A, 1, 1, 64, 64, None, A, A, A, A, A, None, None, 1 << 20, None)
+    assert rc == -3
+    rc = lib.sage_quant_v(A, 1, 1, 64, 64, A, MIS, A, 1 << 20, None)
+    assert rc == -1
+    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, A, 1, 1, 64, 64, 0, 0.125, 1, None, None)
+    assert rc == -1 and b"q_mean" in lib.sage_last_error()       # variant 1 smooths Q by default
+    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, A, 1, 1, 64, 64, 0, 0.125, 0, None, None)
+    assert rc == -1 and b"v is NULL" in lib.sage_last_error()
+    rc = lib.sage_debug_qk_int32(A, A, 1, 1, 64, 64, A, 0, A, None)
+    assert rc == -1 and b"n_tiles" in lib.sage_last_error()
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 1, 8, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        sage.attn(x, x, x)
+    with pytest.raises(TypeError):
+        sage.attn(x.float(), x, x)
