@@ -62,7 +62,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads of the workload the oracle runs")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the workload the oracle runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -114,6 +116,14 @@ def main():
     a1.record(stream)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / args.steps
+
+    if args.copy_calibration:
+        # known traffic: reads 1 GiB, writes 1 GiB; its FETCH_SIZE / WRITE_SIZE scale the counters
+        src_t = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     value = ops / (ms * 1e-3) / 1e12
     attn_tops = ops / (attn_ms * 1e-3) / 1e12

@@ -22,117 +22,180 @@
 //    (variant 1, v_mfma_f32_32x32x64_f8f6f4).
 //  - Causal: tiles past a wave's last row are skipped; workgroups run
 //    longest-first and consecutive workgroups of one head stay on one XCD.
+#include <type_traits>
+
 #include "sage_device.h"
 #include "sage_internal.h"
 
 namespace sage {
 
+constexpr int kAttnWaves = 4;                     // waves per attention workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnRows = 32 * kAttnWaves;        // query rows per attention workgroup
+constexpr int kDbgWaves = 4;                      // the int32 test kernel: 128 x 64 tiles
+
+// LDS tiles are written straight from memory (global_load_lds_dwordx4 /
+// buffer_load_dwordx4 ... lds: lane l of a wave writes 16 bytes at base + 16*l), so a
+// tile is an array of 16-byte slots whose order the copy chooses freely.  Each tile
+// is stored in the order the MFMA operand reads consume it: every read pass of a wave
+// (8 lanes of ds_read_b128, 16 lanes of ds_read_b64_tr_b16) covers one contiguous
+// 128-byte run, which is free of bank conflicts, and every operand address is the
+// lane's base plus a compile-time offset.
 template <int D, int VARIANT>
 struct Lds {
-  static constexpr int KROW = D + 16;            // bytes per K row (padding breaks bank conflicts)
-  static constexpr int VROW = D + 16;            // halves per V row (variant 0)
-  static constexpr int VTROW = kTileKV + 16;     // bytes per V^T row (variant 1)
-  static constexpr int K_BYTES = kTileKV * KROW;
-  static constexpr int V_BYTES = VARIANT == 0 ? kTileKV * VROW * 2 : D * VTROW;
-  static constexpr int K_CHUNKS = kTileKV * D / 16 / kThreads;                          // 16 B per thread
-  static constexpr int V_CHUNKS = (VARIANT == 0 ? kTileKV * D * 2 : D * kTileKV) / 16 / kThreads;
+  static constexpr int K_BYTES = kTileKV * D;                     // 64 keys x D int8
+  static constexpr int V_BYTES = VARIANT == 0 ? kTileKV * D * 2   // 64 keys x D fp16
+                                              : D * kTileKV;      // D channels x 64 keys fp8
 };
 
 // Row of the K tile that feeds A-operand row r: accumulator register i of lane half h
 // then holds key 16h + i of the 32-key block.
 __device__ __forceinline__ int k_perm(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
-template <int D, int VARIANT>
-__device__ __forceinline__ void load_k_tile(const int8_t* __restrict__ kh, int t, i32x4* reg) {
-  using L = Lds<D, VARIANT>;
-#pragma unroll
-  for (int i = 0; i < L::K_CHUNKS; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-    reg[i] = *reinterpret_cast<const i32x4*>(kh + (size_t)(t * kTileKV + row) * D + col);
-  }
-}
-template <int D, int VARIANT>
-__device__ __forceinline__ void store_k_tile(int8_t* sK, const i32x4* reg) {
-  using L = Lds<D, VARIANT>;
-#pragma unroll
-  for (int i = 0; i < L::K_CHUNKS; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    const int row = c / (D / 16), col = (c % (D / 16)) * 16;
-    *reinterpret_cast<i32x4*>(sK + row * L::KROW + col) = reg[i];
-  }
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// V tile t into registers.  Variant 0: fp16 rows [key][D] of the caller's V, keys >= N
-// read as zero.  Variant 1: FP8 V^T rows [channel][64 keys] of the padded tensor.
-template <int D, int VARIANT>
-__device__ __forceinline__ void load_v_tile(const void* __restrict__ vh, int t, int N, int Np, i32x4* reg) {
-  using L = Lds<D, VARIANT>;
-#pragma unroll
-  for (int i = 0; i < L::V_CHUNKS; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    if (VARIANT == 0) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = t * kTileKV + row;
-      reg[i] = key < N ? *reinterpret_cast<const i32x4*>((const uint16_t*)vh + (size_t)key * D + col)
-                       : i32x4{0, 0, 0, 0};
-    } else {
-      const int row = c / 4, col = (c % 4) * 16;
-      reg[i] = *reinterpret_cast<const i32x4*>((const uint8_t*)vh + (size_t)row * Np + t * kTileKV + col);
-    }
-  }
-}
-template <int D, int VARIANT>
-__device__ __forceinline__ void store_v_tile(uint8_t* sV, const i32x4* reg) {
-  using L = Lds<D, VARIANT>;
-#pragma unroll
-  for (int i = 0; i < L::V_CHUNKS; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    if (VARIANT == 0) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<i32x4*>(sV + (row * L::VROW + col) * 2) = reg[i];
-    } else {
-      const int row = c / 4, col = (c % 4) * 16;
-      *reinterpret_cast<i32x4*>(sV + row * L::VTROW + col) = reg[i];
-    }
-  }
-}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Q operand (B of S^T = K Q^T) for this lane's query row: D/32 k-steps of 16 bytes.
+// K tile: slot (st*CPR + c)*32 + x holds bytes 16c..16c+15 of key 32*st + k_perm(x),
+// x = A-operand row.  Lane l of the operand read for 32-key block st, k-step ks, is
+// at 16*l + (st*CPR + 2*ks)*512.
 template <int D>
-__device__ __forceinline__ void load_q_operand(const int8_t* __restrict__ qh, int row, int h, i32x4* qop) {
+__device__ __forceinline__ int k_slot(int key, int chunk) {
+  constexpr int CPR = D / 16;
+  return ((key >> 5) * CPR + chunk) * 32 + 8 * ((key >> 2) & 3) + 4 * ((key >> 4) & 1) + (key & 3);
+}
+
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                              void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// Source offsets of the tile copies.  The waves of the workgroup split a tile's 1 KB
+// copy instructions round-robin; copy i of a wave starts (i * NWAVES) KB after its
+// first one in LDS and a fixed number of bytes after it in memory, so each lane keeps
+// one base offset per tensor, and tile t adds a uniform t * (bytes per tile).
+template <int D, int VARIANT, int NWAVES>
+struct TileCopy {
+  static constexpr int CPR = D / 16;
+  static constexpr int K_COPIES = kTileKV * CPR / 64;                                      // 1 KB each
+  static constexpr int V_COPIES = (VARIANT == 0 ? kTileKV * 2 * D : D * kTileKV) / 16 / 64;
+  static constexpr int K_PER_WAVE = (K_COPIES + NWAVES - 1) / NWAVES;
+  static constexpr int V_PER_WAVE = (V_COPIES + NWAVES - 1) / NWAVES;
+  // memory distance between copy c and copy c + NWAVES of a lane (see the layouts above)
+  static constexpr uint32_t K_STEP = (uint32_t)((NWAVES * 2) / CPR) * 32 * D;
+  static constexpr uint32_t V_STEP = VARIANT == 0 ? (uint32_t)(NWAVES * 8 / (D / 16)) * 4 * 2 * D
+                                                  : (uint32_t)(NWAVES * 2 / 4) * 32;  // channels (x Np)
+  uint32_t koff, voff;
+
+  __device__ __forceinline__ TileCopy(int Np) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    {
+      const int s = (wave % K_COPIES) * 64 + lane;
+      const int x = s & 31, rest = s >> 5;
+      koff = (uint32_t)(32 * (rest / CPR) + k_perm(x)) * D + (rest % CPR) * 16;
+    }
+    {
+      const int s = (wave % V_COPIES) * 64 + lane;
+      if (VARIANT == 0) {
+        constexpr int BPR = D / 16;
+        const int w = s & 7, blk = s >> 3;
+        voff = (uint32_t)(4 * (blk / BPR) + (w >> 1)) * (2 * D) + 2 * (16 * (blk % BPR) + 8 * (w & 1));
+      } else {
+        const int y = s & 31, rest = s >> 5;
+        voff = (uint32_t)(32 * (rest >> 2) + y) * Np + 16 * (rest & 3);
+      }
+    }
+    static_assert((NWAVES * 2) % CPR == 0, "K copies of one wave must step by whole 32-key blocks");
+    static_assert(VARIANT != 0 || (NWAVES * 8) % (D / 16) == 0, "V copies must step by whole key rows");
+    static_assert(VARIANT == 0 || (NWAVES * 2) % 4 == 0, "V^T copies must step by whole channel rows");
+  }
+
+  // K tile t of the padded int8 tensor (resource over this head).
+  __device__ __forceinline__ void k_tile(__amdgpu_buffer_rsrc_t krs, int t, int8_t* sK) const {
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qop[ks] = *reinterpret_cast<const i32x4*>(qh + (size_t)row * D + 32 * ks + 16 * h);
+    for (int i = 0; i < K_PER_WAVE; ++i) {
+      const int c = i * NWAVES + wave;
+      if (K_COPIES % NWAVES == 0 || c < K_COPIES)
+        copy16_to_lds(krs, koff + i * K_STEP, (uint32_t)(t * kTileKV * D), sK + c * 1024);
+    }
+  }
+  // V tile t.  Variant 0 puts the whole offset in the lane offset so keys >= N fall
+  // outside the resource and land as zeros.
+  __device__ __forceinline__ void v_tile(__amdgpu_buffer_rsrc_t vrs, int t, int Np, uint8_t* sV) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < V_PER_WAVE; ++i) {
+      const int c = i * NWAVES + wave;
+      if (V_COPIES % NWAVES == 0 || c < V_COPIES) {
+        if (VARIANT == 0)
+          copy16_to_lds(vrs, voff + i * V_STEP + (uint32_t)(t * kTileKV * 2 * D), 0u, sV + c * 1024);
+        else
+          copy16_to_lds(vrs, voff + i * V_STEP * (uint32_t)Np, (uint32_t)(t * kTileKV), sV + c * 1024);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (uint32_t)bytes, 0x00020000);
+}
+
+// Q operand (B of S^T = K Q^T): each wave copies its 32 query rows into LDS once, as
+// D/32 runs of 64 lanes x 16 bytes (lane l: row l%32, bytes 32*ks + 16*(l/32)), so the
+// operand read of k-step ks is at wave base + ks*1024 + 16*l.
+template <int D>
+__device__ __forceinline__ void load_q_tile(__amdgpu_buffer_rsrc_t qrs, int row0, int8_t* sQw) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t off = (uint32_t)(row0 + (lane & 31)) * D + 16 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) copy16_to_lds(qrs, off + 32 * ks, 0u, sQw + ks * 1024);
 }
 
 // S^T for the 64-key tile in LDS: s[st][i] = Qhat[query l%32] . Khat[key 32*st + 16h + i]
 // (exact int32).
-template <int D, int VARIANT>
-__device__ __forceinline__ void qk_tile(const int8_t* sK, const i32x4* qop, int lane, i32x16* s) {
-  using L = Lds<D, VARIANT>;
-  const int ql = lane & 31, h = lane >> 5;
-  const int pr = k_perm(ql);
+template <int D>
+__device__ __forceinline__ void qk_tile(const int8_t* sK, const int8_t* sQw, int lane, i32x16* s) {
+  constexpr int CPR = D / 16;
+  const int8_t* kbase = sK + 16 * lane;
+  const int8_t* qbase = sQw + 16 * lane;
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     i32x16 acc = {};
-    const int8_t* kr = sK + (32 * st + pr) * L::KROW + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      acc = mfma_i8(*reinterpret_cast<const i32x4*>(kr + 32 * ks), qop[ks], acc);
+      acc = mfma_i8(*reinterpret_cast<const i32x4*>(kbase + (st * CPR + 2 * ks) * 512),
+                    *reinterpret_cast<const i32x4*>(qbase + ks * 1024), acc);
     s[st] = acc;
   }
 }
 
+// 16 bytes of key `key`, chunk `chunk16`, of the K tile.
+template <int D>
+__device__ __forceinline__ const int8_t* k_lds_chunk(const int8_t* sK, int key, int chunk16) {
+  return sK + 16 * k_slot<D>(key, chunk16);
+}
+
+// Rescaling of the running O is skipped while the row max grows by at most 2^8
+// (variant 0 only): P~ is then computed against the older max and may reach 256,
+// which fp16 and the fp32 sums hold exactly as well.
+constexpr float kLazyLog2 = 8.0f;
+
 // Online-softmax update for one 64-key tile of one lane (one query, 32 keys:
 // s[st][i] is key kl + 32*st + i).  Works in the exp2 domain: x = S * c (+ bias),
-// c = dQ * dK * sm_scale * log2(e).  Updates the running max m and the lane's partial
-// sum l (the lane pair l, l^32 shares m; l is summed over the pair at the end), writes
-// P~ (variant 0) or P~ * 448 (variant 1, ready for FP8) and the rescale factor alpha.
+// c = dQ * dK * sm_scale * log2(e).  Updates the reference max m and the lane's
+// partial sum l (the lane pair l, l^32 shares m; l is summed over the pair at the
+// end) and writes P~ already packed as the B operand of the P~V product:
+//  variant 0: pk[st*8 + u*4 + q] = fp16 pair (P~ of keys 8u+2q, 8u+2q+1 of block st);
+//  variant 1: pk[st*4 + w] = four E4M3 codes of P~ * 448 (keys 4w..4w+3 of block st).
+// alpha is the factor the running O must be scaled by (rescale is false for the whole
+// wave when no lane needs it).
 // MASK: keys >= N, and keys > qi when causal, get P~ = 0 and stay out of the max.
 template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK>
 __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, const float* bias, int kl, int N,
-                                             int qi, float& m, float& l, float (&p)[2][16], float& alpha) {
+                                             int qi, float& m, float& l, uint32_t* pk, float& alpha,
+                                             bool& rescale) {
   auto keep = [&](int st, int i) {
     const int key = kl + 32 * st + i;
     return !MASK || (key < N && (!CAUSAL || key <= qi));
@@ -162,33 +225,115 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
     mt = fmaxf(m0, m1);
   }
   mt = pair_max(mt);
-  const float mnew = fmaxf(m, mt);  // finite: key 0 (tile 0) is visible to every row
-  alpha = exp2f(m - mnew);
+  // m is finite after the first tile: key 0 is visible to every row
+  if (VARIANT == 0) {
+    rescale = __builtin_amdgcn_ballot_w64(mt > m + kLazyLog2) != 0;
+  } else {
+    rescale = true;  // P~ * 448 must stay <= 448 for FP8
+  }
+  // branch-free so the caller's fast path stays one basic block
+  const float mnew = rescale ? fmaxf(m, mt) : m;
+  alpha = rescale ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;  // exp2(-inf) = 0 on the first tile
   m = mnew;
-  const float shift = VARIANT == 0 ? -mnew : kLog2_448 - mnew;
+  l *= alpha;
+  const float shift = VARIANT == 0 ? -m : kLog2_448 - m;
   float psum = 0.0f;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = SMOOTHQ ? x[st][i] + shift : fmaf((float)s[st][i], c[st], shift);
-      float pv = __builtin_amdgcn_exp2f(e);
-      if (MASK) pv = keep(st, i) ? pv : 0.0f;
-      p[st][i] = pv;
-      psum += pv;
+    for (int i = 0; i < 16; i += 4) {
+      float pv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = SMOOTHQ ? x[st][i + j] + shift : fmaf((float)s[st][i + j], c[st], shift);
+        pv[j] = __builtin_amdgcn_exp2f(e);
+        if (MASK) pv[j] = keep(st, i + j) ? pv[j] : 0.0f;
+        psum += pv[j];
+      }
+      if constexpr (VARIANT == 0) {
+        pk[st * 8 + i / 2] = pack_f16x2(pv[0], pv[1]);
+        pk[st * 8 + i / 2 + 1] = pack_f16x2(pv[2], pv[3]);
+      } else {
+        pk[st * 4 + i / 4] = cvt_pk_fp8(pv[2], pv[3], cvt_pk_fp8(pv[0], pv[1], 0u, false), true);
+      }
     }
-  l = alpha * l + psum;
+  l += psum;
+}
+
+// K scales of this lane's two 32-key blocks of tile t.
+__device__ __forceinline__ void tile_kscales(const AttnArgs& a, const float* ksc, int t, int h, float* kr) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int kb = min(t * kTileKV + 32 * st + 16 * h, a.N - 1) / a.blk_k;
+    kr[st] = ksc[kb];
+  }
+}
+
+// Q-smoothing term of every key of tile t for each Q block of the workgroup:
+// bias[sb][j] = sm_scale*log2(e) * dK_j * (qmean_sb . Khat_j), in fp32.
+template <int D>
+__device__ __forceinline__ void smooth_q_bias(const AttnArgs& a, const float* ksc, const int8_t* sK,
+                                              const float* sQm, float* sBias, int t) {
+  constexpr int CH = D / 32;  // 32-channel chunks per key, summed across adjacent lanes
+  const int nsub = kAttnRows / a.blk_q;
+  for (int item = threadIdx.x; item < nsub * kTileKV * CH; item += kAttnThreads) {
+    const int chunk = item % CH, key = (item / CH) % kTileKV, sb = item / (CH * kTileKV);
+    const float* qm = sQm + sb * D + chunk * 32;
+    float acc = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int8_t* kr = k_lds_chunk<D>(sK, key, 2 * chunk + half);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc = fmaf(qm[16 * half + c], (float)kr[c], acc);
+    }
+    for (int off = 1; off < CH; off <<= 1) acc += __shfl_xor(acc, off);
+    if (chunk == 0) {
+      const int kj = min(t * kTileKV + key, a.N - 1);
+      sBias[sb * kTileKV + key] = a.kscale * ksc[kj / a.blk_k] * acc;
+    }
+  }
+}
+
+// Instruction order of the interior-tile block: after a few operand reads, each MFMA
+// is followed by the LDS reads for the next one and a share of the softmax's VALU
+// instructions, which execute while the MFMA occupies the matrix unit.  (Written as
+// loops without conditionals: a guarded sched_group_barrier is not honoured.)
+template <int D, int VARIANT>
+__device__ __forceinline__ void interleave_schedule() {
+  constexpr int QK_MFMA = 2 * (D / 32);                          // two 16-byte reads each (K, Q)
+  constexpr int PV_MFMA = VARIANT == 0 ? 4 * (D / 32) : D / 32;  // two reads each
+  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13) : (D == 128 ? 12 : 20);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < QK_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < PV_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+  }
 }
 
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   using L = Lds<D, VARIANT>;
   constexpr int NCT = D / 32;                       // 32-channel output tiles
-  constexpr int NSUB = SMOOTHQ ? 4 : 1;             // Q blocks a workgroup can span (blk_q >= 32)
-  __shared__ __attribute__((aligned(16))) int8_t sK[L::K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[L::V_BYTES];
+  constexpr int NSUB = SMOOTHQ ? kAttnRows / 32 : 1;  // Q blocks a workgroup can span (blk_q >= 32)
+  // Two slots per tile kind, as separate LDS objects: the loop body is instantiated
+  // per slot parity, so the compiler can tell the slot being filled by an in-flight
+  // copy from the slot being read and does not wait for the copy.
+  __shared__ __attribute__((aligned(16))) int8_t sK0[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) int8_t sK1[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[L::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[L::V_BYTES];
+  __shared__ __attribute__((aligned(16))) int8_t sQ[kAttnRows * D];
   __shared__ __attribute__((aligned(16))) float sQm[SMOOTHQ ? NSUB * D : 1];
-  __shared__ float sBias[SMOOTHQ ? NSUB * kTileKV : 1];
+  __shared__ float sBias0[SMOOTHQ ? NSUB * kTileKV : 1];
+  __shared__ float sBias1[SMOOTHQ ? NSUB * kTileKV : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, ql = lane & 31;
@@ -197,38 +342,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   // workgroup -> (head, query tile).  Consecutive workgroup ids go round-robin over the
   // 8 XCDs; remap so each XCD walks a contiguous range of (head, tile) pairs, heads
   // one after another, and for causal the longest tiles of a head first.
-  const int nqt = a.Np / kBlockQ;
+  const int nqt = (a.Np + kAttnRows - 1) / kAttnRows;
   const int total = a.G * nqt;
   int vid = blockIdx.x;
   if ((total & 7) == 0) vid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int g = vid / nqt;
   const int qt = CAUSAL ? nqt - 1 - vid % nqt : vid % nqt;
-  const int q0 = qt * kBlockQ;
+  const int q0 = qt * kAttnRows;
   const int qw = q0 + 32 * wave;  // first row of this wave
   const int qi = qw + ql;         // this lane's query row
   const bool wave_active = qw < N;
 
   const int8_t* __restrict__ qh = a.q_i8 + (size_t)g * a.Np * D;
   const int8_t* __restrict__ kh = a.k_i8 + (size_t)g * a.Np * D;
-  const void* vh = VARIANT == 0 ? (const void*)(a.v + (size_t)g * N * D)
-                                : (const void*)(a.v_f8 + (size_t)g * D * a.Np);
   const float* __restrict__ ksc = a.k_scale + (size_t)g * a.nkb;
 
   const int ntiles_all = (N + kTileKV - 1) / kTileKV;
-  const int wg_last_row = min(q0 + kBlockQ - 1, N - 1);
-  const int ntiles = CAUSAL ? min(ntiles_all, wg_last_row / kTileKV + 1) : ntiles_all;
-  const int wave_last_tile = CAUSAL ? min(ntiles_all - 1, min(qw + 31, N - 1) / kTileKV) : ntiles_all - 1;
+  const int wg_last_row = min(q0 + kAttnRows - 1, N - 1);
+  const int T = CAUSAL ? min(ntiles_all, wg_last_row / kTileKV + 1) : ntiles_all;
+  const int wave_last = CAUSAL ? min(ntiles_all - 1, min(qw + 31, N - 1) / kTileKV) : ntiles_all - 1;
 
-  i32x4 qop[D / 32];
-  load_q_operand<D>(qh, qi, h, qop);
+  int8_t* const sQw = sQ + wave * (D / 32) * 1024;
+  // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
+  if (wave_active) load_q_tile<D>(make_rsrc(qh, (size_t)a.Np * D), qw, sQw);
   const float dq = wave_active ? a.q_scale[(size_t)g * a.nqb + qw / a.blk_q] : 0.0f;
 
   if (SMOOTHQ) {
     // block means of the (up to 4) Q blocks this workgroup's rows belong to
-    for (int e = tid; e < NSUB * D; e += kThreads) {
+    for (int e = tid; e < NSUB * D; e += kAttnThreads) {
       const int sb = e / D, c = e % D;
       const int qb = (q0 + sb * a.blk_q) / a.blk_q;
-      sQm[e] = (sb * a.blk_q < kBlockQ && qb < a.nqb) ? a.q_mean[((size_t)g * a.nqb + qb) * D + c] : 0.0f;
+      sQm[e] = (sb * a.blk_q < kAttnRows && qb < a.nqb) ? a.q_mean[((size_t)g * a.nqb + qb) * D + c] : 0.0f;
     }
   }
 
@@ -237,106 +381,145 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   for (int ct = 0; ct < NCT; ++ct) o[ct] = f32x16{};
   float m = -INFINITY, l = 0.0f;
 
-  i32x4 kreg[L::K_CHUNKS], vreg[L::V_CHUNKS];
-  load_k_tile<D, VARIANT>(kh, 0, kreg);
-  load_v_tile<D, VARIANT>(vh, 0, N, a.Np, vreg);
+  // Software pipeline over key tiles.  Iteration t (t = 0..T) issues the MFMA work
+  // S(t+1) = K(t+1) Q^T and O += P~(t-1) V(t-1), and the VALU work softmax(t); neither
+  // depends on the other, so the wave keeps both units busy.  O is rescaled for tile t
+  // after P~(t-1) V(t-1) has been added, P~(t) waits in registers for the next
+  // iteration.  LDS: K(t+2) is copied into the slot of K(t) at the start of iteration t;
+  // V(t+1) into the slot of V(t-1) right after the barrier that ends iteration t; the
+  // barrier also waits for the copies started before it.
+  const TileCopy<D, VARIANT, kAttnWaves> copy(a.Np);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (size_t)a.Np * D);
+  const __amdgpu_buffer_rsrc_t vrs = VARIANT == 0 ? make_rsrc(a.v + (size_t)g * N * D, (size_t)N * D * 2)
+                                                  : make_rsrc(a.v_f8 + (size_t)g * D * a.Np, (size_t)D * a.Np);
 
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done with the previous tile in LDS
-    store_k_tile<D, VARIANT>(sK, kreg);
-    store_v_tile<D, VARIANT>(sV, vreg);
-    __syncthreads();
-    if (t + 1 < ntiles) {  // next tile's global loads overlap this tile's math
-      load_k_tile<D, VARIANT>(kh, t + 1, kreg);
-      load_v_tile<D, VARIANT>(vh, t + 1, N, a.Np, vreg);
-    }
+  copy.k_tile(krs, 0, sK0);
+  copy.v_tile(vrs, 0, a.Np, sV0);
+  if (T > 1) copy.k_tile(krs, 1, sK1);
+  wait_copies();
+  __syncthreads();
+  if (SMOOTHQ) smooth_q_bias<D>(a, ksc, sK0, sQm, sBias0, 0);
+  // scale factors c = dQ * dK * sm_scale * log2(e); the raw K scales of a tile are
+  // loaded one iteration before they are needed.  S, c and packed P~ alternate
+  // between two register sets by tile parity.
+  constexpr int NPK = VARIANT == 0 ? 16 : 8;
+  i32x16 sA[2], sB[2];
+  float cA[2], cB[2], kr[2] = {0.0f, 0.0f};
+  uint32_t pkA[NPK], pkB[NPK];
+  const float dqs = dq * a.kscale;
+  if (wave_active) {  // tile 0 is visible to every row
+    qk_tile<D>(sK0, sQw, lane, sA);
+    tile_kscales(a, ksc, 0, h, cA);
+    cA[0] *= dqs;
+    cA[1] *= dqs;
+    if (T > 1) tile_kscales(a, ksc, 1, h, kr);
+  }
+  __syncthreads();
+  if (T > 1) copy.v_tile(vrs, 1, a.Np, sV1);
 
-    if (SMOOTHQ) {
-      // Q-smoothing term of every key of the tile for each Q block of the workgroup:
-      // bias[sb][j] = sm_scale*log2(e) * dK_j * (qmean_sb . Khat_j), in fp32.
-      constexpr int CH = D / 32;  // 32-channel chunks per key, summed across adjacent lanes
-      const int nsub = kBlockQ / a.blk_q;
-      for (int item = tid; item < nsub * kTileKV * CH; item += kThreads) {
-        const int chunk = item % CH, key = (item / CH) % kTileKV, sb = item / (CH * kTileKV);
-        const int8_t* kr = sK + key * L::KROW + chunk * 32;
-        const float* qm = sQm + sb * D + chunk * 32;
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 32; ++c) acc = fmaf(qm[c], (float)kr[c], acc);
-        for (int off = 1; off < CH; off <<= 1) acc += __shfl_xor(acc, off);
-        if (chunk == 0) {
-          const int kj = min(t * kTileKV + key, N - 1);
-          sBias[sb * kTileKV + key] = a.kscale * ksc[kj / a.blk_k] * acc;
-        }
-      }
-      __syncthreads();
-    }
+  const int G16 = lane >> 4, j16 = lane & 15;
+  // transpose-read base of this lane in a V tile (variant 0)
+  const int vbase_off = 128 * (4 * (G16 >> 1) * (D / 16) + (G16 & 1)) + 8 * j16;
 
-    if (!wave_active || t > wave_last_tile) continue;
-
-    i32x16 s[2];
-    qk_tile<D, VARIANT>(sK, qop, lane, s);
-
-    const bool full = (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw);
-    float c[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int kb = min(t * kTileKV + 32 * st + 16 * h, N - 1) / a.blk_k;
-      c[st] = dq * ksc[kb] * a.kscale;
-    }
-
-    float p[2][16];
-    float alpha;
-    const float* bias = SMOOTHQ ? sBias + ((qw - q0) / a.blk_q) * kTileKV + 16 * h : nullptr;
-    const int kl = t * kTileKV + 16 * h;  // key of register 0 of this lane
-    if (full)
-      softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, p, alpha);
-    else
-      softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, p, alpha);
-
-    if (VARIANT == 0) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
-      const _Float16* sVh = reinterpret_cast<const _Float16*>(sV);
-      const int G16 = lane >> 4, j16 = lane & 15;
+  // O += P~(t-1) V(t-1) from the V tile in slot sVp with P~ packed in pkp.
+  auto pv_tile = [&](const uint8_t* sVp, const uint32_t* pkp) {
+    if constexpr (VARIANT == 0) {
+      // A operand V^T: a transpose read of 4 keys x 16 channels (one 128-byte block)
+      // gives lane j of a 16-lane group channel C0 + j for 4 keys.
+      const uint8_t* vbase = sVp + vbase_off;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) pk[q] = pack_f16x2(p[st][8 * u + 2 * q], p[st][8 * u + 2 * q + 1]);
-          const f16x8 pb = __builtin_bit_cast(f16x8, pk);
-          const int row = 32 * st + 16 * (G16 >> 1) + 8 * u + (j16 >> 2);
+          const uint32_t pq[4] = {pkp[st * 8 + u * 4], pkp[st * 8 + u * 4 + 1], pkp[st * 8 + u * 4 + 2],
+                                  pkp[st * 8 + u * 4 + 3]};
+          const f16x8 pb = __builtin_bit_cast(f16x8, pq);
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
-            const int col = ct * 32 + 16 * (G16 & 1) + 4 * (j16 & 3);
-            const i16x4 a0 = lds_read_tr16(sVh + row * L::VROW + col);
-            const i16x4 a1 = lds_read_tr16(sVh + (row + 4) * L::VROW + col);
+            const i16x4 a0 = lds_read_tr16(vbase + 128 * ((8 * st + 2 * u) * (D / 16) + 2 * ct));
+            const i16x4 a1 = lds_read_tr16(vbase + 128 * ((8 * st + 2 * u + 1) * (D / 16) + 2 * ct));
             const i16x4 a01[2] = {a0, a1};
             o[ct] = mfma_f16(__builtin_bit_cast(f16x8, a01), pb, o[ct]);
           }
         }
     } else {
-      uint32_t pk[8];
+      // two-level accumulation: the tile's products go to a fresh accumulator and are
+      // added to the (already rescaled) running O
+      i32x8 pb;
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int st = w / 4, b = 4 * (w % 4);
-        const uint32_t lo = cvt_pk_fp8(p[st][b], p[st][b + 1], 0u, false);
-        pk[w] = cvt_pk_fp8(p[st][b + 2], p[st][b + 3], lo, true);
-      }
-      const i32x8 pb = __builtin_bit_cast(i32x8, pk);
+      for (int w = 0; w < 8; ++w) pb[w] = (int)pkp[w];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const uint8_t* vr = sV + (ct * 32 + ql) * L::VTROW + 16 * h;
-        const i32x4 v0 = *reinterpret_cast<const i32x4*>(vr);
-        const i32x4 v1 = *reinterpret_cast<const i32x4*>(vr + 32);
+        const i32x4 v0 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + (4 * ct) * 512);
+        const i32x4 v1 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + (4 * ct + 2) * 512);
         const i32x4 vv[2] = {v0, v1};
-        const f32x16 inner = mfma_f8(__builtin_bit_cast(i32x8, vv), pb, f32x16{});  // fresh per tile
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[ct][i] = fmaf(alpha, o[ct][i], inner[i]);
+        const f32x16 inner = mfma_f8(__builtin_bit_cast(i32x8, vv), pb, f32x16{});
+        o[ct] += inner;
       }
     }
+  };
+
+  auto iteration = [&](int t, auto parity) {
+    constexpr int cur = decltype(parity)::value;
+    int8_t* const sKc = cur == 0 ? sK0 : sK1;         // K(t), refilled with K(t+2)
+    const int8_t* const sKn = cur == 0 ? sK1 : sK0;   // K(t+1)
+    uint8_t* const sVp = cur == 0 ? sV1 : sV0;        // V(t-1), refilled with V(t+1)
+    const float* const sBc = cur == 0 ? sBias0 : sBias1;
+    float* const sBn = cur == 0 ? sBias1 : sBias0;
+    i32x16* const s = cur == 0 ? sA : sB;             // S(t)
+    i32x16* const sn = cur == 0 ? sB : sA;            // S(t+1)
+    float* const c = cur == 0 ? cA : cB;
+    float* const cn = cur == 0 ? cB : cA;
+    uint32_t* const pk = cur == 0 ? pkA : pkB;        // P~(t)
+    const uint32_t* const pkp = cur == 0 ? pkB : pkA; // P~(t-1)
+
+    const bool compute = wave_active && t < T && t <= wave_last;
+    const bool compute_next = wave_active && t + 1 <= wave_last && t + 1 < T;
+    const bool pv_prev = wave_active && t >= 1 && t - 1 <= wave_last;
+    const bool full = (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw);
+
+    cn[0] = dqs * kr[0];                                                 // tile t+1
+    cn[1] = dqs * kr[1];
+    if (compute_next && t + 2 < T) tile_kscales(a, ksc, t + 2, h, kr);   // used next iteration
+    if (t + 2 < T) copy.k_tile(krs, t + 2, sKc);
+    if (SMOOTHQ && t + 1 < T) smooth_q_bias<D>(a, ksc, sKn, sQm, sBn, t + 1);
+
+    float alpha = 1.0f;
+    bool rescale = false;
+    const float* bias = SMOOTHQ ? sBc + ((qw - q0) / a.blk_q) * kTileKV + 16 * h : nullptr;
+    const int kl = t * kTileKV + 16 * h;  // key of register 0 of this lane
+    if (compute && compute_next && pv_prev && full) {
+      // Interior tile: one basic block, MFMA work (S(t+1), P~(t-1) V(t-1)) interleaved
+      // with the softmax of tile t so the matrix and vector units run together.
+      qk_tile<D>(sKn, sQw, lane, sn);
+      pv_tile(sVp, pkp);
+      softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+      interleave_schedule<D, VARIANT>();
+    } else {
+      if (compute_next) qk_tile<D>(sKn, sQw, lane, sn);
+      if (pv_prev) pv_tile(sVp, pkp);
+      if (compute) {
+        if (full)
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+        else
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+      }
+    }
+    if (rescale) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+    }
+
+    if (t < T) {
+      wait_copies();
+      __syncthreads();
+      if (t + 1 < T) copy.v_tile(vrs, t + 1, a.Np, sVp);
+    }
+  };
+
+  for (int t = 0; t <= T; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{});
+    if (t + 1 <= T) iteration(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (!wave_active) return;
@@ -364,29 +547,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 // qk_tile.  tiles[3i..3i+2] = (head, query tile of 128, key tile of 64).
 // A tile entry outside the tensors yields a tile of zeros.
 template <int D>
-__global__ __launch_bounds__(kThreads) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
+__global__ __launch_bounds__(64 * kDbgWaves) void debug_qk_kernel(const int8_t* __restrict__ q_i8,
                                                             const int8_t* __restrict__ k_i8, int G, int Np,
                                                             const int* __restrict__ tiles,
                                                             int32_t* __restrict__ s_out) {
-  using L = Lds<D, 0>;
-  __shared__ __attribute__((aligned(16))) int8_t sK[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) int8_t sK[Lds<D, 0>::K_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
   const int g = tiles[3 * blockIdx.x], qt = tiles[3 * blockIdx.x + 1], kt = tiles[3 * blockIdx.x + 2];
   if (g < 0 || g >= G || qt < 0 || qt >= Np / kBlockQ || kt < 0 || kt >= Np / kTileKV) {
     int32_t* out = s_out + (size_t)blockIdx.x * kBlockQ * kTileKV;
-    for (int e = tid; e < kBlockQ * kTileKV; e += kThreads) out[e] = 0;
+    for (int e = tid; e < kBlockQ * kTileKV; e += 64 * kDbgWaves) out[e] = 0;
     return;
   }
   const int8_t* qh = q_i8 + (size_t)g * Np * D;
   const int8_t* kh = k_i8 + (size_t)g * Np * D;
-  i32x4 kreg[L::K_CHUNKS];
-  load_k_tile<D, 0>(kh, kt, kreg);
-  store_k_tile<D, 0>(sK, kreg);
+  __shared__ __attribute__((aligned(16))) int8_t sQ[64 * kDbgWaves / 2 * D];
+  const TileCopy<D, 0, kDbgWaves> copy(Np);
+  copy.k_tile(make_rsrc(kh, (size_t)Np * D), kt, sK);
+  int8_t* const sQw = sQ + wave * (D / 32) * 1024;
+  load_q_tile<D>(make_rsrc(qh, (size_t)Np * D), qt * kBlockQ + 32 * wave, sQw);
+  wait_copies();
   __syncthreads();
-  i32x4 qop[D / 32];
-  load_q_operand<D>(qh, qt * kBlockQ + 32 * wave + ql, h, qop);
   i32x16 s[2];
-  qk_tile<D, 0>(sK, qop, lane, s);
+  qk_tile<D>(sK, sQw, lane, s);
   int32_t* out = s_out + (size_t)blockIdx.x * kBlockQ * kTileKV + (size_t)(32 * wave + ql) * kTileKV;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
@@ -400,8 +583,8 @@ __global__ __launch_bounds__(kThreads) void debug_qk_kernel(const int8_t* __rest
 
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
-  const int grid = a.G * (a.Np / kBlockQ);
-  attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ><<<grid, kThreads, 0, st>>>(a);
+  const int grid = a.G * ((a.Np + kAttnRows - 1) / kAttnRows);
+  attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ><<<grid, kAttnThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -421,9 +604,9 @@ hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnA
 hipError_t launch_debug_qk(int d, const int8_t* q_i8, const int8_t* k_i8, int G, int Np, const int* tiles,
                            int n_tiles, int32_t* s_out, hipStream_t st) {
   if (d == 64)
-    debug_qk_kernel<64><<<n_tiles, kThreads, 0, st>>>(q_i8, k_i8, G, Np, tiles, s_out);
+    debug_qk_kernel<64><<<n_tiles, 64 * kDbgWaves, 0, st>>>(q_i8, k_i8, G, Np, tiles, s_out);
   else
-    debug_qk_kernel<128><<<n_tiles, kThreads, 0, st>>>(q_i8, k_i8, G, Np, tiles, s_out);
+    debug_qk_kernel<128><<<n_tiles, 64 * kDbgWaves, 0, st>>>(q_i8, k_i8, G, Np, tiles, s_out);
   return hipGetLastError();
 }
 
