@@ -33,7 +33,6 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kPad = 128;
-constexpr int kStatRows = 512;
 
 int pad_len(int N) { return (N + kPad - 1) / kPad * kPad; }
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -86,7 +85,7 @@ struct Layout {
 size_t up(size_t x) { return (x + 255) / 256 * 256; }
 
 Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
-  const size_t G = (size_t)B * H, Np = pad_len(N), ns = ceil_div(N, kStatRows);
+  const size_t G = (size_t)B * H, Np = pad_len(N), ns = ceil_div(N, sage::kStatRows);
   const size_t nqb = ceil_div(N, p.blk_q), nkb = ceil_div(N, p.blk_k);
   Layout L{};
   size_t off = 0;
@@ -139,7 +138,7 @@ sage::QuantArgs quant_args(const void* q, const void* k, int B, int H, int N, in
   a.blk_k = p.blk_k;
   a.nqb = ceil_div(N, p.blk_q);
   a.nkb = ceil_div(N, p.blk_k);
-  a.nsplit = ceil_div(N, kStatRows);
+  a.nsplit = ceil_div(N, sage::kStatRows);
   a.smooth_k = p.smooth_k;
   a.smooth_q = p.smooth_q;
   return a;
@@ -249,7 +248,7 @@ int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, cons
     return rc;
   if (k_mean && !aligned(k_mean, 4)) return fail(SAGE_ERR_INVALID_ARG, "k_mean must be 4-byte aligned");
   if (p.smooth_q && (rc = check_ptr(q_mean, 4, "q_mean (required with smooth_q)"))) return rc;
-  const size_t need = p.smooth_k ? up((size_t)B * H * ceil_div(N, kStatRows) * d * sizeof(long long)) : 0;
+  const size_t need = p.smooth_k ? up((size_t)B * H * ceil_div(N, sage::kStatRows) * d * sizeof(long long)) : 0;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   rc = run_quant_qk(q, k, B, H, N, d, p, q_i8, k_i8, q_scale, k_scale, k_mean, p.smooth_q ? q_mean : nullptr,
                     (long long*)ws, (hipStream_t)stream);
@@ -262,7 +261,7 @@ int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float
   if ((rc = check_shape(B, H, N, d))) return rc;
   if ((rc = check_ptr(v, 16, "v")) || (rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")))
     return rc;
-  const size_t G = (size_t)B * H, ns = ceil_div(N, kStatRows);
+  const size_t G = (size_t)B * H, ns = ceil_div(N, sage::kStatRows);
   const size_t off_v = up(G * ns * d * sizeof(long long));
   const size_t need = off_v + up(G * ns * d * sizeof(float));
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;

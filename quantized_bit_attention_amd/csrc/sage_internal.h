@@ -33,6 +33,9 @@ struct AttnArgs {
   float kscale;           // sm_scale * log2(e)
 };
 
+// token rows per workgroup of the statistics pass; the workspace holds one partial
+// sum per (head, split of kStatRows tokens, channel)
+constexpr int kStatRows = 256;
 int stat_splits(int N);
 hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long long* ksum_part,
                         float* vmax_part, hipStream_t st);

@@ -19,44 +19,56 @@
 
 namespace sage {
 
-constexpr int kStatRows = 512;  // token rows per workgroup of the statistics pass
-
 // Pass 1: per (head, split of kStatRows tokens) partial sums of K (exact, int64) and,
 // when v != nullptr, partial max |V| per channel.
 //   ksum_part [G][nsplit][D] int64, vmax_part [G][nsplit][D] fp32.
-template <int D>
+// A thread accumulates its at most kStatRows / RPI values per channel in fp64, which is
+// exact: every fp16 value is an integer multiple of 2^-24 below 2^16 in magnitude, so
+// up to 2^13 of them sum exactly within fp64's 53-bit significand.  The thread totals
+// are then converted to int64 units of 2^-24 and summed exactly.  A thread issues all
+// its row loads at once (8 at a time when it also reads V).
+template <int D, bool WITH_V>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, int N,
                                                          int nsplit, long long* __restrict__ ksum_part,
                                                          float* __restrict__ vmax_part) {
   constexpr int TPR = D / 8;            // threads per row
   constexpr int RPI = kThreads / TPR;   // rows per iteration
+  constexpr int NIT = kStatRows / RPI;  // rows per thread
+  constexpr int BATCH = WITH_V ? 8 : NIT;
+  static_assert(NIT % BATCH == 0 && NIT <= 8192, "row batches; exact fp64 thread sums");
   const int split = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, cg = tid % TPR, r0 = tid / TPR;
   const size_t head = (size_t)g * N * D;
   const int t0 = split * kStatRows, t1 = min(N, t0 + kStatRows);
 
-  long long acc[8];
+  double acc[8];
   float vm[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { acc[j] = 0; vm[j] = 0.0f; }
+  for (int j = 0; j < 8; ++j) { acc[j] = 0.0; vm[j] = 0.0f; }
 
-  for (int t = t0 + r0; t < t1; t += RPI) {
-    const uint4 kk = *reinterpret_cast<const uint4*>(k + head + (size_t)t * D + cg * 8);
-    const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll 1
+  for (int base = 0; base < NIT; base += BATCH) {
+    uint4 kk[BATCH], vv[BATCH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += f16_bits_to_fixed24(w[j] & 0xffffu);
-      acc[2 * j + 1] += f16_bits_to_fixed24(w[j] >> 16);
+    for (int b = 0; b < BATCH; ++b) {
+      const int t = t0 + r0 + RPI * (base + b);
+      kk[b] = t < t1 ? *reinterpret_cast<const uint4*>(k + head + (size_t)t * D + cg * 8) : make_uint4(0, 0, 0, 0);
+      vv[b] = (WITH_V && t < t1) ? *reinterpret_cast<const uint4*>(v + head + (size_t)t * D + cg * 8)
+                                 : make_uint4(0, 0, 0, 0);
     }
-    if (v) {
-      const uint4 vv = *reinterpret_cast<const uint4*>(v + head + (size_t)t * D + cg * 8);
-      const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const uint32_t w[4] = {kk[b].x, kk[b].y, kk[b].z, kk[b].w};
+      const uint32_t u[4] = {vv[b].x, vv[b].y, vv[b].z, vv[b].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f16x2 h = __builtin_bit_cast(f16x2, u[j]);
-        vm[2 * j] = fmaxf(vm[2 * j], fabsf((float)h[0]));
-        vm[2 * j + 1] = fmaxf(vm[2 * j + 1], fabsf((float)h[1]));
+        const f16x2 hk = __builtin_bit_cast(f16x2, w[j]);
+        acc[2 * j] += (double)(float)hk[0];
+        acc[2 * j + 1] += (double)(float)hk[1];
+        const f16x2 hv = __builtin_bit_cast(f16x2, u[j]);
+        vm[2 * j] = fmaxf(vm[2 * j], fabsf((float)hv[0]));
+        vm[2 * j + 1] = fmaxf(vm[2 * j + 1], fabsf((float)hv[1]));
       }
     }
   }
@@ -64,7 +76,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   __shared__ long long s_sum[kThreads][8];
   __shared__ float s_max[kThreads][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { s_sum[tid][j] = acc[j]; s_max[tid][j] = vm[j]; }
+  for (int j = 0; j < 8; ++j) {
+    s_sum[tid][j] = (long long)(acc[j] * 16777216.0);  // exact: an integer below 2^53
+    s_max[tid][j] = vm[j];
+  }
   __syncthreads();
   if (tid < D) {
     const int c = tid, cgc = c / 8, jj = c % 8;
@@ -76,7 +91,33 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
     }
     const size_t o = ((size_t)g * nsplit + split) * D + c;
     ksum_part[o] = s;
-    if (v) vmax_part[o] = m;
+    if (WITH_V) vmax_part[o] = m;
+  }
+}
+
+// Pass 1b: fold the per-split partials of each head into split 0 (exact int64 sums of
+// K, max |V|), so the later passes read D values per head instead of nsplit * D.
+// Four threads per channel take every fourth split, then combine through LDS.
+template <int D>
+__global__ __launch_bounds__(4 * D) void stats_finalize_kernel(int nsplit, long long* __restrict__ ksum_part,
+                                                               float* __restrict__ vmax_part) {
+  __shared__ long long s_sum[4][D];
+  __shared__ float s_max[4][D];
+  const int g = blockIdx.x, c = threadIdx.x % D, j = threadIdx.x / D;
+  const size_t base = (size_t)g * nsplit * D + c;
+  long long s = 0;
+  float m = 0.0f;
+#pragma unroll 4
+  for (int sp = j; sp < nsplit; sp += 4) {
+    if (ksum_part) s += ksum_part[base + (size_t)sp * D];
+    if (vmax_part) m = fmaxf(m, vmax_part[base + (size_t)sp * D]);
+  }
+  s_sum[j][c] = s;
+  s_max[j][c] = m;
+  __syncthreads();  // every thread has read its splits before split 0 is overwritten
+  if (j == 0) {
+    if (ksum_part) ksum_part[base] = s_sum[0][c] + s_sum[1][c] + s_sum[2][c] + s_sum[3][c];
+    if (vmax_part) vmax_part[base] = fmaxf(fmaxf(s_max[0][c], s_max[1][c]), fmaxf(s_max[2][c], s_max[3][c]));
   }
 }
 
@@ -127,8 +168,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   if (smooth) {
     if (is_k) {
       if (tid < D) {
-        long long s = 0;
-        for (int sp = 0; sp < a.nsplit; ++sp) s += a.ksum_part[((size_t)g * a.nsplit + sp) * D + tid];
+        const long long s = a.ksum_part[(size_t)g * a.nsplit * D + tid];  // folded into split 0
         const float m = fixed24_mean(s, a.N);
         s_mean[tid] = m;
         if (b == 0 && a.k_mean) a.k_mean[(size_t)g * D + tid] = m;
@@ -226,8 +266,7 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __res
   __shared__ uint8_t s_t[D][TT + 4];
   const int tile = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   if (tid < D) {
-    float m = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, vmax_part[((size_t)g * nsplit + sp) * D + tid]);
+    const float m = vmax_part[(size_t)g * nsplit * D + tid];  // folded into split 0
     s_r[tid] = m > 0.0f ? 448.0f / m : 0.0f;
     if (tile == 0) v_scale[(size_t)g * D + tid] = m / 448.0f;
   }
@@ -269,15 +308,25 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __res
 
 int stat_splits(int N) { return (N + kStatRows - 1) / kStatRows; }
 
+template <int D>
+static void launch_stats_d(const void* k, const void* v, int G, int N, long long* ksum_part, float* vmax_part,
+                           hipStream_t st) {
+  const int ns = stat_splits(N);
+  dim3 grid(ns, G);
+  if (v)
+    stats_kernel<D, true><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, ns, ksum_part,
+                                                     vmax_part);
+  else
+    stats_kernel<D, false><<<grid, kThreads, 0, st>>>((const uint16_t*)k, nullptr, N, ns, ksum_part, nullptr);
+  stats_finalize_kernel<D><<<G, 4 * D, 0, st>>>(ns, ksum_part, v ? vmax_part : nullptr);
+}
+
 hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long long* ksum_part,
                         float* vmax_part, hipStream_t st) {
-  dim3 grid(stat_splits(N), G);
   if (d == 64)
-    stats_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, stat_splits(N),
-                                                ksum_part, vmax_part);
+    launch_stats_d<64>(k, v, G, N, ksum_part, vmax_part, st);
   else
-    stats_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, stat_splits(N),
-                                                 ksum_part, vmax_part);
+    launch_stats_d<128>(k, v, G, N, ksum_part, vmax_part, st);
   return hipGetLastError();
 }
 

@@ -55,11 +55,12 @@ def test_pure_helpers(lib):
 
 
 def test_workspace_size(lib):
-    # variant 0, config-2 shape: int64 partial sums + int8 Q/K + scales + k_mean (each piece 256-aligned)
+    # variant 0, config-2 shape: int64 partial sums (one per 256 tokens) + int8 Q/K + scales + k_mean
+    # (each piece 256-aligned)
     B, H, N, d = 4, 32, 4096, 128
     G, Np = B * H, 4096
     up = lambda x: (x + 255) // 256 * 256
-    expect = (up(G * 8 * d * 8) + up(G * Np * d) * 2 + up(G * 32 * 4) + up(G * 64 * 4) + up(G * d * 4))
+    expect = (up(G * 16 * d * 8) + up(G * Np * d) * 2 + up(G * 32 * 4) + up(G * 64 * 4) + up(G * d * 4))
     assert sage.workspace_bytes(B, H, N, d, 0) == expect
     assert sage.workspace_bytes(B, H, N, d, 1) > expect   # V in FP8 + q means
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
