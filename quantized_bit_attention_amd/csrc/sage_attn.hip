@@ -237,7 +237,7 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
   m = mnew;
   l *= alpha;
   const float shift = VARIANT == 0 ? -m : kLog2_448 - m;
-  float psum = 0.0f;
+  float psum[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -248,8 +248,8 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
         const float e = SMOOTHQ ? x[st][i + j] + shift : fmaf((float)s[st][i + j], c[st], shift);
         pv[j] = __builtin_amdgcn_exp2f(e);
         if (MASK) pv[j] = keep(st, i + j) ? pv[j] : 0.0f;
-        psum += pv[j];
       }
+      psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
       if constexpr (VARIANT == 0) {
         pk[st * 8 + i / 2] = pack_f16x2(pv[0], pv[1]);
         pk[st * 8 + i / 2 + 1] = pack_f16x2(pv[2], pv[3]);
@@ -257,14 +257,15 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
         pk[st * 4 + i / 4] = cvt_pk_fp8(pv[2], pv[3], cvt_pk_fp8(pv[0], pv[1], 0u, false), true);
       }
     }
-  l += psum;
+  l += psum[0] + psum[1];
 }
 
-// K scales of this lane's two 32-key blocks of tile t.
-__device__ __forceinline__ void tile_kscales(const AttnArgs& a, const float* ksc, int t, int h, float* kr) {
+// K scales of this lane's two 32-key blocks of tile t (blk_k = 2^kshift).
+__device__ __forceinline__ void tile_kscales(const AttnArgs& a, const float* ksc, int t, int h, int kshift,
+                                             float* kr) {
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    const int kb = min(t * kTileKV + 32 * st + 16 * h, a.N - 1) / a.blk_k;
+    const int kb = min(t * kTileKV + 32 * st + 16 * h, a.N - 1) >> kshift;
     kr[st] = ksc[kb];
   }
 }
@@ -289,7 +290,7 @@ __device__ __forceinline__ void smooth_q_bias(const AttnArgs& a, const float* ks
     for (int off = 1; off < CH; off <<= 1) acc += __shfl_xor(acc, off);
     if (chunk == 0) {
       const int kj = min(t * kTileKV + key, a.N - 1);
-      sBias[sb * kTileKV + key] = a.kscale * ksc[kj / a.blk_k] * acc;
+      sBias[sb * kTileKV + key] = a.kscale * ksc[kj >> __builtin_ctz(a.blk_k)] * acc;
     }
   }
 }
@@ -365,7 +366,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   int8_t* const sQw = sQ + wave * (D / 32) * 1024;
   // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
   if (wave_active) load_q_tile<D>(make_rsrc(qh, (size_t)a.Np * D), qw, sQw);
-  const float dq = wave_active ? a.q_scale[(size_t)g * a.nqb + qw / a.blk_q] : 0.0f;
+  // block sizes are powers of two
+  const int kshift = __builtin_ctz(a.blk_k), qshift = __builtin_ctz(a.blk_q);
+  const float dq = wave_active ? a.q_scale[(size_t)g * a.nqb + (qw >> qshift)] : 0.0f;
 
   if (SMOOTHQ) {
     // block means of the (up to 4) Q blocks this workgroup's rows belong to
@@ -409,13 +412,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const float dqs = dq * a.kscale;
   if (wave_active) {  // tile 0 is visible to every row
     qk_tile<D>(sK0, sQw, lane, sA);
-    tile_kscales(a, ksc, 0, h, cA);
+    tile_kscales(a, ksc, 0, h, kshift, cA);
     cA[0] *= dqs;
     cA[1] *= dqs;
-    if (T > 1) tile_kscales(a, ksc, 1, h, kr);
+    if (T > 1) tile_kscales(a, ksc, 1, h, kshift, kr);
   }
   __syncthreads();
-  if (T > 1) copy.v_tile(vrs, 1, a.Np, sV1);
+  // V(1) is copied by iteration 0, after its barrier.  Nothing is in flight when the
+  // loop starts, so the compiler sees no pending copy into a slot the loop reads.
 
   const int G16 = lane >> 4, j16 = lane & 15;
   // transpose-read base of this lane in a V tile (variant 0)
@@ -480,13 +484,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
 
     cn[0] = dqs * kr[0];                                                 // tile t+1
     cn[1] = dqs * kr[1];
-    if (compute_next && t + 2 < T) tile_kscales(a, ksc, t + 2, h, kr);   // used next iteration
+    if (compute_next && t + 2 < T) tile_kscales(a, ksc, t + 2, h, kshift, kr);   // used next iteration
     if (t + 2 < T) copy.k_tile(krs, t + 2, sKc);
     if (SMOOTHQ && t + 1 < T) smooth_q_bias<D>(a, ksc, sKn, sQm, sBn, t + 1);
 
     float alpha = 1.0f;
     bool rescale = false;
-    const float* bias = SMOOTHQ ? sBc + ((qw - q0) / a.blk_q) * kTileKV + 16 * h : nullptr;
+    const float* bias = SMOOTHQ ? sBc + ((qw - q0) >> qshift) * kTileKV + 16 * h : nullptr;
     const int kl = t * kTileKV + 16 * h;  // key of register 0 of this lane
     if (compute && compute_next && pv_prev && full) {
       // Interior tile: one basic block, MFMA work (S(t+1), P~(t-1) V(t-1)) interleaved
