@@ -260,13 +260,22 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
   l += psum[0] + psum[1];
 }
 
-// K scales of this lane's two 32-key blocks of tile t (blk_k = 2^kshift).
+// K scales of this lane's two 32-key blocks of tile t (blk_k = 2^kshift).  The block of
+// each 16-key half of a 32-key block is the same for the whole wave, so the candidates
+// are scalar loads (off the vector-memory path of the tile copies) and each lane picks
+// its half.
 __device__ __forceinline__ void tile_kscales(const AttnArgs& a, const float* ksc, int t, int h, int kshift,
                                              float* kr) {
+  // the scales are read-only while the kernel runs: read them through the constant
+  // address space, which allows scalar loads
+  typedef const __attribute__((address_space(4))) float* const_ptr;
+  const const_ptr kc = (const_ptr)ksc;
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    const int kb = min(t * kTileKV + 32 * st + 16 * h, a.N - 1) >> kshift;
-    kr[st] = ksc[kb];
+    const int key = t * kTileKV + 32 * st;
+    const float s0 = kc[min(key, a.N - 1) >> kshift];
+    const float s1 = kc[min(key + 16, a.N - 1) >> kshift];
+    kr[st] = h ? s1 : s0;
   }
 }
 
