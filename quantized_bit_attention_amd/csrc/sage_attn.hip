@@ -160,15 +160,17 @@ __device__ __forceinline__ void qk_tile(const int8_t* sK, const int8_t* sQw, int
   constexpr int CPR = D / 16;
   const int8_t* kbase = sK + 16 * lane;
   const int8_t* qbase = sQw + 16 * lane;
+  // the two 32-key accumulation chains alternate, so consecutive MFMAs are independent
+  i32x16 acc[2] = {i32x16{}, i32x16{}};
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    i32x16 acc = {};
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const i32x4 qop = *reinterpret_cast<const i32x4*>(qbase + ks * 1024);
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      acc = mfma_i8(*reinterpret_cast<const i32x4*>(kbase + (st * CPR + 2 * ks) * 512),
-                    *reinterpret_cast<const i32x4*>(qbase + ks * 1024), acc);
-    s[st] = acc;
+    for (int st = 0; st < 2; ++st)
+      acc[st] = mfma_i8(*reinterpret_cast<const i32x4*>(kbase + (st * CPR + 2 * ks) * 512), qop, acc[st]);
   }
+  s[0] = acc[0];
+  s[1] = acc[1];
 }
 
 // 16 bytes of key `key`, chunk `chunk16`, of the K tile.
@@ -408,6 +410,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   copy.k_tile(krs, 0, sK0);
   copy.v_tile(vrs, 0, a.Np, sV0);
   if (T > 1) copy.k_tile(krs, 1, sK1);
+  // iteration 0 multiplies P~(-1) = 0 by the V slot it reads, which is filled only after
+  // it; clear that slot (0 times a stale NaN pattern would not be 0)
+  for (int e = tid; e < L::V_BYTES / 16; e += kAttnThreads)
+    reinterpret_cast<uint4*>(sV1)[e] = make_uint4(0u, 0u, 0u, 0u);
   wait_copies();
   __syncthreads();
   if (SMOOTHQ) smooth_q_bias<D>(a, ksc, sK0, sQm, sBias0, 0);
@@ -418,6 +424,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   i32x16 sA[2], sB[2];
   float cA[2], cB[2], kr[2] = {0.0f, 0.0f};
   uint32_t pkA[NPK], pkB[NPK];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) pkB[i] = 0u;  // P~(-1)
   const float dqs = dq * a.kscale;
   if (wave_active) {  // tile 0 is visible to every row
     qk_tile<D>(sK0, sQw, lane, sA);
@@ -488,7 +496,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
 
     const bool compute = wave_active && t < T && t <= wave_last;
     const bool compute_next = wave_active && t + 1 <= wave_last && t + 1 < T;
-    const bool pv_prev = wave_active && t >= 1 && t - 1 <= wave_last;
+    // P~(-1) and the V slot read at t = 0 are zeros, so iteration 0 may run the
+    // interleaved block too: its P~V adds nothing
+    const bool pv_prev = wave_active && t - 1 <= wave_last;
     const bool full = (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw);
 
     cn[0] = dqs * kr[0];                                                 // tile t+1
