@@ -32,7 +32,8 @@ namespace sage {
 constexpr int kAttnWaves = 4;                     // waves per attention workgroup
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnRows = 32 * kAttnWaves;        // query rows per attention workgroup
-constexpr int kDbgWaves = 4;                      // the int32 test kernel: 128 x 64 tiles
+constexpr int kDbgWaves = 4;
+                      // the int32 test kernel: 128 x 64 tiles
 
 // LDS tiles are written straight from memory (global_load_lds_dwordx4 /
 // buffer_load_dwordx4 ... lds: lane l of a wave writes 16 bytes at base + 16*l), so a
@@ -312,20 +313,17 @@ __device__ __forceinline__ void smooth_q_bias(const AttnArgs& a, const float* ks
 // loops without conditionals: a guarded sched_group_barrier is not honoured.)
 template <int D, int VARIANT>
 __device__ __forceinline__ void interleave_schedule() {
-  constexpr int QK_MFMA = 2 * (D / 32);                          // two 16-byte reads each (K, Q)
-  constexpr int PV_MFMA = VARIANT == 0 ? 4 * (D / 32) : D / 32;  // two reads each
+  // every MFMA takes two LDS operand reads (K and Q, two V transposes, or two V^T
+  // halves); they are issued LEAD MFMAs ahead of their use, so the LDS latency (about
+  // 200 cycles) overlaps the MFMAs and VALU work in between
+  constexpr int LEAD = 2;
+  constexpr int MFMA = 2 * (D / 32) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
   constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13) : (D == 128 ? 12 : 20);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
 #pragma unroll
-  for (int i = 0; i < QK_MFMA; ++i) {
+  for (int i = 0; i < MFMA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < PV_MFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
   }
 }
