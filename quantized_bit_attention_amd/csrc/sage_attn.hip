@@ -436,6 +436,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // V(1) is copied by iteration 0, after its barrier.  Nothing is in flight when the
   // loop starts, so the compiler sees no pending copy into a slot the loop reads.
 
+  float alpha_prev = 1.0f;  // variant 1: rescale factor of the tile whose P~V is pending
   const int G16 = lane >> 4, j16 = lane & 15;
   // transpose-read base of this lane in a V tile (variant 0)
   const int vbase_off = 128 * (4 * (G16 >> 1) * (D / 16) + (G16 & 1)) + 8 * j16;
@@ -462,8 +463,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
           }
         }
     } else {
-      // two-level accumulation: the tile's products go to a fresh accumulator and are
-      // added to the (already rescaled) running O
+      // two-level accumulation: the tile's products go to a fresh fp32 accumulator, and
+      // O <- alpha(t-1) * O + inner (one fma per element; alpha(t-1) is the rescale
+      // factor the softmax of tile t-1 produced, applied here together with its tile)
       i32x8 pb;
 #pragma unroll
       for (int w = 0; w < 8; ++w) pb[w] = (int)pkp[w];
@@ -473,7 +475,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
         const i32x4 v1 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + (4 * ct + 2) * 512);
         const i32x4 vv[2] = {v0, v1};
         const f32x16 inner = mfma_f8(__builtin_bit_cast(i32x8, vv), pb, f32x16{});
-        o[ct] += inner;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[ct][e] = fmaf(o[ct][e], alpha_prev, inner[e]);
       }
     }
   };
@@ -526,9 +529,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
           softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
       }
     }
-    if (rescale) {
+    if constexpr (VARIANT == 0) {
+      if (rescale) {  // O already holds P~(t-1) V(t-1)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+        for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+      }
+    } else {
+      alpha_prev = alpha;  // applied with tile t's products in the next iteration
     }
 
     if (t < T) {
