@@ -475,8 +475,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
         const i32x4 v1 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + (4 * ct + 2) * 512);
         const i32x4 vv[2] = {v0, v1};
         const f32x16 inner = mfma_f8(__builtin_bit_cast(i32x8, vv), pb, f32x16{});
+        // (through a temporary: the compiler then keeps O in its registers instead of
+        // producing it in the MFMA's and copying it back)
+        f32x16 r;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[ct][e] = fmaf(o[ct][e], alpha_prev, inner[e]);
+        for (int e = 0; e < 16; ++e) r[e] = fmaf(o[ct][e], alpha_prev, inner[e]);
+        o[ct] = r;
       }
     }
   };
