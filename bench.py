@@ -103,16 +103,24 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # the attention kernel alone (same stream, same launch configuration)
+    # the attention kernel alone, as the step launches it (same stream, same launch
+    # configuration): variant 0 quantises Q inside the kernel, variant 1 reads the
+    # pre-quantised Q and FP8 V
     qk = sage.quant_qk(q, k, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=variant == 1)
     vq = sage.quant_v(v) if variant == 1 else None
+    if variant == 0:
+        def kernel():
+            sage.attn_qf16(q, qk, v, out=out, causal=bool(causal), blk_q=cfg["blk_q"], blk_k=cfg["blk_k"])
+    else:
+        def kernel():
+            sage.attn_prequant(qk, v, N, vq=vq, out=out, **opts)
     for _ in range(3):
-        sage.attn_prequant(qk, v, N, vq=vq, out=out, **opts)
+        kernel()
     torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record(stream)
     for _ in range(args.steps):
-        sage.attn_prequant(qk, v, N, vq=vq, out=out, **opts)
+        kernel()
     a1.record(stream)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / args.steps

@@ -105,7 +105,8 @@ int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float
 
 /*
  * o = SageAttention(q, k, v): the whole plug-and-play forward (quantisation kernels
- * plus the attention kernel).  causal: key j is visible to query i iff j <= i.
+ * plus the attention kernel; for variant 0 without Q smoothing the attention kernel
+ * quantises Q itself, see sage_attn_fwd_qf16).  causal: key j is visible to query i iff j <= i.
  * sm_scale: softmax scale (finite, > 0; normally 1/sqrt(d)), applied when the int32
  * scores are dequantised.  variant: SAGE_VARIANT_*.  ws: device workspace of at
  * least sage_workspace_bytes(...) bytes.
@@ -128,6 +129,18 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
                            const uint8_t* v_f8, const float* v_scale, void* o, int B, int H, int N,
                            int d, int causal, float sm_scale, int variant, const sage_params* p,
                            void* stream);
+
+/*
+ * The attention kernel that sage_attn_fwd runs for variant 0 without Q smoothing: Q
+ * is fp16 and each workgroup quantises its own rows per block of blk_q tokens (the
+ * sage_quant_qk rule above, same codes and scales); K comes pre-quantised from
+ * sage_quant_qk (k_i8, k_scale, same p); v is fp16.  Variant 0 only: p->smooth_q = 1
+ * returns SAGE_ERR_UNSUPPORTED.  Used to time the fused kernel by itself, and for
+ * callers that keep K quantised across calls.
+ */
+int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, const void* v,
+                       void* o, int B, int H, int N, int d, int causal, float sm_scale,
+                       const sage_params* p, void* stream);
 
 /*
  * Test surface: the int32 products S = Qhat Khat^T that the attention kernel forms,

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "debug_qk_int32", "workspace_bytes",
+__all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "debug_qk_int32", "workspace_bytes",
            "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV"]
 
 VARIANT_FP16PV = 0
@@ -61,6 +61,7 @@ def _load():
         "sage_attn_fwd": ([P, P, P, P, I, I, I, I, I, F, I, P, S, P], I),
         "sage_attn_fwd_ex": ([P, P, P, P, I, I, I, I, I, F, I, PP, P, S, P], I),
         "sage_attn_fwd_prequant": ([P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
+        "sage_attn_fwd_qf16": ([P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
         "sage_last_error": ([], ctypes.c_char_p),
     }
@@ -205,6 +206,20 @@ def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_F
         _ptr(vq["v_f8"]) if variant == 1 else None, _ptr(vq["v_scale"]) if variant == 1 else None,
         _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale), int(variant), ctypes.byref(p), _stream(dev))
     _check(rc, "sage_attn_fwd_prequant")
+    return out
+
+
+def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, out=None):
+    """Variant 0 attention on fp16 q (quantised inside the kernel) and the K of quant_qk()."""
+    B, H, N, d = _check_qkv(q, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    p = _params(blk_q, blk_k, True, False)
+    rc = _load().sage_attn_fwd_qf16(_ptr(q), _ptr(qk["k_i8"]), _ptr(qk["k_scale"]), _ptr(v), _ptr(out), B, H, N, d,
+                                    int(bool(causal)), float(sm_scale), ctypes.byref(p), _stream(q.device))
+    _check(rc, "sage_attn_fwd_qf16")
     return out
 
 

@@ -77,6 +77,9 @@ int check_ptr(const void* p, size_t align, const char* name) {
   return SAGE_OK;
 }
 
+// Variant 0 without Q smoothing quantises Q inside the attention kernel.
+bool fuse_q(int variant, const Params& p) { return variant == 0 && !p.smooth_q; }
+
 // Workspace layout (each piece 256-byte aligned).
 struct Layout {
   size_t ksum, vmax, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, total;
@@ -92,9 +95,10 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
   L.ksum = take(G * ns * d * sizeof(long long));
   L.vmax = take(variant == 1 ? G * ns * d * sizeof(float) : 0);
-  L.q_i8 = take(G * Np * d);
+  const bool fq = fuse_q(variant, p);
+  L.q_i8 = take(fq ? 0 : G * Np * d);
   L.k_i8 = take(G * Np * d);
-  L.q_scale = take(G * nqb * sizeof(float));
+  L.q_scale = take(fq ? 0 : G * nqb * sizeof(float));
   L.k_scale = take(G * nkb * sizeof(float));
   L.k_mean = take(G * d * sizeof(float));
   L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
@@ -141,6 +145,20 @@ sage::QuantArgs quant_args(const void* q, const void* k, int B, int H, int N, in
   a.nsplit = ceil_div(N, sage::kStatRows);
   a.smooth_k = p.smooth_k;
   a.smooth_q = p.smooth_q;
+  a.with_q = 1;
+  return a;
+}
+
+sage::AttnArgs attn_args(int B, int H, int N, const Params& p, float sm_scale) {
+  sage::AttnArgs a{};
+  a.G = B * H;
+  a.N = N;
+  a.Np = pad_len(N);
+  a.blk_q = p.blk_q;
+  a.blk_k = p.blk_k;
+  a.nqb = ceil_div(N, p.blk_q);
+  a.nkb = ceil_div(N, p.blk_k);
+  a.kscale = sm_scale * 1.4426950408889634f;
   return a;
 }
 
@@ -181,35 +199,30 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
                            variant == 1 ? at<float>(ws, L.vmax) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
-  e = sage::launch_quant(d,
-                         quant_args(q, k, B, H, N, d, p, at<int8_t>(ws, L.q_i8), at<int8_t>(ws, L.k_i8),
-                                    at<float>(ws, L.q_scale), at<float>(ws, L.k_scale), at<float>(ws, L.k_mean),
-                                    p.smooth_q ? at<float>(ws, L.q_mean) : nullptr, at<long long>(ws, L.ksum)),
-                         st);
+  const bool fq = fuse_q(variant, p);
+  sage::QuantArgs qa = quant_args(q, k, B, H, N, d, p, fq ? nullptr : at<int8_t>(ws, L.q_i8), at<int8_t>(ws, L.k_i8),
+                                  fq ? nullptr : at<float>(ws, L.q_scale), at<float>(ws, L.k_scale),
+                                  at<float>(ws, L.k_mean), p.smooth_q ? at<float>(ws, L.q_mean) : nullptr,
+                                  at<long long>(ws, L.ksum));
+  qa.with_q = fq ? 0 : 1;
+  e = sage::launch_quant(d, qa, st);
   if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
   if (variant == 1) {
     e = sage::launch_quant_v(d, v, G, N, Np, at<float>(ws, L.vmax), at<uint8_t>(ws, L.v_f8),
                              at<float>(ws, L.v_scale), st);
     if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
   }
-  sage::AttnArgs a{};
-  a.q_i8 = at<int8_t>(ws, L.q_i8);
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
+  a.q = fq ? (const uint16_t*)q : nullptr;
+  a.q_i8 = fq ? nullptr : at<int8_t>(ws, L.q_i8);
   a.k_i8 = at<int8_t>(ws, L.k_i8);
-  a.q_scale = at<float>(ws, L.q_scale);
+  a.q_scale = fq ? nullptr : at<float>(ws, L.q_scale);
   a.k_scale = at<float>(ws, L.k_scale);
   a.q_mean = p.smooth_q ? at<float>(ws, L.q_mean) : nullptr;
   a.v = (const uint16_t*)v;
   a.v_f8 = variant == 1 ? at<uint8_t>(ws, L.v_f8) : nullptr;
   a.v_scale = variant == 1 ? at<float>(ws, L.v_scale) : nullptr;
   a.o = (uint16_t*)o;
-  a.G = G;
-  a.N = N;
-  a.Np = Np;
-  a.blk_q = p.blk_q;
-  a.blk_k = p.blk_k;
-  a.nqb = ceil_div(N, p.blk_q);
-  a.nkb = ceil_div(N, p.blk_k);
-  a.kscale = sm_scale * 1.4426950408889634f;
   e = sage::launch_attn(d, variant, causal, p.smooth_q, a, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
@@ -305,7 +318,7 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
   if (variant == 0 && (rc = check_ptr(v, 16, "v"))) return rc;
   if (variant == 1 && ((rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")))) return rc;
   if (p.smooth_q && (rc = check_ptr(q_mean, 4, "q_mean (required with smooth_q)"))) return rc;
-  sage::AttnArgs a{};
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
   a.q_i8 = q_i8;
   a.k_i8 = k_i8;
   a.q_scale = q_scale;
@@ -315,15 +328,31 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
   a.v_f8 = v_f8;
   a.v_scale = v_scale;
   a.o = (uint16_t*)o;
-  a.G = B * H;
-  a.N = N;
-  a.Np = pad_len(N);
-  a.blk_q = p.blk_q;
-  a.blk_k = p.blk_k;
-  a.nqb = ceil_div(N, p.blk_q);
-  a.nkb = ceil_div(N, p.blk_k);
-  a.kscale = sm_scale * 1.4426950408889634f;
   hipError_t e = sage::launch_attn(d, variant, causal, p.smooth_q, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, const void* v, void* o, int B,
+                       int H, int N, int d, int causal, float sm_scale, const sage_params* pp, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, 0, &p))) return rc;
+  if (p.smooth_q) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_qf16 quantises Q without smoothing (smooth_q must be 0)");
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k_i8, 16, "k_i8")) || (rc = check_ptr(k_scale, 4, "k_scale")) ||
+      (rc = check_ptr(v, 16, "v")) || (rc = check_ptr(o, 16, "o")))
+    return rc;
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
+  a.q = (const uint16_t*)q;
+  a.k_i8 = k_i8;
+  a.k_scale = k_scale;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  hipError_t e = sage::launch_attn(d, 0, causal, 0, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
 }

@@ -328,8 +328,12 @@ __device__ __forceinline__ void interleave_schedule() {
   }
 }
 
-template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ>
+// FUSEQ (variant 0 without Q smoothing): Q arrives as fp16 and each workgroup quantises
+// its own rows into the LDS operand tile, with the per-block scale of the quantisation
+// pass (the workgroup's 128 rows are whole Q blocks of 32, 64 or 128 rows).
+template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
+  static_assert(!FUSEQ || (VARIANT == 0 && !SMOOTHQ), "in-kernel Q quantisation: variant 0, no Q smoothing");
   using L = Lds<D, VARIANT>;
   constexpr int NCT = D / 32;                       // 32-channel output tiles
   constexpr int NSUB = SMOOTHQ ? kAttnRows / 32 : 1;  // Q blocks a workgroup can span (blk_q >= 32)
@@ -344,6 +348,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sQm[SMOOTHQ ? NSUB * D : 1];
   __shared__ float sBias0[SMOOTHQ ? NSUB * kTileKV : 1];
   __shared__ float sBias1[SMOOTHQ ? NSUB * kTileKV : 1];
+  __shared__ float sAmax[kAttnWaves];  // FUSEQ: |Q| max of each wave's rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, ql = lane & 31;
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const int qi = qw + ql;         // this lane's query row
   const bool wave_active = qw < N;
 
-  const int8_t* __restrict__ qh = a.q_i8 + (size_t)g * a.Np * D;
+  const int8_t* __restrict__ qh = FUSEQ ? nullptr : a.q_i8 + (size_t)g * a.Np * D;
   const int8_t* __restrict__ kh = a.k_i8 + (size_t)g * a.Np * D;
   const float* __restrict__ ksc = a.k_scale + (size_t)g * a.nkb;
 
@@ -373,11 +378,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const int wave_last = CAUSAL ? min(ntiles_all - 1, min(qw + 31, N - 1) / kTileKV) : ntiles_all - 1;
 
   int8_t* const sQw = sQ + wave * (D / 32) * 1024;
-  // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
-  if (wave_active) load_q_tile<D>(make_rsrc(qh, (size_t)a.Np * D), qw, sQw);
+  // FUSEQ: lane l holds fp16 Q of row qw + l%32, channels 32*ks + 16*h .. +15 in
+  // qraw[2ks], qraw[2ks+1] (the bytes its operand read takes); rows >= N are zeros
+  uint4 qraw[FUSEQ ? D / 16 : 1];
+  if constexpr (FUSEQ) {
+    const bool row_ok = wave_active && qi < N;
+    const uint16_t* qsrc = a.q + ((size_t)g * N + (row_ok ? qi : 0)) * D + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        qraw[2 * ks + j] = row_ok ? *reinterpret_cast<const uint4*>(qsrc + 32 * ks + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
+    if (wave_active) load_q_tile<D>(make_rsrc(qh, (size_t)a.Np * D), qw, sQw);
+  }
   // block sizes are powers of two
   const int kshift = __builtin_ctz(a.blk_k), qshift = __builtin_ctz(a.blk_q);
-  const float dq = wave_active ? a.q_scale[(size_t)g * a.nqb + (qw >> qshift)] : 0.0f;
+  // Q scale of this wave's block (FUSEQ: set once the block's |Q| max is known)
+  float dq = (!FUSEQ && wave_active) ? a.q_scale[(size_t)g * a.nqb + (qw >> qshift)] : 0.0f;
 
   if (SMOOTHQ) {
     // block means of the (up to 4) Q blocks this workgroup's rows belong to
@@ -412,8 +431,44 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // it; clear that slot (0 times a stale NaN pattern would not be 0)
   for (int e = tid; e < L::V_BYTES / 16; e += kAttnThreads)
     reinterpret_cast<uint4*>(sV1)[e] = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (FUSEQ) {
+    // |Q| max: with the sign bits cleared, fp16 bit patterns order like the values, so a
+    // packed 16-bit integer max finds it exactly
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
+    }
+    const u16x2 mb = {__builtin_elementwise_max(mx[0], mx[1]), 0};
+    const float am = wave_max((float)__builtin_bit_cast(f16x2, mb)[0]);
+    if (lane == 0) sAmax[wave] = am;
+  }
   wait_copies();
   __syncthreads();
+  if constexpr (FUSEQ) {
+    // the Q block of this wave spans waves w0 .. w0 + blk_q/32 - 1
+    const int wpb = a.blk_q >> 5, w0 = wave & ~(wpb - 1);
+    float amax = sAmax[w0];
+    for (int w = 1; w < wpb; ++w) amax = fmaxf(amax, sAmax[w0 + w]);
+    dq = i8_scale(amax);
+    const float r = i8_factor(amax);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      uint32_t pk4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 src = qraw[2 * ks + u / 2];
+        const uint32_t w0v = (u & 1) ? src.z : src.x, w1v = (u & 1) ? src.w : src.y;
+        const f16x2 h0 = __builtin_bit_cast(f16x2, w0v), h1 = __builtin_bit_cast(f16x2, w1v);
+        pk4[u] = pack_bytes4(i8_code_int((float)h0[0], r), i8_code_int((float)h0[1], r),
+                             i8_code_int((float)h1[0], r), i8_code_int((float)h1[1], r));
+      }
+      *reinterpret_cast<uint4*>(sQw + ks * 1024 + 16 * lane) = make_uint4(pk4[0], pk4[1], pk4[2], pk4[3]);
+    }
+  }
   if (SMOOTHQ) smooth_q_bias<D>(a, ksc, sK0, sQm, sBias0, 0);
   // scale factors c = dQ * dK * sm_scale * log2(e); the raw K scales of a tile are
   // loaded one iteration before they are needed.  S, c and packed P~ alternate
@@ -613,10 +668,10 @@ __global__ __launch_bounds__(64 * kDbgWaves) void debug_qk_kernel(const int8_t* 
 // ---------------------------------------------------------------------------
 // launchers
 
-template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ>
+template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ = false>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
   const int grid = a.G * ((a.Np + kAttnRows - 1) / kAttnRows);
-  attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ><<<grid, kAttnThreads, 0, st>>>(a);
+  attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ, FUSEQ><<<grid, kAttnThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -628,6 +683,11 @@ static hipError_t launch_dv(int causal, int smooth_q, const AttnArgs& a, hipStre
 }
 
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st) {
+  if (a.q) {  // fp16 Q, quantised in the kernel (variant 0, no Q smoothing)
+    if (variant != 0 || smooth_q) return hipErrorInvalidValue;
+    if (d == 64) return causal ? launch_one<64, 0, true, false, true>(a, st) : launch_one<64, 0, false, false, true>(a, st);
+    return causal ? launch_one<128, 0, true, false, true>(a, st) : launch_one<128, 0, false, false, true>(a, st);
+  }
   if (d == 64)
     return variant == 0 ? launch_dv<64, 0>(causal, smooth_q, a, st) : launch_dv<64, 1>(causal, smooth_q, a, st);
   return variant == 0 ? launch_dv<128, 0>(causal, smooth_q, a, st) : launch_dv<128, 1>(causal, smooth_q, a, st);

@@ -75,6 +75,40 @@ __device__ __forceinline__ uint32_t cvt_pk_fp8(float a, float b, uint32_t old, b
             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
+// Per-block INT8 quantisation of Q and K: scale = absmax / 127, code = x * (127 / absmax)
+// rounded to nearest even and saturated at +-127 (an all-zero block gets factor 0).
+// Every kernel that quantises goes through these, so their codes and scales agree bit
+// for bit.
+// (x * r is formed as fma(x, r, +0): the same fp32 value, except that -0 becomes +0,
+// which gives the same code.)
+__device__ __forceinline__ float i8_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ float i8_factor(float amax) { return amax > 0.0f ? 127.0f / amax : 0.0f; }
+__device__ __forceinline__ int i8_code_int(float x, float r) {
+  float t = rintf(__builtin_fmaf(x, r, 0.0f));
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return (int)t;
+}
+__device__ __forceinline__ uint32_t i8_code(float x, float r) { return (uint32_t)i8_code_int(x, r) & 0xffu; }
+// Low bytes of four ints packed as bytes 0..3.
+__device__ __forceinline__ uint32_t pack_bytes4(int c0, int c1, int c2, int c3) {
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c1, (uint32_t)c0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c3, (uint32_t)c2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Maximum of x over the 64 lanes of the wave (rows of 16 lanes by DPP, then the row
+// pairs and the two halves by permlane swaps).
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));  // quad [1,0,3,2]
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));  // quad [2,3,0,1]
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false))); // row_ror 4
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false))); // row_ror 8
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   f32x2 v = {a, b};
   f16x2 h = __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even

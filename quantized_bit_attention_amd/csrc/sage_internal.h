@@ -17,10 +17,12 @@ struct QuantArgs {
   float* q_mean;      // [G][nqb][D] or null
   const long long* ksum_part;  // [G][nsplit][D] from the statistics pass
   int G, N, Np, blk_q, blk_k, nqb, nkb, nsplit, smooth_k, smooth_q;
+  int with_q;         // 0: quantise only K
 };
 
 struct AttnArgs {
-  const int8_t* q_i8;     // [G][Np][D]
+  const uint16_t* q;      // [G][N][D] fp16 (Q quantised in the kernel) or null
+  const int8_t* q_i8;     // [G][Np][D] (pre-quantised Q)
   const int8_t* k_i8;     // [G][Np][D]
   const float* q_scale;   // [G][nqb]
   const float* k_scale;   // [G][nkb]

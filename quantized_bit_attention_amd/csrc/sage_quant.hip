@@ -133,7 +133,8 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 
 // Pass 2: smooth + quantise one block of rows (a K block or a Q block) per workgroup.
 //   blockIdx.x < G * nkb: K block (mean from the pass-1 partial sums when smooth_k);
-//   otherwise a Q block (its own exact block mean when smooth_q).
+//   otherwise a Q block (its own exact block mean when smooth_q).  With with_q = 0 the
+//   grid holds only the K blocks (the attention kernel then quantises Q itself).
 // MAXR: rows per block rounded up to a multiple of kThreads / (D/8).
 template <int D, int MAXR>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
@@ -224,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     }
   }
   amax = block_max(amax, s_red);
-  const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (tid == 0) (is_k ? a.k_scale : a.q_scale)[(size_t)g * nb + b] = amax / 127.0f;
+  const float r = i8_factor(amax);
+  if (tid == 0) (is_k ? a.k_scale : a.q_scale)[(size_t)g * nb + b] = i8_scale(amax);
 
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -233,11 +234,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     if (row < rows) {
       uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float t = rintf(x[it][j] * r);
-        t = fminf(fmaxf(t, -127.0f), 127.0f);
-        packed[j / 4] |= ((uint32_t)(int)t & 0xffu) << (8 * (j % 4));
-      }
+      for (int j = 0; j < 8; ++j) packed[j / 4] |= i8_code(x[it][j], r) << (8 * (j % 4));
       *reinterpret_cast<uint2*>(dst + (size_t)(t0 + row) * D + cg * 8) = make_uint2(packed[0], packed[1]);
     }
   }
@@ -332,8 +329,8 @@ hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long 
 
 template <int D>
 static hipError_t launch_quant_d(const QuantArgs& a, hipStream_t st) {
-  const int maxblk = a.blk_q > a.blk_k ? a.blk_q : a.blk_k;
-  const int grid = a.G * (a.nkb + a.nqb);
+  const int maxblk = (a.with_q && a.blk_q > a.blk_k) ? a.blk_q : a.blk_k;
+  const int grid = a.G * (a.nkb + (a.with_q ? a.nqb : 0));
   constexpr int RPI = kThreads / (D / 8);
   if (maxblk <= 32 && 32 % RPI == 0)
     quant_kernel<D, (32 > RPI ? 32 : RPI)><<<grid, kThreads, 0, st>>>(a);

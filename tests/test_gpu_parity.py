@@ -275,6 +275,38 @@ def test_prequant_matches_whole_call_and_is_deterministic(sage):
     assert torch.equal(a, p)
 
 
+FUSED = [
+    # recipe cfg, shape overrides, blk_q, blk_k, causal
+    (2, dict(N=333, B=1, H=3), 128, 64, 1),
+    (2, dict(N=1000, B=2, H=1), 64, 16, 0),
+    (3, dict(N=200, B=1, H=2), 32, 64, 1),
+    (3, dict(N=4096, B=1, H=2), 128, 128, 0),
+    (1, dict(N=65, B=1, H=1), 32, 32, 0),
+]
+
+
+@pytest.mark.parametrize("cfg,shape,blk_q,blk_k,causal", FUSED)
+def test_fused_q_quantisation_matches_quant_pass(sage, cfg, shape, blk_q, blk_k, causal):
+    """Variant 0 quantises Q inside the attention kernel: the whole call, the fused kernel
+    alone and the quantisation pass + pre-quantised kernel give the same bits.  One Q block
+    is all zeros (scale 0, codes 0)."""
+    c = workloads.make_inputs(cfg, **shape)
+    q = c["q"].copy()
+    q[0, 0, :blk_q] = 0
+    say(f"fused Q {q.shape} blk_q={blk_q} blk_k={blk_k} causal={causal}")
+    qd, kd, vd = dev(q), dev(c["k"]), dev(c["v"])
+    N = q.shape[2]
+    kw = dict(causal=bool(causal), blk_q=blk_q, blk_k=blk_k)
+    whole = sage.attn(qd, kd, vd, variant=0, **kw)
+    qk = sage.quant_qk(qd, kd, blk_q=blk_q, blk_k=blk_k)
+    fused = sage.attn_qf16(qd, qk, vd, **kw)
+    pre = sage.attn_prequant(qk, vd, N, variant=0, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(whole.float()).all()
+    assert torch.equal(whole, fused)
+    assert torch.equal(whole, pre)
+
+
 def test_api_rejects_bad_arguments_on_gpu(sage):
     q = torch.zeros((1, 1, 64, 96), dtype=torch.float16, device="cuda")
     with pytest.raises(sage.SageError, match="head dim"):

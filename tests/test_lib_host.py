@@ -55,13 +55,16 @@ def test_pure_helpers(lib):
 
 
 def test_workspace_size(lib):
-    # variant 0, config-2 shape: int64 partial sums (one per 256 tokens) + int8 Q/K + scales + k_mean
-    # (each piece 256-aligned)
+    # variant 0, config-2 shape: int64 partial sums (one per 256 tokens) + int8 K + K scales + k_mean
+    # (each piece 256-aligned); the attention kernel quantises Q itself, so there is no int8 Q
     B, H, N, d = 4, 32, 4096, 128
     G, Np = B * H, 4096
     up = lambda x: (x + 255) // 256 * 256
-    expect = (up(G * 16 * d * 8) + up(G * Np * d) * 2 + up(G * 32 * 4) + up(G * 64 * 4) + up(G * d * 4))
+    expect = up(G * 16 * d * 8) + up(G * Np * d) + up(G * 64 * 4) + up(G * d * 4)
     assert sage.workspace_bytes(B, H, N, d, 0) == expect
+    # with Q smoothing the quantisation pass writes int8 Q, its scales and block means
+    assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) == (expect + up(G * Np * d) + up(G * 32 * 4)
+                                                                  + up(G * 32 * d * 4))
     assert sage.workspace_bytes(B, H, N, d, 1) > expect   # V in FP8 + q means
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
     assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
@@ -126,6 +129,13 @@ def test_other_entry_points_reject(lib):
     assert rc == -1 and b"v is NULL" in lib.sage_last_error()
     rc = lib.sage_debug_qk_int32(A, A, 1, 1, 64, 64, A, 0, A, None)
     assert rc == -1 and b"n_tiles" in lib.sage_last_error()
+    # the fused-Q kernel quantises Q without smoothing only
+    rc = lib.sage_attn_fwd_qf16(A, A, A, A, A, 1, 1, 64, 64, 0, 0.125, ctypes.byref(sage._params(smooth_q=True)), None)
+    assert rc == -2 and b"smooth_q" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16(A, None, A, A, A, 1, 1, 64, 64, 0, 0.125, None, None)
+    assert rc == -1 and b"k_i8 is NULL" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16(A, A, A, A, A, 1, 1, 64, 96, 0, 0.125, None, None)
+    assert rc == -2
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
