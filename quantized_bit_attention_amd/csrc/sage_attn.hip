@@ -58,6 +58,10 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Index of this wave in the workgroup as a scalar, so LDS destinations of the tile
+// copies (M0) are formed with scalar instructions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // K tile: slot (st*CPR + c)*32 + x holds bytes 16c..16c+15 of key 32*st + k_perm(x),
 // x = A-operand row.  Lane l of the operand read for 32-key block st, k-step ks, is
 // at 16*l + (st*CPR + 2*ks)*512.
@@ -112,20 +116,21 @@ struct TileCopy {
     static_assert(VARIANT == 0 || (NWAVES * 2) % 4 == 0, "V^T copies must step by whole channel rows");
   }
 
-  // K tile t of the padded int8 tensor (resource over this head).
+  // K tile t of the padded int8 tensor (resource over this head); the tile and copy
+  // steps go in the scalar offset.
   __device__ __forceinline__ void k_tile(__amdgpu_buffer_rsrc_t krs, int t, int8_t* sK) const {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
 #pragma unroll
     for (int i = 0; i < K_PER_WAVE; ++i) {
       const int c = i * NWAVES + wave;
       if (K_COPIES % NWAVES == 0 || c < K_COPIES)
-        copy16_to_lds(krs, koff + i * K_STEP, (uint32_t)(t * kTileKV * D), sK + c * 1024);
+        copy16_to_lds(krs, koff, (uint32_t)(t * kTileKV * D) + i * K_STEP, sK + c * 1024);
     }
   }
   // V tile t.  Variant 0 puts the whole offset in the lane offset so keys >= N fall
   // outside the resource and land as zeros.
   __device__ __forceinline__ void v_tile(__amdgpu_buffer_rsrc_t vrs, int t, int Np, uint8_t* sV) const {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
 #pragma unroll
     for (int i = 0; i < V_PER_WAVE; ++i) {
       const int c = i * NWAVES + wave;
@@ -574,8 +579,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     if (compute && compute_next && pv_prev && full) {
       // Interior tile: one basic block, MFMA work (S(t+1), P~(t-1) V(t-1)) interleaved
       // with the softmax of tile t so the matrix and vector units run together.
-      qk_tile<D>(sKn, sQw, lane, sn);
-      pv_tile(sVp, pkp);
+      if constexpr (VARIANT == 1) {
+        // the O update of the two-level accumulation follows each P~V MFMA: issuing
+        // those MFMAs first lets the updates overlap the score MFMAs
+        pv_tile(sVp, pkp);
+        qk_tile<D>(sKn, sQw, lane, sn);
+      } else {
+        qk_tile<D>(sKn, sQw, lane, sn);
+        pv_tile(sVp, pkp);
+      }
       softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
       interleave_schedule<D, VARIANT>();
     } else {
