@@ -268,24 +268,20 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
   l += psum[0] + psum[1];
 }
 
-// K scales of this lane's two 32-key blocks of tile t (blk_k = 2^kshift).  The block of
-// each 16-key half of a 32-key block is the same for the whole wave, so the candidates
-// are scalar loads (off the vector-memory path of the tile copies) and each lane picks
-// its half.
-__device__ __forceinline__ void tile_kscales(const AttnArgs& a, const float* ksc, int t, int h, int kshift,
-                                             float* kr) {
+// K scales of the four 16-key quarters of tile t (blk_k = 2^kshift, keys clamped to
+// the last one, so any t reads inside the array).  A quarter's block is the same for the
+// whole wave, so these are scalar loads (off the vector-memory path of the tile copies);
+// lane half h of 32-key block st then takes quarter 2*st + h (kscale_of).
+__device__ __forceinline__ void tile_kscales(const float* ksc, int t, unsigned last_key, int kshift,
+                                             float* kq) {
   // the scales are read-only while the kernel runs: read them through the constant
   // address space, which allows scalar loads
   typedef const __attribute__((address_space(4))) float* const_ptr;
   const const_ptr kc = (const_ptr)ksc;
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int key = t * kTileKV + 32 * st;
-    const float s0 = kc[min(key, a.N - 1) >> kshift];
-    const float s1 = kc[min(key + 16, a.N - 1) >> kshift];
-    kr[st] = h ? s1 : s0;
-  }
+  for (int j = 0; j < 4; ++j) kq[j] = kc[min((unsigned)(t * kTileKV + 16 * j), last_key) >> kshift];
 }
+__device__ __forceinline__ float kscale_of(const float* kq, int st, int h) { return h ? kq[2 * st + 1] : kq[2 * st]; }
 
 // Q-smoothing term of every key of tile t for each Q block of the workgroup:
 // bias[sb][j] = sm_scale*log2(e) * dK_j * (qmean_sb . Khat_j), in fp32.
@@ -480,18 +476,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // between two register sets by tile parity.
   constexpr int NPK = VARIANT == 0 ? 16 : 8;
   i32x16 sA[2], sB[2];
-  float cA[2], cB[2], kr[2] = {0.0f, 0.0f};
+  float cA[2], cB[2], kq[4];  // kq: raw K scales of tile t+1 (see tile_kscales)
+  const unsigned last_key = (unsigned)(N - 1);
   uint32_t pkA[NPK], pkB[NPK];
 #pragma unroll
   for (int i = 0; i < NPK; ++i) pkB[i] = 0u;  // P~(-1)
   const float dqs = dq * a.kscale;
   if (wave_active) {  // tile 0 is visible to every row
     qk_tile<D>(sK0, sQw, lane, sA);
-    tile_kscales(a, ksc, 0, h, kshift, cA);
-    cA[0] *= dqs;
-    cA[1] *= dqs;
-    if (T > 1) tile_kscales(a, ksc, 1, h, kshift, kr);
   }
+  tile_kscales(ksc, 0, last_key, kshift, kq);
+  cA[0] = dqs * kscale_of(kq, 0, h);
+  cA[1] = dqs * kscale_of(kq, 1, h);
+  tile_kscales(ksc, 1, last_key, kshift, kq);
   __syncthreads();
   // V(1) is copied by iteration 0, after its barrier.  Nothing is in flight when the
   // loop starts, so the compiler sees no pending copy into a slot the loop reads.
@@ -566,9 +563,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     const bool pv_prev = wave_active && t - 1 <= wave_last;
     const bool full = (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw);
 
-    cn[0] = dqs * kr[0];                                                 // tile t+1
-    cn[1] = dqs * kr[1];
-    if (compute_next && t + 2 < T) tile_kscales(a, ksc, t + 2, h, kshift, kr);   // used next iteration
+    cn[0] = dqs * kscale_of(kq, 0, h);                                   // tile t+1
+    cn[1] = dqs * kscale_of(kq, 1, h);
     if (t + 2 < T) copy.k_tile(krs, t + 2, sKc);
     if (SMOOTHQ && t + 1 < T) smooth_q_bias<D>(a, ksc, sKn, sQm, sBn, t + 1);
 
@@ -609,6 +605,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       alpha_prev = alpha;  // applied with tile t's products in the next iteration
     }
 
+    // K scales of tile t+2 for the next iteration: issued here, their latency overlaps
+    // the barrier
+    tile_kscales(ksc, t + 2, last_key, kshift, kq);
     if (t < T) {
       wait_copies();
       __syncthreads();
