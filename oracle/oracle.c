@@ -12,6 +12,7 @@
  *  [SA2]     "SageAttention2: Efficient Attention with Thorough Outlier Smoothing
  *            and Per-thread INT4 Quantization" (ICML 2025 abstract), and the
  *            arXiv 2411.10958 abstract of SageAttention2.
+ *  [SA2-v]   the arXiv 2502.01776 abstract of SageAttention2 ("smooth Q and V").
  *  [FA]      FlashAttention / FlashAttention-2 and "Online normalizer calculation
  *            for softmax", entries of the reference list on the [SA-sum] page.
  *
@@ -25,8 +26,10 @@
  *   7. online softmax over key tiles of `bkv` keys in ascending order ([FA])
  *   8. P~ V: P~ rounded to fp16 (variant 0) or P~*448 to FP8 E4M3 with V in
  *      per-channel-scaled FP8 and a fresh accumulator per tile (variant 1, [SA2]
- *      "two-level accumulation")
- *   9. O / l (variant 1 also * dV / 448)
+ *      "two-level accumulation"); with V smoothing ([SA2-v]) the FP8 V is of
+ *      V' = V - v_mean (token mean per channel)
+ *   9. O / l (variant 1 also * dV / 448, plus v_mean with V smoothing: the rows
+ *      of P~ / l sum to one, so the mean comes back out unchanged)
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - means are exact: fp16 inputs are integer multiples of 2^-24, so the token
@@ -40,6 +43,8 @@
  *  - P~ in FP8 uses the static scale 448 (P~ <= 1 after max subtraction).
  *  - V in FP8: per channel, scale = absmax_t |V[t, c]| / 448, codes =
  *    E4M3FN(V * (448 / absmax)) rounded to nearest even after clamping to +-448.
+ *  - V smoothing (variant 1, optional): v_mean is the exact token mean like
+ *    k_mean, V' = V - v_mean in fp32, and V' takes V's place in the rule above.
  *
  * Floating-point decisions that produce integer codes (int8 Q/K codes, fp8 V
  * codes) are taken in fp32, the precision the GPU kernels use.  Everything else
@@ -181,11 +186,19 @@ static void quant_head(const uint16_t* x, int N, int Np, int d, int blk, int mea
 }
 
 /* V in FP8 for one head: per-channel scale absmax / 448, codes transposed to
- * vt[d][Np] (columns >= N zero). */
-static void quant_v_head(const uint16_t* v, int N, int Np, int d, uint8_t* vt, float* vscale) {
+ * vt[d][Np] (columns >= N zero).  With smooth_v, each channel first loses its
+ * exact token mean (written to vmean[d]); otherwise vmean (when non-NULL) is 0. */
+static void quant_v_head(const uint16_t* v, int N, int Np, int d, int smooth_v, uint8_t* vt, float* vscale,
+                         float* vmean) {
   for (int c = 0; c < d; ++c) {
+    const float mean = smooth_v ? exact_mean(v, d, 0, N, c) : 0.0f;
+    if (vmean) vmean[c] = mean;
     float a = 0.0f;
-    for (int t = 0; t < N; ++t) a = fmaxf(a, fabsf((float)oracle_f16_decode(v[(size_t)t * d + c])));
+    for (int t = 0; t < N; ++t) {
+      float x = (float)oracle_f16_decode(v[(size_t)t * d + c]);
+      if (smooth_v) x = x - mean;
+      a = fmaxf(a, fabsf(x));
+    }
     uint8_t* row = vt + (size_t)c * Np;
     memset(row, 0, (size_t)Np);
     if (a == 0.0f) {
@@ -194,7 +207,9 @@ static void quant_v_head(const uint16_t* v, int N, int Np, int d, uint8_t* vt, f
     }
     float r = 448.0f / a;
     for (int t = 0; t < N; ++t) {
-      float y = (float)oracle_f16_decode(v[(size_t)t * d + c]) * r;
+      float x = (float)oracle_f16_decode(v[(size_t)t * d + c]);
+      if (smooth_v) x = x - mean;
+      float y = x * r;
       if (y > 448.0f) y = 448.0f;
       if (y < -448.0f) y = -448.0f;
       row[t] = oracle_e4m3_encode((double)y);
@@ -210,7 +225,7 @@ static void quant_v_head(const uint16_t* v, int N, int Np, int d, uint8_t* vt, f
 typedef struct {
   int B, H, N, d, causal, variant;
   int blk_q, blk_k, bkv;
-  int smooth_k, smooth_q;
+  int smooth_k, smooth_q, smooth_v;
   int exact;      /* 1: no quantisation at all, fp64 everywhere (pins the online softmax) */
   double sm_scale;
 } params_t;
@@ -224,6 +239,7 @@ typedef struct {
   float *qmean;      /* [nqb][d] (only with smooth_q) */
   uint8_t* vt;       /* [d][Np] (variant 1) */
   float* vs;         /* [d] (variant 1) */
+  float* vm;         /* [d] (variant 1): v_mean, zeros without V smoothing */
 } prep_t;
 
 static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -243,13 +259,14 @@ static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, c
   if (P->variant == 1) {
     h->vt = (uint8_t*)malloc((size_t)d * Np);
     h->vs = (float*)malloc(sizeof(float) * (size_t)d);
-    quant_v_head(v, N, Np, d, h->vt, h->vs);
+    h->vm = (float*)malloc(sizeof(float) * (size_t)d);
+    quant_v_head(v, N, Np, d, P->smooth_v, h->vt, h->vs, h->vm);
   }
 }
 
 static void free_prep(prep_t* h) {
   free(h->qi); free(h->ki); free(h->qs); free(h->ks); free(h->kmean); free(h->qmean);
-  free(h->vt); free(h->vs);
+  free(h->vt); free(h->vs); free(h->vm);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -348,7 +365,7 @@ static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, cons
   if (P->exact || P->variant == 0) {
     for (int c = 0; c < d; ++c) o[c] = o[c] / l;
   } else {
-    for (int c = 0; c < d; ++c) o[c] = o[c] * (double)h->vs[c] / (448.0 * l);
+    for (int c = 0; c < d; ++c) o[c] = o[c] * (double)h->vs[c] / (448.0 * l) + (double)h->vm[c];
   }
 }
 
@@ -426,6 +443,7 @@ static int check_params(const params_t* P) {
   if (P->blk_q < 1 || P->blk_k < 1 || P->bkv < 1) return -1;
   if (P->causal != 0 && P->causal != 1) return -1;
   if (P->variant != 0 && P->variant != 1) return -1;
+  if (P->smooth_v != 0 && P->smooth_v != 1) return -1;
   if (!(P->sm_scale > 0.0) || !isfinite(P->sm_scale)) return -1;
   if ((int64_t)P->d * 127 * 127 > 2147483647LL) return -1; /* int32 bound of S */
   return 0;
@@ -440,9 +458,9 @@ static int check_params(const params_t* P) {
  */
 int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N,
                      int d, int causal, double sm_scale, int variant, int blk_q, int blk_k, int bkv,
-                     int smooth_k, int smooth_q, int exact, const int* heads, const int* rows,
+                     int smooth_k, int smooth_q, int smooth_v, int exact, const int* heads, const int* rows,
                      int n_items, double* out, int nthreads, int* threads_used) {
-  params_t P = {B, H, N, d, causal, variant, blk_q, blk_k, bkv, smooth_k, smooth_q, exact, sm_scale};
+  params_t P = {B, H, N, d, causal, variant, blk_q, blk_k, bkv, smooth_k, smooth_q, smooth_v, exact, sm_scale};
   if (check_params(&P)) return -1;
   for (int i = 0; i < n_items; ++i)
     if (heads[i] < 0 || heads[i] >= B * H || rows[i] < 0 || rows[i] >= N) return -1;
@@ -478,15 +496,15 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
 /*
  * Quantised tensors of steps 1-3 (and the FP8 V of variant 1) for all heads.
  *  q_i8, k_i8: [G][Np][d];  q_scale [G][nqb], k_scale [G][nkb];  k_mean [G][d];
- *  q_mean [G][nqb][d] (zeros unless smooth_q);  v_f8 [G][d][Np], v_scale [G][d]
- *  (only when v_f8 != NULL).  Np = oracle_pad_len(N).  Heads run on a thread pool;
+ *  q_mean [G][nqb][d] (zeros unless smooth_q);  v_f8 [G][d][Np], v_scale [G][d],
+ *  v_mean [G][d] (zeros unless smooth_v; may be NULL) (only when v_f8 != NULL).  Np = oracle_pad_len(N).  Heads run on a thread pool;
  *  each head is computed sequentially, so the result does not depend on threading.
  */
 typedef struct {
   const uint16_t *q, *k, *v;
-  int N, d, Np, blk_q, blk_k, smooth_k, smooth_q, nqb, nkb;
+  int N, d, Np, blk_q, blk_k, smooth_k, smooth_q, smooth_v, nqb, nkb;
   int8_t *q_i8, *k_i8;
-  float *q_scale, *k_scale, *k_mean, *q_mean, *v_scale;
+  float *q_scale, *k_scale, *k_mean, *q_mean, *v_scale, *v_mean;
   uint8_t* v_f8;
   int G, next;
   pthread_mutex_t mu;
@@ -507,19 +525,22 @@ static void* quant_worker(void* arg) {
                J->k_scale + (size_t)g * J->nkb, J->k_mean ? J->k_mean + (size_t)g * d : NULL, NULL);
     quant_head(J->q + g * hs, J->N, J->Np, d, J->blk_q, J->smooth_q ? 2 : 0, J->q_i8 + g * hp,
                J->q_scale + (size_t)g * J->nqb, NULL, J->q_mean ? J->q_mean + (size_t)g * J->nqb * d : NULL);
-    if (J->v_f8) quant_v_head(J->v + g * hs, J->N, J->Np, d, J->v_f8 + g * hp, J->v_scale + (size_t)g * d);
+    if (J->v_f8)
+      quant_v_head(J->v + g * hs, J->N, J->Np, d, J->smooth_v, J->v_f8 + g * hp, J->v_scale + (size_t)g * d,
+                   J->v_mean ? J->v_mean + (size_t)g * d : NULL);
   }
   return NULL;
 }
 
 int oracle_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N, int d,
-                 int blk_q, int blk_k, int smooth_k, int smooth_q, int8_t* q_i8, int8_t* k_i8,
+                 int blk_q, int blk_k, int smooth_k, int smooth_q, int smooth_v, int8_t* q_i8, int8_t* k_i8,
                  float* q_scale, float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
-                 float* v_scale) {
+                 float* v_scale, float* v_mean) {
   if (B < 1 || H < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1) return -1;
-  quantjob_t J = {q, k, v, N, d, oracle_pad_len(N), blk_q, blk_k, smooth_k, smooth_q,
+  if (smooth_v != 0 && smooth_v != 1) return -1;
+  quantjob_t J = {q, k, v, N, d, oracle_pad_len(N), blk_q, blk_k, smooth_k, smooth_q, smooth_v,
                   (N + blk_q - 1) / blk_q, (N + blk_k - 1) / blk_k, q_i8, k_i8, q_scale, k_scale,
-                  k_mean, q_mean, v_scale, v_f8, B * H, 0, PTHREAD_MUTEX_INITIALIZER};
+                  k_mean, q_mean, v_scale, v_mean, v_f8, B * H, 0, PTHREAD_MUTEX_INITIALIZER};
   int nt = pick_threads(0);
   if (nt > J.G) nt = J.G;
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);

@@ -38,6 +38,11 @@ MUTANTS = {
     "dequant drops q scale": ("sj = P->sm_scale * (double)h->qs[qb] * dk * (double)S;",
                               "sj = P->sm_scale * dk * (double)S;"),
     "p~ fp8 scale dropped": ("oracle_e4m3_encode(p[j - j0] * 448.0)", "oracle_e4m3_encode(p[j - j0])"),
+    "v mean not added back": ("/ (448.0 * l) + (double)h->vm[c];", "/ (448.0 * l);"),
+    "v mean subtracted twice": ("      if (smooth_v) x = x - mean;\n      float y = x * r;",
+                                "      if (smooth_v) x = x - mean - mean;\n      float y = x * r;"),
+    "v absmax before smoothing": ("      if (smooth_v) x = x - mean;\n      a = fmaxf(a, fabsf(x));",
+                                  "      a = fmaxf(a, fabsf(x));"),
 }
 
 
@@ -62,6 +67,11 @@ def _battery(orc):
     yield "single token", lambda: pins.test_closed_form_single_token_and_causal_row0(orc)
     yield "q smoothing term", lambda: pins.test_q_smoothing_term_restores_scores(orc)
     yield "vs fp64 cfg1", lambda: pins.test_oracle_vs_fp64_attention_config1(orc)
+    yield "v smoothing quant", lambda: pins.test_v_smoothing_quant_matches_fraction_bruteforce(orc)
+    for causal in (0, 1):
+        yield f"v smoothing constant c{causal}", (
+            lambda causal=causal: pins.test_v_smoothing_constant_v_is_returned_exactly(orc, causal))
+    yield "v smoothing offset", lambda: pins.test_v_smoothing_removes_the_channel_offset_error(orc)
 
 
 @pytest.fixture(scope="module")

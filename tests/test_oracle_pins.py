@@ -447,3 +447,75 @@ def test_int8_beats_fp8_for_qk(orc):
     s52 = fp8(q, torch.float8_e5m2, 57344.0, 128) @ np.swapaxes(fp8(k, torch.float8_e5m2, 57344.0, 64), -1, -2)
     c8, c43, c52 = cos_sim(s8, exact), cos_sim(s43, exact), cos_sim(s52, exact)
     assert c8 > c43 > c52
+
+
+# --------------------------------------------------------------------------
+# V smoothing (variant 1, optional): "SageAttention2 ..." arXiv 2502.01776
+# abstract ("smooth Q and V ... FP8 PV").  Reading: V loses its exact token mean
+# per channel before the FP8 rule, and the mean is added to O after O / l.
+# --------------------------------------------------------------------------
+
+def test_v_smoothing_quant_matches_fraction_bruteforce(orc):
+    """v_mean: exact rational mean, rounded once to double and once to float.
+    V' = fl32(V - v_mean); scale = max|V'| / 448; code = E4M3 of clamp(fl32(V' * fl32(448 / max)))
+    (torch's float8_e4m3fn cast, round to nearest even, is the independent codec)."""
+    N, d = 11, 5
+    v = _tiny(N, d, 41, shift=6.0)
+    v[0, 0, :, 4] = np.float16(2.5)          # a constant channel: V' = 0, scale 0, codes 0
+    q, k = _tiny(N, d, 42), _tiny(N, d, 43)
+    r = orc.quant(q, k, v, with_v=True, smooth_v=1)
+    vh = v[0, 0]
+    for c in range(d):
+        vm = np.float32(float(_frac_mean(vh[:, c])))
+        assert r["v_mean"][0, 0, c] == vm
+        vs = [rn32(Fraction(float(vh[t, c])) - Fraction(float(vm))) for t in range(N)]
+        a = max(abs(Fraction(float(x))) for x in vs)
+        if a == 0:
+            assert r["v_scale"][0, 0, c] == 0 and not r["v_f8"][0, 0, c].any()
+            continue
+        r448 = rn32(Fraction(448) / a)
+        ys = [float(min(448.0, max(-448.0, rn32(Fraction(float(x)) * Fraction(float(r448)))))) for x in vs]
+        codes = torch.tensor(ys, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(r["v_f8"][0, 0, c, :N], codes)
+        assert not r["v_f8"][0, 0, c, N:].any()
+        assert r["v_scale"][0, 0, c] == rn32(a / 448)
+    # without smoothing the mean output is zero and the codes are those of V itself
+    r0 = orc.quant(q, k, v, with_v=True, smooth_v=0)
+    assert not r0["v_mean"].any()
+    assert not np.array_equal(r0["v_f8"], r["v_f8"])
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_v_smoothing_constant_v_is_returned_exactly(orc, causal):
+    """Every row of V equal: V' = 0, so O is v_mean, i.e. V's row, exactly (softmax rows
+    sum to one); unsmoothed FP8 V carries its rounding error instead."""
+    rng = np.random.default_rng(44)
+    N, d = 90, 16
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    row = (rng.standard_normal(d) * 5).astype(np.float16)
+    v = np.broadcast_to(row, (1, 1, N, d)).copy()
+    o1 = orc.attn(q, k, v, causal=causal, variant=1, blk_q=64, blk_k=32, bkv=64, smooth_v=1)
+    assert np.array_equal(o1[0, 0], np.broadcast_to(row.astype(np.float64), (N, d)))
+    o0 = orc.attn(q, k, v, causal=causal, variant=1, blk_q=64, blk_k=32, bkv=64, smooth_v=0)
+    assert not np.array_equal(o0[0, 0], o1[0, 0])
+
+
+def test_v_smoothing_removes_the_channel_offset_error(orc):
+    """V with a large per-channel offset: FP8 V alone loses ~2^-4 of the offset; with V
+    smoothing only |V - v_mean| is quantised and the mean returns exactly, so the error
+    against textbook attention drops by well over 10x and stays within the FP8 bound of
+    the centred values."""
+    rng = np.random.default_rng(45)
+    N, d = 256, 32
+    q = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    off = rng.uniform(20, 60, d) * rng.choice([-1, 1], d)
+    v = (rng.standard_normal((1, 1, N, d)) + off).astype(np.float16)
+    ref = attention_fp64(q[0, 0], k[0, 0], v[0, 0])
+    kw = dict(variant=1, blk_q=64, blk_k=64, bkv=64)
+    e0 = np.max(np.abs(orc.attn(q, k, v, smooth_v=0, **kw)[0, 0] - ref))
+    e1 = np.max(np.abs(orc.attn(q, k, v, smooth_v=1, **kw)[0, 0] - ref))
+    centred = np.max(np.abs(v[0, 0].astype(np.float64) - v[0, 0].astype(np.float64).mean(0)))
+    assert e1 < e0 / 10
+    assert e1 < 2.0 ** -5 * centred
