@@ -59,6 +59,9 @@ typedef struct {
   int blk_k;    /* tokens per K scale block: 16, 32, 64 or 128 (default 64) */
   int smooth_k; /* subtract the token mean of K (default 1) */
   int smooth_q; /* subtract the block mean of Q and add its term back (default: variant == 1) */
+  int smooth_v; /* variant 1 only: subtract the token mean of V before FP8, add it to O
+                   (SageAttention2 abstract, "smooth Q and V"; default 0).  The older
+                   five-int layout (struct_size 20) is still accepted and means 0. */
 } sage_params;
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -104,6 +107,17 @@ int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sage_quant_v with optional V smoothing (SageAttention2 abstract: Q and V are
+ * smoothed).  smooth_v = 1: v_mean[B,H,d] = exact token mean of V per channel (the
+ * k_mean rule of sage_quant_qk), V' = V - v_mean in fp32, and the rule above applies
+ * to V' (v_scale = max|V'| / 448).  The attention output adds v_mean back: each row
+ * of the normalised P~ sums to one.  v_mean (16-byte aligned) is required with
+ * smooth_v and ignored without it; smooth_v = 0 is sage_quant_v.
+ */
+int sage_quant_v_ex(const void* v, int B, int H, int N, int d, int smooth_v, uint8_t* v_f8,
+                    float* v_scale, float* v_mean, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * o = SageAttention(q, k, v): the whole plug-and-play forward (quantisation kernels
  * plus the attention kernel; for variant 0 without Q smoothing the attention kernel
  * quantises Q itself, see sage_attn_fwd_qf16).  causal: key j is visible to query i iff j <= i.
@@ -120,15 +134,17 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B
                      size_t ws_bytes, void* stream);
 
 /*
- * The attention kernel alone, on tensors sage_quant_qk / sage_quant_v produced
- * (same p).  Variant 0 reads v (fp16); variant 1 reads v_f8 / v_scale and, with
- * smooth_q, q_mean.  Used to time the attention kernel by itself.
+ * The attention kernel alone, on tensors sage_quant_qk / sage_quant_v(_ex) produced
+ * (same p).  Variant 0 reads v (fp16); variant 1 reads v_f8 / v_scale, with
+ * smooth_q q_mean, and with smooth_v v_mean (16-byte aligned, [B,H,d]).  Pointers a
+ * call does not read may be NULL.  Used to time the attention kernel by itself.
+ * (Library 0.2 added v_mean after v_scale.)
  */
 int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* q_scale,
                            const float* k_scale, const float* q_mean, const void* v,
-                           const uint8_t* v_f8, const float* v_scale, void* o, int B, int H, int N,
-                           int d, int causal, float sm_scale, int variant, const sage_params* p,
-                           void* stream);
+                           const uint8_t* v_f8, const float* v_scale, const float* v_mean, void* o,
+                           int B, int H, int N, int d, int causal, float sm_scale, int variant,
+                           const sage_params* p, void* stream);
 
 /*
  * The attention kernel that sage_attn_fwd runs for variant 0 without Q smoothing: Q

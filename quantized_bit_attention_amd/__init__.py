@@ -34,7 +34,7 @@ class SageError(RuntimeError):
 
 class _Params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_int), ("blk_q", ctypes.c_int), ("blk_k", ctypes.c_int),
-                ("smooth_k", ctypes.c_int), ("smooth_q", ctypes.c_int)]
+                ("smooth_k", ctypes.c_int), ("smooth_q", ctypes.c_int), ("smooth_v", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -58,9 +58,10 @@ def _load():
         "sage_workspace_bytes": ([I, I, I, I, I, PP], S),
         "sage_quant_qk": ([P, P, I, I, I, I, PP, P, P, P, P, P, P, P, S, P], I),
         "sage_quant_v": ([P, I, I, I, I, P, P, P, S, P], I),
+        "sage_quant_v_ex": ([P, I, I, I, I, I, P, P, P, P, S, P], I),
         "sage_attn_fwd": ([P, P, P, P, I, I, I, I, I, F, I, P, S, P], I),
         "sage_attn_fwd_ex": ([P, P, P, P, I, I, I, I, I, F, I, PP, P, S, P], I),
-        "sage_attn_fwd_prequant": ([P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
+        "sage_attn_fwd_prequant": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
         "sage_attn_fwd_qf16": ([P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
         "sage_last_error": ([], ctypes.c_char_p),
@@ -79,8 +80,9 @@ def _check(rc: int, what: str):
         raise SageError(f"{what} failed ({rc}): {msg}")
 
 
-def _params(blk_q=128, blk_k=64, smooth_k=True, smooth_q=False) -> _Params:
-    return _Params(ctypes.sizeof(_Params), int(blk_q), int(blk_k), int(bool(smooth_k)), int(bool(smooth_q)))
+def _params(blk_q=128, blk_k=64, smooth_k=True, smooth_q=False, smooth_v=False) -> _Params:
+    return _Params(ctypes.sizeof(_Params), int(blk_q), int(blk_k), int(bool(smooth_k)), int(bool(smooth_q)),
+                   int(bool(smooth_v)))
 
 
 def _ptr(t):
@@ -113,10 +115,11 @@ def kv_tile(variant: int, d: int) -> int:
     return _load().sage_kv_tile(variant, d)
 
 
-def workspace_bytes(B, H, N, d, variant=0, blk_q=128, blk_k=64, smooth_k=True, smooth_q=None) -> int:
+def workspace_bytes(B, H, N, d, variant=0, blk_q=128, blk_k=64, smooth_k=True, smooth_q=None,
+                    smooth_v=False) -> int:
     if smooth_q is None:
         smooth_q = variant == VARIANT_FP8PV
-    p = _params(blk_q, blk_k, smooth_k, smooth_q)
+    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v)
     return _load().sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))
 
 
@@ -129,8 +132,10 @@ def _workspace(nbytes, device, workspace):
 
 
 def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128, blk_k=64,
-         smooth_k=True, smooth_q=None, out=None, workspace=None):
-    """o = SageAttention(q, k, v) for [B, H, N, d] fp16 tensors on the GPU."""
+         smooth_k=True, smooth_q=None, smooth_v=False, out=None, workspace=None):
+    """o = SageAttention(q, k, v) for [B, H, N, d] fp16 tensors on the GPU.
+
+    smooth_v (variant 1 only) subtracts V's token mean before FP8 and adds it to O."""
     B, H, N, d = _check_qkv(q, k, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -138,7 +143,7 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
         smooth_q = variant == VARIANT_FP8PV
     if out is None:
         out = torch.empty_like(q)
-    p = _params(blk_q, blk_k, smooth_k, smooth_q)
+    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v)
     lib = _load()
     nbytes = lib.sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))
     if nbytes == 0:
@@ -173,24 +178,27 @@ def quant_qk(q, k, blk_q=128, blk_k=64, smooth_k=True, smooth_q=False) -> dict:
     return r
 
 
-def quant_v(v) -> dict:
-    """FP8 E4M3 V with per-channel scales: v_f8 [B, H, d, Np] (uint8 codes), v_scale [B, H, d]."""
+def quant_v(v, smooth_v=False) -> dict:
+    """FP8 E4M3 V with per-channel scales: v_f8 [B, H, d, Np] (uint8 codes), v_scale [B, H, d],
+    v_mean [B, H, d] (the token mean taken out with smooth_v, else zeros)."""
     B, H, N, d = _check_qkv(v)
     dev = v.device
     Np = pad_len(N)
     r = dict(v_f8=torch.empty((B, H, d, Np), dtype=torch.uint8, device=dev),
-             v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev))
+             v_scale=torch.empty((B, H, d), dtype=torch.float32, device=dev),
+             v_mean=torch.zeros((B, H, d), dtype=torch.float32, device=dev))
     lib = _load()
     ws = _workspace(lib.sage_workspace_bytes(B, H, N, d, 1, None), dev, None)
-    rc = lib.sage_quant_v(_ptr(v), B, H, N, d, _ptr(r["v_f8"]), _ptr(r["v_scale"]), _ptr(ws), ws.numel(),
-                          _stream(dev))
-    _check(rc, "sage_quant_v")
+    rc = lib.sage_quant_v_ex(_ptr(v), B, H, N, d, int(bool(smooth_v)), _ptr(r["v_f8"]), _ptr(r["v_scale"]),
+                             _ptr(r["v_mean"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "sage_quant_v_ex")
     return r
 
 
 def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_FP16PV, vq: dict | None = None,
-                  blk_q=128, blk_k=64, smooth_q=None, out=None):
-    """The attention kernel alone, on quant_qk() / quant_v() outputs."""
+                  blk_q=128, blk_k=64, smooth_q=None, smooth_v=False, out=None):
+    """The attention kernel alone, on quant_qk() / quant_v() outputs (quant_v(smooth_v=True) with
+    smooth_v)."""
     B, H, Np, d = qk["q_i8"].shape
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -199,12 +207,12 @@ def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_F
     dev = qk["q_i8"].device
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
-    p = _params(blk_q, blk_k, True, smooth_q)
+    p = _params(blk_q, blk_k, True, smooth_q, smooth_v)
     rc = _load().sage_attn_fwd_prequant(
         _ptr(qk["q_i8"]), _ptr(qk["k_i8"]), _ptr(qk["q_scale"]), _ptr(qk["k_scale"]),
         _ptr(qk["q_mean"]) if smooth_q else None, _ptr(v) if variant == 0 else None,
         _ptr(vq["v_f8"]) if variant == 1 else None, _ptr(vq["v_scale"]) if variant == 1 else None,
-        _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale), int(variant), ctypes.byref(p), _stream(dev))
+        _ptr(vq["v_mean"]) if smooth_v else None, _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale), int(variant), ctypes.byref(p), _stream(dev))
     _check(rc, "sage_attn_fwd_prequant")
     return out
 

@@ -39,26 +39,33 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
 struct Params {
-  int blk_q = 128, blk_k = 64, smooth_k = 1, smooth_q = 0;
+  int blk_q = 128, blk_k = 64, smooth_k = 1, smooth_q = 0, smooth_v = 0;
 };
+
+// sage_params before smooth_v was added (library 0.1): five ints.
+constexpr int kParamsV1Size = 5 * (int)sizeof(int);
 
 int read_params(const sage_params* p, int variant, Params* out) {
   Params r;
   r.smooth_q = variant == SAGE_VARIANT_INT8QK_FP8PV ? 1 : 0;
   if (p) {
-    if (p->struct_size != (int)sizeof(sage_params))
+    if (p->struct_size != (int)sizeof(sage_params) && p->struct_size != kParamsV1Size)
       return fail(SAGE_ERR_INVALID_ARG, "sage_params.struct_size must be %d", (int)sizeof(sage_params));
     r.blk_q = p->blk_q;
     r.blk_k = p->blk_k;
     r.smooth_k = p->smooth_k;
     r.smooth_q = p->smooth_q;
+    if (p->struct_size >= (int)sizeof(sage_params)) r.smooth_v = p->smooth_v;
   }
   if (r.blk_q != 32 && r.blk_q != 64 && r.blk_q != 128)
     return fail(SAGE_ERR_UNSUPPORTED, "blk_q must be 32, 64 or 128 (got %d)", r.blk_q);
   if (r.blk_k != 16 && r.blk_k != 32 && r.blk_k != 64 && r.blk_k != 128)
     return fail(SAGE_ERR_UNSUPPORTED, "blk_k must be 16, 32, 64 or 128 (got %d)", r.blk_k);
-  if ((r.smooth_k != 0 && r.smooth_k != 1) || (r.smooth_q != 0 && r.smooth_q != 1))
-    return fail(SAGE_ERR_INVALID_ARG, "smooth_k / smooth_q must be 0 or 1");
+  if ((r.smooth_k != 0 && r.smooth_k != 1) || (r.smooth_q != 0 && r.smooth_q != 1) ||
+      (r.smooth_v != 0 && r.smooth_v != 1))
+    return fail(SAGE_ERR_INVALID_ARG, "smooth_k / smooth_q / smooth_v must be 0 or 1");
+  if (r.smooth_v && variant != SAGE_VARIANT_INT8QK_FP8PV)
+    return fail(SAGE_ERR_UNSUPPORTED, "smooth_v applies to the FP8 P~V variant only");
   *out = r;
   return SAGE_OK;
 }
@@ -82,7 +89,7 @@ bool fuse_q(int variant, const Params& p) { return variant == 0 && !p.smooth_q; 
 
 // Workspace layout (each piece 256-byte aligned).
 struct Layout {
-  size_t ksum, vmax, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, total;
+  size_t ksum, vsum, vmax, vmin, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, v_mean, total;
 };
 
 size_t up(size_t x) { return (x + 255) / 256 * 256; }
@@ -94,7 +101,9 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
   L.ksum = take(G * ns * d * sizeof(long long));
+  L.vsum = take(variant == 1 ? G * ns * d * sizeof(long long) : 0);
   L.vmax = take(variant == 1 ? G * ns * d * sizeof(float) : 0);
+  L.vmin = take(variant == 1 ? G * ns * d * sizeof(float) : 0);
   const bool fq = fuse_q(variant, p);
   L.q_i8 = take(fq ? 0 : G * Np * d);
   L.k_i8 = take(G * Np * d);
@@ -104,6 +113,7 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
   L.v_f8 = take(variant == 1 ? G * d * Np : 0);
   L.v_scale = take(variant == 1 ? G * d * sizeof(float) : 0);
+  L.v_mean = take(p.smooth_v ? G * d * sizeof(float) : 0);
   L.total = off;
   return L;
 }
@@ -167,7 +177,7 @@ int run_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const
                  hipStream_t st) {
   hipError_t e;
   if (p.smooth_k) {
-    e = sage::launch_stats(d, k, nullptr, B * H, N, ksum, nullptr, st);
+    e = sage::launch_stats(d, k, nullptr, B * H, N, sage::StatsOut{ksum, nullptr, nullptr, nullptr}, st);
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
   e = sage::launch_quant(d, quant_args(q, k, B, H, N, d, p, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, ksum), st);
@@ -194,9 +204,10 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   hipStream_t st = (hipStream_t)stream;
   const int G = B * H, Np = pad_len(N);
   hipError_t e;
+  const sage::StatsOut stats{at<long long>(ws, L.ksum), at<long long>(ws, L.vsum), at<float>(ws, L.vmax),
+                             at<float>(ws, L.vmin)};
   if (p.smooth_k || variant == 1) {
-    e = sage::launch_stats(d, k, variant == 1 ? v : nullptr, G, N, at<long long>(ws, L.ksum),
-                           variant == 1 ? at<float>(ws, L.vmax) : nullptr, st);
+    e = sage::launch_stats(d, k, variant == 1 ? v : nullptr, G, N, stats, st);
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
   const bool fq = fuse_q(variant, p);
@@ -208,8 +219,8 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   e = sage::launch_quant(d, qa, st);
   if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
   if (variant == 1) {
-    e = sage::launch_quant_v(d, v, G, N, Np, at<float>(ws, L.vmax), at<uint8_t>(ws, L.v_f8),
-                             at<float>(ws, L.v_scale), st);
+    e = sage::launch_quant_v(d, v, G, N, Np, stats, p.smooth_v, at<uint8_t>(ws, L.v_f8), at<float>(ws, L.v_scale),
+                             p.smooth_v ? at<float>(ws, L.v_mean) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
   }
   sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
@@ -222,6 +233,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   a.v = (const uint16_t*)v;
   a.v_f8 = variant == 1 ? at<uint8_t>(ws, L.v_f8) : nullptr;
   a.v_scale = variant == 1 ? at<float>(ws, L.v_scale) : nullptr;
+  a.v_mean = p.smooth_v ? at<float>(ws, L.v_mean) : nullptr;
   a.o = (uint16_t*)o;
   e = sage::launch_attn(d, variant, causal, p.smooth_q, a, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
@@ -232,7 +244,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
 
 extern "C" {
 
-int sage_version(void) { return 100; }
+int sage_version(void) { return 200; }
 
 int sage_pad_len(int N) { return N < 1 ? -1 : pad_len(N); }
 
@@ -268,25 +280,32 @@ int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, cons
   return rc ? rc : ok();
 }
 
-int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float* v_scale, void* ws,
-                 size_t ws_bytes, void* stream) {
+int sage_quant_v_ex(const void* v, int B, int H, int N, int d, int smooth_v, uint8_t* v_f8, float* v_scale,
+                    float* v_mean, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(B, H, N, d))) return rc;
+  if (smooth_v != 0 && smooth_v != 1) return fail(SAGE_ERR_INVALID_ARG, "smooth_v must be 0 or 1");
   if ((rc = check_ptr(v, 16, "v")) || (rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")))
     return rc;
+  if (smooth_v && (rc = check_ptr(v_mean, 16, "v_mean (required with smooth_v)"))) return rc;
   const size_t G = (size_t)B * H, ns = ceil_div(N, sage::kStatRows);
-  const size_t off_v = up(G * ns * d * sizeof(long long));
-  const size_t need = off_v + up(G * ns * d * sizeof(float));
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  const size_t i64 = up(G * ns * d * sizeof(long long)), f32 = up(G * ns * d * sizeof(float));
+  if ((rc = check_ws(ws, ws_bytes, 2 * i64 + 2 * f32))) return rc;
   hipStream_t st = (hipStream_t)stream;
-  long long* ksum = (long long*)ws;
-  float* vmax = at<float>(ws, off_v);
+  const sage::StatsOut stats{at<long long>(ws, 0), at<long long>(ws, i64), at<float>(ws, 2 * i64),
+                             at<float>(ws, 2 * i64 + f32)};
   // the statistics pass reads K and V together; with V as "K" too the K sums are unused
-  hipError_t e = sage::launch_stats(d, v, v, (int)G, N, ksum, vmax, st);
+  hipError_t e = sage::launch_stats(d, v, v, (int)G, N, stats, st);
   if (e != hipSuccess) return hip_fail(e, "statistics kernel");
-  e = sage::launch_quant_v(d, v, (int)G, N, pad_len(N), vmax, v_f8, v_scale, st);
+  e = sage::launch_quant_v(d, v, (int)G, N, pad_len(N), stats, smooth_v, v_f8, v_scale, smooth_v ? v_mean : nullptr,
+                           st);
   if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
   return ok();
+}
+
+int sage_quant_v(const void* v, int B, int H, int N, int d, uint8_t* v_f8, float* v_scale, void* ws,
+                 size_t ws_bytes, void* stream) {
+  return sage_quant_v_ex(v, B, H, N, d, 0, v_f8, v_scale, nullptr, ws, ws_bytes, stream);
 }
 
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
@@ -300,9 +319,9 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B
 }
 
 int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* q_scale, const float* k_scale,
-                           const float* q_mean, const void* v, const uint8_t* v_f8, const float* v_scale, void* o,
-                           int B, int H, int N, int d, int causal, float sm_scale, int variant,
-                           const sage_params* pp, void* stream) {
+                           const float* q_mean, const void* v, const uint8_t* v_f8, const float* v_scale,
+                           const float* v_mean, void* o, int B, int H, int N, int d, int causal, float sm_scale,
+                           int variant, const sage_params* pp, void* stream) {
   int rc;
   if ((rc = check_shape(B, H, N, d))) return rc;
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -318,6 +337,7 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
   if (variant == 0 && (rc = check_ptr(v, 16, "v"))) return rc;
   if (variant == 1 && ((rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")))) return rc;
   if (p.smooth_q && (rc = check_ptr(q_mean, 4, "q_mean (required with smooth_q)"))) return rc;
+  if (p.smooth_v && (rc = check_ptr(v_mean, 16, "v_mean (required with smooth_v)"))) return rc;
   sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
   a.q_i8 = q_i8;
   a.k_i8 = k_i8;
@@ -327,6 +347,7 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
   a.v = (const uint16_t*)v;
   a.v_f8 = v_f8;
   a.v_scale = v_scale;
+  a.v_mean = p.smooth_v ? v_mean : nullptr;
   a.o = (uint16_t*)o;
   hipError_t e = sage::launch_attn(d, variant, causal, p.smooth_q, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");

@@ -636,6 +636,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       if (VARIANT == 1) {
         const float4 dv = *reinterpret_cast<const float4*>(a.v_scale + (size_t)g * D + c0);
         y[0] *= dv.x; y[1] *= dv.y; y[2] *= dv.z; y[3] *= dv.w;
+        if (a.v_mean) {  // V smoothing: every row of P~ sums to one after the division by l
+          const float4 vm = *reinterpret_cast<const float4*>(a.v_mean + (size_t)g * D + c0);
+          y[0] += vm.x; y[1] += vm.y; y[2] += vm.z; y[3] += vm.w;
+        }
       }
       *reinterpret_cast<uint2*>(orow + c0) = make_uint2(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]));
     }

@@ -30,6 +30,7 @@ struct AttnArgs {
   const uint16_t* v;      // [G][N][D] fp16 (variant 0)
   const uint8_t* v_f8;    // [G][D][Np] (variant 1)
   const float* v_scale;   // [G][D] (variant 1)
+  const float* v_mean;    // [G][D] (variant 1 with V smoothing) or null
   uint16_t* o;            // [G][N][D] fp16
   int G, N, Np, blk_q, blk_k, nqb, nkb;
   float kscale;           // sm_scale * log2(e)
@@ -39,11 +40,18 @@ struct AttnArgs {
 // sum per (head, split of kStatRows tokens, channel)
 constexpr int kStatRows = 256;
 int stat_splits(int N);
-hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long long* ksum_part,
-                        float* vmax_part, hipStream_t st);
+// Statistics pass outputs, [G][nsplit][D] each, folded into split 0 by the pass; the V
+// arrays are only written when V is given.
+struct StatsOut {
+  long long* ksum;  // exact sums of K in units of 2^-24
+  long long* vsum;  // the same for V
+  float* vmax;      // max of V per channel
+  float* vmin;      // min of V per channel
+};
+hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, const StatsOut& out, hipStream_t st);
 hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st);
-hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const float* vmax_part,
-                          uint8_t* v_f8, float* v_scale, hipStream_t st);
+hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
+                          uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st);
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st);
 hipError_t launch_debug_qk(int d, const int8_t* q_i8, const int8_t* k_i8, int G, int Np, const int* tiles,
                            int n_tiles, int32_t* s_out, hipStream_t st);

@@ -20,8 +20,8 @@
 namespace sage {
 
 // Pass 1: per (head, split of kStatRows tokens) partial sums of K (exact, int64) and,
-// when v != nullptr, partial max |V| per channel.
-//   ksum_part [G][nsplit][D] int64, vmax_part [G][nsplit][D] fp32.
+// for WITH_V, of V, plus the partial max and min of V per channel.
+//   ksum_part, vsum_part [G][nsplit][D] int64; vmax_part, vmin_part [G][nsplit][D] fp32.
 // A thread accumulates its at most kStatRows / RPI values per channel in fp64, which is
 // exact: every fp16 value is an integer multiple of 2^-24 below 2^16 in magnitude, so
 // up to 2^13 of them sum exactly within fp64's 53-bit significand.  The thread totals
@@ -31,7 +31,9 @@ template <int D, bool WITH_V>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, int N,
                                                          int nsplit, long long* __restrict__ ksum_part,
-                                                         float* __restrict__ vmax_part) {
+                                                         long long* __restrict__ vsum_part,
+                                                         float* __restrict__ vmax_part,
+                                                         float* __restrict__ vmin_part) {
   constexpr int TPR = D / 8;            // threads per row
   constexpr int RPI = kThreads / TPR;   // rows per iteration
   constexpr int NIT = kStatRows / RPI;  // rows per thread
@@ -42,10 +44,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   const size_t head = (size_t)g * N * D;
   const int t0 = split * kStatRows, t1 = min(N, t0 + kStatRows);
 
-  double acc[8];
-  float vm[8];
+  double acc[8], vacc[8];
+  float vm[8], vn[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { acc[j] = 0.0; vm[j] = 0.0f; }
+  for (int j = 0; j < 8; ++j) { acc[j] = 0.0; vacc[j] = 0.0; vm[j] = -INFINITY; vn[j] = INFINITY; }
 
 #pragma unroll 1
   for (int base = 0; base < NIT; base += BATCH) {
@@ -66,58 +68,91 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
         const f16x2 hk = __builtin_bit_cast(f16x2, w[j]);
         acc[2 * j] += (double)(float)hk[0];
         acc[2 * j + 1] += (double)(float)hk[1];
-        const f16x2 hv = __builtin_bit_cast(f16x2, u[j]);
-        vm[2 * j] = fmaxf(vm[2 * j], fabsf((float)hv[0]));
-        vm[2 * j + 1] = fmaxf(vm[2 * j + 1], fabsf((float)hv[1]));
+        if (WITH_V) {
+          // rows past N hold zeros; they stay out of the max and min below
+          const f16x2 hv = __builtin_bit_cast(f16x2, u[j]);
+          const bool in = t0 + r0 + RPI * (base + b) < t1;
+          vacc[2 * j] += (double)(float)hv[0];
+          vacc[2 * j + 1] += (double)(float)hv[1];
+          vm[2 * j] = in ? fmaxf(vm[2 * j], (float)hv[0]) : vm[2 * j];
+          vm[2 * j + 1] = in ? fmaxf(vm[2 * j + 1], (float)hv[1]) : vm[2 * j + 1];
+          vn[2 * j] = in ? fminf(vn[2 * j], (float)hv[0]) : vn[2 * j];
+          vn[2 * j + 1] = in ? fminf(vn[2 * j + 1], (float)hv[1]) : vn[2 * j + 1];
+        }
       }
     }
   }
 
+  // two rounds through LDS: (K sums, V max), then (V sums, V min)
   __shared__ long long s_sum[kThreads][8];
   __shared__ float s_max[kThreads][8];
+  const size_t o = ((size_t)g * nsplit + split) * D + tid;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    s_sum[tid][j] = (long long)(acc[j] * 16777216.0);  // exact: an integer below 2^53
-    s_max[tid][j] = vm[j];
-  }
-  __syncthreads();
-  if (tid < D) {
-    const int c = tid, cgc = c / 8, jj = c % 8;
-    long long s = 0;
-    float m = 0.0f;
-    for (int r = 0; r < RPI; ++r) {
-      s += s_sum[r * TPR + cgc][jj];
-      m = fmaxf(m, s_max[r * TPR + cgc][jj]);
+  for (int round = 0; round < (WITH_V ? 2 : 1); ++round) {
+    if (round) __syncthreads();  // the first round's reads are done
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s_sum[tid][j] = (long long)((round ? vacc[j] : acc[j]) * 16777216.0);  // exact: an integer below 2^53
+      s_max[tid][j] = round ? vn[j] : vm[j];
     }
-    const size_t o = ((size_t)g * nsplit + split) * D + c;
-    ksum_part[o] = s;
-    if (WITH_V) vmax_part[o] = m;
+    __syncthreads();
+    if (tid < D) {
+      const int cgc = tid / 8, jj = tid % 8;
+      long long sm = 0;
+      float m = round ? INFINITY : -INFINITY;
+      for (int r = 0; r < RPI; ++r) {
+        sm += s_sum[r * TPR + cgc][jj];
+        m = round ? fminf(m, s_max[r * TPR + cgc][jj]) : fmaxf(m, s_max[r * TPR + cgc][jj]);
+      }
+      if (round == 0) {
+        ksum_part[o] = sm;
+        if (WITH_V) vmax_part[o] = m;
+      } else {
+        vsum_part[o] = sm;
+        vmin_part[o] = m;
+      }
+    }
   }
 }
 
 // Pass 1b: fold the per-split partials of each head into split 0 (exact int64 sums of
-// K, max |V|), so the later passes read D values per head instead of nsplit * D.
-// Four threads per channel take every fourth split, then combine through LDS.
+// K and V, max and min of V), so the later passes read D values per head instead of
+// nsplit * D.  Four threads per channel take every fourth split, then combine
+// through LDS.  The V arrays are null when only K was summed.
 template <int D>
 __global__ __launch_bounds__(4 * D) void stats_finalize_kernel(int nsplit, long long* __restrict__ ksum_part,
-                                                               float* __restrict__ vmax_part) {
-  __shared__ long long s_sum[4][D];
-  __shared__ float s_max[4][D];
+                                                               long long* __restrict__ vsum_part,
+                                                               float* __restrict__ vmax_part,
+                                                               float* __restrict__ vmin_part) {
+  __shared__ long long s_sum[4][D], s_vsum[4][D];
+  __shared__ float s_max[4][D], s_min[4][D];
   const int g = blockIdx.x, c = threadIdx.x % D, j = threadIdx.x / D;
   const size_t base = (size_t)g * nsplit * D + c;
-  long long s = 0;
-  float m = 0.0f;
+  const bool with_v = vsum_part != nullptr;
+  long long s = 0, vs = 0;
+  float mx = -INFINITY, mn = INFINITY;
 #pragma unroll 4
   for (int sp = j; sp < nsplit; sp += 4) {
-    if (ksum_part) s += ksum_part[base + (size_t)sp * D];
-    if (vmax_part) m = fmaxf(m, vmax_part[base + (size_t)sp * D]);
+    const size_t o = base + (size_t)sp * D;
+    s += ksum_part[o];
+    if (with_v) {
+      vs += vsum_part[o];
+      mx = fmaxf(mx, vmax_part[o]);
+      mn = fminf(mn, vmin_part[o]);
+    }
   }
   s_sum[j][c] = s;
-  s_max[j][c] = m;
+  s_vsum[j][c] = vs;
+  s_max[j][c] = mx;
+  s_min[j][c] = mn;
   __syncthreads();  // every thread has read its splits before split 0 is overwritten
   if (j == 0) {
-    if (ksum_part) ksum_part[base] = s_sum[0][c] + s_sum[1][c] + s_sum[2][c] + s_sum[3][c];
-    if (vmax_part) vmax_part[base] = fmaxf(fmaxf(s_max[0][c], s_max[1][c]), fmaxf(s_max[2][c], s_max[3][c]));
+    ksum_part[base] = s_sum[0][c] + s_sum[1][c] + s_sum[2][c] + s_sum[3][c];
+    if (with_v) {
+      vsum_part[base] = s_vsum[0][c] + s_vsum[1][c] + s_vsum[2][c] + s_vsum[3][c];
+      vmax_part[base] = fmaxf(fmaxf(s_max[0][c], s_max[1][c]), fmaxf(s_max[2][c], s_max[3][c]));
+      vmin_part[base] = fminf(fminf(s_min[0][c], s_min[1][c]), fminf(s_min[2][c], s_min[3][c]));
+    }
   }
 }
 
@@ -249,23 +284,36 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 }
 
 // Pass 3 (variant 1): V -> FP8 E4M3 with per-channel scales, transposed to [G][D][Np].
+// With V smoothing each channel first loses its exact token mean (v_mean, from the
+// pass-1 sums); the absmax of V - v_mean is max(fl(max - v_mean), fl(v_mean - min))
+// because rounding is monotonic, so no second pass over V is needed.
 // One workgroup per (64-token tile, head); the tile goes through LDS so both the fp16
 // reads and the fp8 writes are contiguous.
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __restrict__ v, int N, int Np,
-                                                           int nsplit, const float* __restrict__ vmax_part,
+                                                           int nsplit, const long long* __restrict__ vsum_part,
+                                                           const float* __restrict__ vmax_part,
+                                                           const float* __restrict__ vmin_part, int smooth_v,
                                                            uint8_t* __restrict__ v_f8,
-                                                           float* __restrict__ v_scale) {
+                                                           float* __restrict__ v_scale,
+                                                           float* __restrict__ v_mean) {
   constexpr int TPR = D / 8;
   constexpr int RPI = kThreads / TPR;
   constexpr int TT = 64;  // tokens per tile
-  __shared__ float s_r[D];
+  __shared__ float s_r[D], s_mean[D];
   __shared__ uint8_t s_t[D][TT + 4];
   const int tile = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   if (tid < D) {
-    const float m = vmax_part[(size_t)g * nsplit * D + tid];  // folded into split 0
+    const size_t o = (size_t)g * nsplit * D + tid;  // folded into split 0
+    const float mean = smooth_v ? fixed24_mean(vsum_part[o], N) : 0.0f;
+    const float hi = vmax_part[o] - mean, lo = mean - vmin_part[o];
+    const float m = fmaxf(hi, lo) > 0.0f ? fmaxf(hi, lo) : 0.0f;  // +0 for a constant channel
     s_r[tid] = m > 0.0f ? 448.0f / m : 0.0f;
-    if (tile == 0) v_scale[(size_t)g * D + tid] = m / 448.0f;
+    s_mean[tid] = mean;
+    if (tile == 0) {
+      v_scale[(size_t)g * D + tid] = m / 448.0f;
+      if (v_mean) v_mean[(size_t)g * D + tid] = mean;
+    }
   }
   __syncthreads();
   const int cg = tid % TPR, r0 = tid / TPR;
@@ -275,12 +323,15 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __res
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (t < N) raw = *reinterpret_cast<const uint4*>(v + head + (size_t)t * D + cg * 8);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const bool centre = smooth_v && t < N;  // padding columns stay code 0
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f16x2 h = __builtin_bit_cast(f16x2, w[j]);
       const int c = cg * 8 + 2 * j;
-      float y0 = fminf(fmaxf((float)h[0] * s_r[c], -448.0f), 448.0f);
-      float y1 = fminf(fmaxf((float)h[1] * s_r[c + 1], -448.0f), 448.0f);
+      const float x0 = centre ? (float)h[0] - s_mean[c] : (float)h[0];
+      const float x1 = centre ? (float)h[1] - s_mean[c + 1] : (float)h[1];
+      float y0 = fminf(fmaxf(x0 * s_r[c], -448.0f), 448.0f);
+      float y1 = fminf(fmaxf(x1 * s_r[c + 1], -448.0f), 448.0f);
       const uint32_t p = cvt_pk_fp8(y0, y1, 0u, false);
       s_t[c][rr] = (uint8_t)(p & 0xffu);
       s_t[c + 1][rr] = (uint8_t)((p >> 8) & 0xffu);
@@ -306,24 +357,24 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __res
 int stat_splits(int N) { return (N + kStatRows - 1) / kStatRows; }
 
 template <int D>
-static void launch_stats_d(const void* k, const void* v, int G, int N, long long* ksum_part, float* vmax_part,
-                           hipStream_t st) {
+static void launch_stats_d(const void* k, const void* v, int G, int N, const StatsOut& out, hipStream_t st) {
   const int ns = stat_splits(N);
   dim3 grid(ns, G);
   if (v)
-    stats_kernel<D, true><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, ns, ksum_part,
-                                                     vmax_part);
+    stats_kernel<D, true><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, ns, out.ksum,
+                                                     out.vsum, out.vmax, out.vmin);
   else
-    stats_kernel<D, false><<<grid, kThreads, 0, st>>>((const uint16_t*)k, nullptr, N, ns, ksum_part, nullptr);
-  stats_finalize_kernel<D><<<G, 4 * D, 0, st>>>(ns, ksum_part, v ? vmax_part : nullptr);
+    stats_kernel<D, false><<<grid, kThreads, 0, st>>>((const uint16_t*)k, nullptr, N, ns, out.ksum, nullptr,
+                                                      nullptr, nullptr);
+  stats_finalize_kernel<D><<<G, 4 * D, 0, st>>>(ns, out.ksum, v ? out.vsum : nullptr, v ? out.vmax : nullptr,
+                                                v ? out.vmin : nullptr);
 }
 
-hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, long long* ksum_part,
-                        float* vmax_part, hipStream_t st) {
+hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, const StatsOut& out, hipStream_t st) {
   if (d == 64)
-    launch_stats_d<64>(k, v, G, N, ksum_part, vmax_part, st);
+    launch_stats_d<64>(k, v, G, N, out, st);
   else
-    launch_stats_d<128>(k, v, G, N, ksum_part, vmax_part, st);
+    launch_stats_d<128>(k, v, G, N, out, st);
   return hipGetLastError();
 }
 
@@ -345,15 +396,16 @@ hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st) {
   return d == 64 ? launch_quant_d<64>(a, st) : launch_quant_d<128>(a, st);
 }
 
-hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const float* vmax_part,
-                          uint8_t* v_f8, float* v_scale, hipStream_t st) {
+hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
+                          uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st) {
   dim3 grid(Np / 64, G);
+  const int ns = stat_splits(N);
   if (d == 64)
-    quant_v_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, stat_splits(N), vmax_part, v_f8,
-                                                  v_scale);
+    quant_v_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, ns, stats.vsum, stats.vmax, stats.vmin,
+                                                  smooth_v, v_f8, v_scale, v_mean);
   else
-    quant_v_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, stat_splits(N), vmax_part, v_f8,
-                                                   v_scale);
+    quant_v_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, ns, stats.vsum, stats.vmax,
+                                                   stats.vmin, smooth_v, v_f8, v_scale, v_mean);
   return hipGetLastError();
 }
 

@@ -51,12 +51,14 @@ def host(t):
 
 
 def cfg_kw(c):
-    return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"])
+    return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"],
+                smooth_v=bool(c.get("smooth_v", 0)))
 
 
 def oracle_kw(c, bkv=64):
     return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"], bkv=bkv,
-                smooth_k=c.get("smooth_k", 1), smooth_q=c.get("smooth_q", 1 if c["variant"] == 1 else 0))
+                smooth_k=c.get("smooth_k", 1), smooth_q=c.get("smooth_q", 1 if c["variant"] == 1 else 0),
+                smooth_v=c.get("smooth_v", 0))
 
 
 def check_o(name, g16, o64):
@@ -102,12 +104,23 @@ def test_quant_qk_bitexact(sage, orc, cfg):
         assert same, key
 
 
-@pytest.mark.parametrize("case", ["cfg5", "ragged_d64", "ties"])
-def test_quant_v_bitexact(sage, orc, case):
+@pytest.mark.parametrize("smooth_v", [0, 1])
+@pytest.mark.parametrize("case", ["cfg5", "ragged_d64", "ties", "offset", "const_channels"])
+def test_quant_v_bitexact(sage, orc, case, smooth_v):
     if case == "cfg5":
         v = inputs(5)["v"]
     elif case == "ragged_d64":
         v = workloads.make_inputs(1, N=333, B=1, H=3)["v"]
+    elif case == "offset":
+        v = workloads.make_inputs(5, N=777, B=1, H=2, v_sigma=1.0)["v"]
+    elif case == "const_channels":
+        # constant channels: zero, positive, negative; with V smoothing all become 0
+        # (scale 0, codes 0) and the mean carries the whole channel
+        v = workloads.make_inputs(1, N=300, B=1, H=2)["v"].copy()
+        v[0, 0, :, 0] = 0
+        v[0, 0, :, 1] = 1.5
+        v[0, 1, :, 5] = -0.2
+        v[0, 1, :, 63] = 65504
     else:
         # every channel's absmax is 448, so the scale is 1 and the codes are E4M3(V):
         # the values are all E4M3 ties, their fp16 neighbours and the codes themselves
@@ -127,10 +140,11 @@ def test_quant_v_bitexact(sage, orc, case):
         v = np.tile(col[:, None], (1, 64))[None, None].copy()
         v[0, 0, :, 1::2] *= np.float16(-1)
         v = v.astype(np.float16)
-    say(f"quant_v {case} {v.shape}")
-    g = sage.quant_v(dev(v))
-    r = orc.quant(v, v, v, with_v=True)
+    say(f"quant_v {case} {v.shape} smooth_v={smooth_v}")
+    g = sage.quant_v(dev(v), smooth_v=bool(smooth_v))
+    r = orc.quant(v, v, v, with_v=True, smooth_v=smooth_v)
     assert np.array_equal(host(g["v_scale"]).view(np.uint32), r["v_scale"].view(np.uint32))
+    assert np.array_equal(host(g["v_mean"]).view(np.uint32), r["v_mean"].view(np.uint32))
     gv = host(g["v_f8"])
     if not np.array_equal(gv, r["v_f8"]):
         bad = np.nonzero(gv != r["v_f8"])
@@ -219,6 +233,12 @@ EDGE = [
     ("nosmooth", 1, dict(N=256, B=1, H=2), dict(causal=0, variant=0, smooth_k=0)),
     ("v0_smoothq", 2, dict(N=256, B=1, H=2), dict(causal=1, variant=0, smooth_q=1)),
     ("v1_no_smoothq", 5, dict(N=256, B=1, H=2), dict(causal=1, variant=1, smooth_q=0)),
+    # V smoothing (variant 1): N = 1 leaves V' = 0, so O is the mean, i.e. V itself
+    ("n1_v1_smoothv", 5, dict(N=1, B=1, H=1), dict(causal=1, variant=1, smooth_v=1)),
+    ("n200_v1_d64_smoothv", 1, dict(N=200, B=1, H=2), dict(causal=0, variant=1, smooth_v=1)),
+    ("n333_v1_causal_smoothv", 5, dict(N=333, B=1, H=2), dict(causal=1, variant=1, smooth_v=1)),
+    ("blk32_v1_smoothqv", 5, dict(N=400, B=1, H=2), dict(causal=0, variant=1, blk_q=32, blk_k=32, smooth_v=1)),
+    ("v1_smoothv_no_smoothq", 5, dict(N=256, B=1, H=2), dict(causal=1, variant=1, smooth_q=0, smooth_v=1)),
 ]
 
 
@@ -244,6 +264,58 @@ def test_attn_q_offset_stress_variant1(sage, orc):
     g = run_gpu(sage, c)
     o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
     check_o("q_offset_v1", g, o)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_attn_full_size_smooth_v_sampled_rows(sage, orc, cfg):
+    """Variant 1 with Q and V smoothing on each workload's full shape (sampled rows)."""
+    c = dict(inputs(cfg))
+    c.update(variant=1, smooth_q=1, smooth_v=1)
+    B, H, N, d = c["q"].shape
+    G = B * H
+    say(f"attn smooth_v cfg{cfg} full size {c['q'].shape} causal={c['causal']}")
+    g = run_gpu(sage, c).reshape(G, N, d)
+    rng = np.random.default_rng(100 + cfg)
+    heads, rows = [], []
+    for hd in (0, G // 3, G - 1):
+        for r in sample_rows(N, c["causal"], rng):
+            heads.append(hd)
+            rows.append(r)
+    o = orc.attn_rows(c["q"], c["k"], c["v"], heads, rows, **oracle_kw(c))
+    check_o(f"smooth_v cfg{cfg} sampled {len(rows)} rows", g[heads, rows], o)
+
+
+def test_attn_v_offset_stress_smooth_v(sage, orc):
+    """V = 0.25 z + a per-channel offset ~ N(0, 1): parity with and without V smoothing, and
+    the smoothed GPU output is the closer one to exact attention (the point of smoothing V;
+    the oracle gives mean errors of about 2.0e-3 and 0.54e-3 here)."""
+    c = dict(workloads.config(5))
+    c.update(workloads.make_inputs(5, N=2048, B=1, H=2, v_sigma=1.0, v_spread=0.25))
+    exact = orc.attn(c["q"], c["k"], c["v"], causal=1, exact=1)
+    err = {}
+    for sv in (0, 1):
+        c["smooth_v"] = sv
+        say(f"attn v1 v-offset stress N=2048 smooth_v={sv}")
+        g = run_gpu(sage, c)
+        o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
+        check_o(f"v_offset smooth_v={sv}", g, o)
+        err[sv] = float(np.abs(g.astype(np.float64) - exact).mean())
+    say(f"  mean |O - exact|: plain {err[0]:.3e}, smoothed {err[1]:.3e}")
+    assert err[1] < 0.5 * err[0]
+
+
+def test_prequant_smooth_v_matches_whole_call(sage):
+    c = workloads.make_inputs(5, N=1000, B=1, H=2, v_sigma=1.0)
+    say("prequant vs whole call, variant 1 with Q and V smoothing")
+    q, k, v = dev(c["q"]), dev(c["k"]), dev(c["v"])
+    N = c["q"].shape[2]
+    whole = sage.attn(q, k, v, causal=True, variant=1, smooth_v=True)
+    qk = sage.quant_qk(q, k, smooth_q=True)
+    vq = sage.quant_v(v, smooth_v=True)
+    pre = sage.attn_prequant(qk, None, N, causal=True, variant=1, vq=vq, smooth_v=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(whole.float()).all()
+    assert torch.equal(whole, pre)
 
 
 @pytest.mark.parametrize("variant", [0, 1])

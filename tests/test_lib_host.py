@@ -65,7 +65,11 @@ def test_workspace_size(lib):
     # with Q smoothing the quantisation pass writes int8 Q, its scales and block means
     assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) == (expect + up(G * Np * d) + up(G * 32 * 4)
                                                                   + up(G * 32 * d * 4))
-    assert sage.workspace_bytes(B, H, N, d, 1) > expect   # V in FP8 + q means
+    v1 = sage.workspace_bytes(B, H, N, d, 1)
+    assert v1 > expect   # V in FP8 + q means
+    # V smoothing adds the [G, d] fp32 means; it has no meaning for the fp16 P~V variant
+    assert sage.workspace_bytes(B, H, N, d, 1, smooth_v=True) == v1 + up(G * d * 4)
+    assert sage.workspace_bytes(B, H, N, d, 0, smooth_v=True) == 0
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
     assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
 
@@ -111,6 +115,20 @@ def test_params_rejected(lib):
     p = sage._params()
     p.smooth_k = 3
     assert attn(lib, params=p) == -1
+    p = sage._params(smooth_v=True)
+    p.smooth_v = 2
+    assert attn(lib, params=p, variant=1) == -1 and b"smooth_v" in lib.sage_last_error()
+    p = sage._params(smooth_v=True)
+    assert attn(lib, params=p, variant=0) == -2 and b"smooth_v" in lib.sage_last_error()
+
+
+def test_older_params_layout_is_accepted(lib):
+    # the five-int sage_params of library 0.1 (no smooth_v) still parses: the call gets
+    # past the parameters and fails on the NULL q instead
+    p = sage._params(smooth_v=True)
+    p.struct_size = 5 * ctypes.sizeof(ctypes.c_int)
+    assert attn(lib, params=p, q=None) == -1 and b"q is NULL" in lib.sage_last_error()
+    assert lib.sage_version() >= 200
 
 
 def test_other_entry_points_reject(lib):
@@ -123,10 +141,21 @@ def test_other_entry_points_reject(lib):
     assert rc == -3
     rc = lib.sage_quant_v(A, 1, 1, 64, 64, A, MIS, A, 1 << 20, None)
     assert rc == -1
-    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, A, 1, 1, 64, 64, 0, 0.125, 1, None, None)
+    # V smoothing needs somewhere to put the means, and 0 / 1 only
+    rc = lib.sage_quant_v_ex(A, 1, 1, 64, 64, 1, A, A, None, A, 1 << 20, None)
+    assert rc == -1 and b"v_mean" in lib.sage_last_error()
+    rc = lib.sage_quant_v_ex(A, 1, 1, 64, 64, 2, A, A, A, A, 1 << 20, None)
+    assert rc == -1 and b"smooth_v" in lib.sage_last_error()
+    rc = lib.sage_quant_v_ex(A, 1, 1, 64, 64, 1, A, A, A, A, 16, None)
+    assert rc == -3
+    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, 1, None, None)
     assert rc == -1 and b"q_mean" in lib.sage_last_error()       # variant 1 smooths Q by default
-    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, A, 1, 1, 64, 64, 0, 0.125, 0, None, None)
+    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, 0, None, None)
     assert rc == -1 and b"v is NULL" in lib.sage_last_error()
+    p = sage._params(smooth_q=True, smooth_v=True)
+    rc = lib.sage_attn_fwd_prequant(A, A, A, A, A, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, 1,
+                                    ctypes.byref(p), None)
+    assert rc == -1 and b"v_mean" in lib.sage_last_error()
     rc = lib.sage_debug_qk_int32(A, A, 1, 1, 64, 64, A, 0, A, None)
     assert rc == -1 and b"n_tiles" in lib.sage_last_error()
     # the fused-Q kernel quantises Q without smoothing only

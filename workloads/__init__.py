@@ -16,7 +16,8 @@ off ~ N(0, sigma) drawn once per (b, h, channel); config 3 additionally
 multiplies exactly ceil(0.01 * B * H * d) (b, h, channel) columns of K by 20.
 Values are drawn in fp64, rounded to fp32, then to fp16 (nearest even).
 Sub-streams of the seed: Q = 0, K = 1, V = 2, offsets = 3, outlier choice = 4,
-Q offsets (only for the Q-smoothing stress input) = 5.
+Q offsets (only for the Q-smoothing stress input) = 5, V offsets (only for the
+V-smoothing stress input) = 6.
 """
 from __future__ import annotations
 
@@ -105,12 +106,14 @@ def config(cfg) -> dict:
 
 
 def make_inputs(cfg, seed: int | None = None, N: int | None = None, B: int | None = None,
-                H: int | None = None, q_sigma: float = 0.0) -> dict:
+                H: int | None = None, q_sigma: float = 0.0, v_sigma: float = 0.0,
+                v_spread: float = 1.0) -> dict:
     """Draw Q, K, V (fp16, [B, H, N, d]) for a config.
 
     N, B, H override the config's shape (same recipe, other size).  q_sigma > 0
     adds a per-channel offset ~ N(0, q_sigma) to Q as well (stress input for Q
-    smoothing).
+    smoothing); v_sigma > 0 does the same for V (stress input for V smoothing), and
+    v_spread scales V's token noise: V = v_spread * z + off, off ~ N(0, v_sigma).
     """
     c = config(cfg)
     cid = cfg if isinstance(cfg, int) else 0
@@ -139,9 +142,14 @@ def make_inputs(cfg, seed: int | None = None, N: int | None = None, B: int | Non
     q_shift = None
     if q_sigma > 0:
         q_shift = normal(seed, 5, G * d).reshape(G, d) * q_sigma
+    v_shift = v_mult = None
+    if v_sigma > 0:
+        v_shift = normal(seed, 6, G * d).reshape(G, d) * (v_sigma / v_spread)
+    if v_spread != 1.0:
+        v_mult = np.full((G, d), v_spread)
     q = tensor_f16(seed, 0, G, Nv, d, shift=q_shift)
     k = tensor_f16(seed, 1, G, Nv, d, shift=off, scale=mult)
-    v = tensor_f16(seed, 2, G, Nv, d)
+    v = tensor_f16(seed, 2, G, Nv, d, shift=v_shift, scale=v_mult)
     shp = (Bv, Hv, Nv, d)
     c.update(seed=seed, q=q.reshape(shp), k=k.reshape(shp), v=v.reshape(shp))
     return c
