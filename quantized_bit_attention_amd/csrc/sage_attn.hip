@@ -234,11 +234,10 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
   }
   mt = pair_max(mt);
   // m is finite after the first tile: key 0 is visible to every row
-  if (VARIANT == 0) {
-    rescale = __builtin_amdgcn_ballot_w64(mt > m + kLazyLog2) != 0;
-  } else {
-    rescale = true;  // P~ * 448 must stay <= 448 for FP8
-  }
+  // variant 1: P~ * 448 must stay <= 448 for FP8, so the max moves as soon as a row's
+  // does (a wave whose rows all keep their max has alpha = 1 exactly and skips the
+  // rescale)
+  rescale = __builtin_amdgcn_ballot_w64(mt > m + (VARIANT == 0 ? kLazyLog2 : 0.0f)) != 0;
   // branch-free so the caller's fast path stays one basic block
   const float mnew = rescale ? fmaxf(m, mt) : m;
   alpha = rescale ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;  // exp2(-inf) = 0 on the first tile
@@ -282,45 +281,96 @@ __device__ __forceinline__ void tile_kscales(const float* ksc, int t, unsigned l
   for (int j = 0; j < 4; ++j) kq[j] = kc[min((unsigned)(t * kTileKV + 16 * j), last_key) >> kshift];
 }
 __device__ __forceinline__ float kscale_of(const float* kq, int st, int h) { return h ? kq[2 * st + 1] : kq[2 * st]; }
+// K scale of the 16 keys 16*w .. of tile t (w uniform: a scalar load).
+__device__ __forceinline__ float kscale_quarter(const float* ksc, int t, int w, unsigned last_key, int kshift) {
+  typedef const __attribute__((address_space(4))) float* const_ptr;
+  return ((const_ptr)ksc)[min((unsigned)(t * kTileKV + 16 * w), last_key) >> kshift];
+}
 
-// Q-smoothing term of every key of tile t for each Q block of the workgroup:
-// bias[sb][j] = sm_scale*log2(e) * dK_j * (qmean_sb . Khat_j), in fp32.
+// Q smoothing: the term sm_scale*log2(e) * dK_j * (qmean_sb . Khat_j) of every key j of a
+// tile, for each Q block sb of the workgroup (up to 4), runs on the matrix unit.  The
+// prologue splits each block mean into four int8 limbs (split_qmean), so qmean . Khat
+// is four exact int32 dot products; limb k of block sb is column 4*sb + k of a
+// 16-column int8 matrix in LDS.
+//
+// Limbs of one block mean (wave sb, D/64 channels per lane): with |qmean| < 2^e and
+// s0 = 2^(e-6), l0 = rint(qmean / s0), then each next limb is the rounded residual in
+// units 128 times smaller: l_k = rint(r_k / (s0 * 2^-7k)), r_(k+1) = r_k - l_k*s0*2^-7k.
+// Each residual is exact in fp32 and every limb lies in [-64, 64]:
+// qmean = s3 * (2^21*l0 + 2^14*l1 + 2^7*l2 + l3) up to s3/2 per channel, s3 = s0 * 2^-21
+// (2^-27 of the block's largest mean), below the fp32 rounding of the bias itself.
 template <int D>
-__device__ __forceinline__ void smooth_q_bias(const AttnArgs& a, const float* ksc, const int8_t* sK,
-                                              const float* sQm, float* sBias, int t) {
-  constexpr int CH = D / 32;  // 32-channel chunks per key, summed across adjacent lanes
-  const int nsub = kAttnRows / a.blk_q;
-  for (int item = threadIdx.x; item < nsub * kTileKV * CH; item += kAttnThreads) {
-    const int chunk = item % CH, key = (item / CH) % kTileKV, sb = item / (CH * kTileKV);
-    const float* qm = sQm + sb * D + chunk * 32;
-    float acc = 0.0f;
+__device__ __forceinline__ void split_qmean(const float* qmean, bool valid, int8_t* sQl, float* sScale, int sb) {
+  const int lane = threadIdx.x & 63;
+  float x[D / 64];
+  float am = 0.0f;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int8_t* kr = k_lds_chunk<D>(sK, key, 2 * chunk + half);
+  for (int j = 0; j < D / 64; ++j) {
+    x[j] = valid ? qmean[lane + 64 * j] : 0.0f;
+    am = fmaxf(am, fabsf(x[j]));
+  }
+  am = wave_max(am);
+  // am < 2^e; tiny means share the exponent of 2^-100 so that 1/s0 stays finite
+  const int e = max(__builtin_amdgcn_frexp_expf(am), -100);
 #pragma unroll
-      for (int c = 0; c < 16; ++c) acc = fmaf(qm[16 * half + c], (float)kr[c], acc);
-    }
-    for (int off = 1; off < CH; off <<= 1) acc += __shfl_xor(acc, off);
-    if (chunk == 0) {
-      const int kj = min(t * kTileKV + key, a.N - 1);
-      sBias[sb * kTileKV + key] = a.kscale * ksc[kj >> __builtin_ctz(a.blk_k)] * acc;
+  for (int j = 0; j < D / 64; ++j) {
+    float v = x[j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float lk = rintf(v * __builtin_amdgcn_ldexpf(1.0f, 6 - e + 7 * k));
+      v = v - lk * __builtin_amdgcn_ldexpf(1.0f, e - 6 - 7 * k);  // exact
+      sQl[(4 * sb + k) * D + lane + 64 * j] = (int8_t)(int)lk;
     }
   }
+  if (lane == 0) sScale[sb] = __builtin_amdgcn_ldexpf(1.0f, e - 27);  // s3
+}
+
+// The bias of keys 16*wave .. 16*wave + 15 of the K tile in sK for every Q block, one
+// 16x16x64 INT8 MFMA per 64 channels: A = those keys (row = lane%16), B = the limb
+// matrix (column = lane%16), same 16 channels per lane for both.  The result in lane l
+// is column n = l%16 (block n/4, limb n%4) for keys 4*(l/16) + 0..3; the lane holding
+// limb 0 takes limbs 1 and 2 from the next lanes of its quad and writes four biases.
+// wk = sm_scale * log2(e) * dK of those 16 keys (one K block: blk_k >= 16).
+template <int D>
+__device__ __forceinline__ void smooth_q_bias(const int8_t* sK, const int8_t* sQl, const float* sScale, float wk,
+                                              float* sBias) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk) {
+    const i32x4 ka = *reinterpret_cast<const i32x4*>(k_lds_chunk<D>(sK, 16 * wave + n, 4 * kk + grp));
+    const i32x4 qa = *reinterpret_cast<const i32x4*>(sQl + n * D + 64 * kk + 16 * grp);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qa, acc, 0, 0, 0);
+  }
+  const float w = wk * sScale[n >> 2];
+  float b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // |l_k . Khat| <= 64*127*D < 2^21, so 128*L0 + L1 and 128*L2 + L3 fit in int32
+    const int l1 = __builtin_amdgcn_update_dpp(0, acc[i], 0x55, 0xF, 0xF, false);  // lane 1 of the quad
+    const int l2 = __builtin_amdgcn_update_dpp(0, acc[i], 0xAA, 0xF, 0xF, false);  // lane 2
+    const int l3 = __builtin_amdgcn_update_dpp(0, acc[i], 0xFF, 0xF, 0xF, false);  // lane 3
+    b[i] = w * fmaf((float)(acc[i] * 128 + l1), 16384.0f, (float)(l2 * 128 + l3));
+  }
+  if ((n & 3) == 0)
+    *reinterpret_cast<float4*>(sBias + (n >> 2) * kTileKV + 16 * wave + 4 * grp) = make_float4(b[0], b[1], b[2], b[3]);
 }
 
 // Instruction order of the interior-tile block: after a few operand reads, each MFMA
 // is followed by the LDS reads for the next one and a share of the softmax's VALU
 // instructions, which execute while the MFMA occupies the matrix unit.  (Written as
 // loops without conditionals: a guarded sched_group_barrier is not honoured.)
-template <int D, int VARIANT>
+template <int D, int VARIANT, bool SMOOTHQ>
 __device__ __forceinline__ void interleave_schedule() {
   // every MFMA takes two LDS operand reads (K and Q, two V transposes, or two V^T
   // halves); they are issued LEAD MFMAs ahead of their use, so the LDS latency (about
   // 200 cycles) overlaps the MFMAs and VALU work in between
   constexpr int LEAD = 2;
   constexpr int MFMA = 2 * (D / 32) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
-  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13) : (D == 128 ? 12 : 20);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13) : (D == 128 ? 8 : 14);
+  // with Q smoothing the softmax first reads its 32 biases (8 reads of 16 bytes)
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD + (SMOOTHQ ? 8 : 0), 0);
 #pragma unroll
   for (int i = 0; i < MFMA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -346,9 +396,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sV0[L::V_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sV1[L::V_BYTES];
   __shared__ __attribute__((aligned(16))) int8_t sQ[kAttnRows * D];
-  __shared__ __attribute__((aligned(16))) float sQm[SMOOTHQ ? NSUB * D : 1];
-  __shared__ float sBias0[SMOOTHQ ? NSUB * kTileKV : 1];
-  __shared__ float sBias1[SMOOTHQ ? NSUB * kTileKV : 1];
+  __shared__ __attribute__((aligned(16))) int8_t sQl[SMOOTHQ ? 16 * D : 1];  // limbs of the Q block means
+  __shared__ float sQs[SMOOTHQ ? NSUB : 1];                                   // their scales
+  __shared__ __attribute__((aligned(16))) float sBias0[SMOOTHQ ? NSUB * kTileKV : 1];
+  __shared__ __attribute__((aligned(16))) float sBias1[SMOOTHQ ? NSUB * kTileKV : 1];
   __shared__ float sAmax[kAttnWaves];  // FUSEQ: |Q| max of each wave's rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -399,13 +450,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // Q scale of this wave's block (FUSEQ: set once the block's |Q| max is known)
   float dq = (!FUSEQ && wave_active) ? a.q_scale[(size_t)g * a.nqb + (qw >> qshift)] : 0.0f;
 
-  if (SMOOTHQ) {
-    // block means of the (up to 4) Q blocks this workgroup's rows belong to
-    for (int e = tid; e < NSUB * D; e += kAttnThreads) {
-      const int sb = e / D, c = e % D;
-      const int qb = (q0 + sb * a.blk_q) / a.blk_q;
-      sQm[e] = (sb * a.blk_q < kAttnRows && qb < a.nqb) ? a.q_mean[((size_t)g * a.nqb + qb) * D + c] : 0.0f;
-    }
+  if constexpr (SMOOTHQ) {
+    // wave sb splits the mean of the workgroup's Q block sb (up to 4 blocks; the others
+    // get zero limbs)
+    static_assert(NSUB == kAttnWaves, "one wave per Q block of the workgroup");
+    const int sb = wave, qb = (q0 >> qshift) + sb;
+    split_qmean<D>(a.q_mean + ((size_t)g * a.nqb + qb) * D, sb * a.blk_q < kAttnRows && qb < a.nqb, sQl, sQs, sb);
   }
 
   f32x16 o[NCT];
@@ -470,7 +520,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint4*>(sQw + ks * 1024 + 16 * lane) = make_uint4(pk4[0], pk4[1], pk4[2], pk4[3]);
     }
   }
-  if (SMOOTHQ) smooth_q_bias<D>(a, ksc, sK0, sQm, sBias0, 0);
   // scale factors c = dQ * dK * sm_scale * log2(e); the raw K scales of a tile are
   // loaded one iteration before they are needed.  S, c and packed P~ alternate
   // between two register sets by tile parity.
@@ -488,12 +537,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   tile_kscales(ksc, 0, last_key, kshift, kq);
   cA[0] = dqs * kscale_of(kq, 0, h);
   cA[1] = dqs * kscale_of(kq, 1, h);
+  if (SMOOTHQ) smooth_q_bias<D>(sK0, sQl, sQs, a.kscale * kscale_quarter(ksc, 0, wave_id(), last_key, kshift), sBias0);
   tile_kscales(ksc, 1, last_key, kshift, kq);
   __syncthreads();
   // V(1) is copied by iteration 0, after its barrier.  Nothing is in flight when the
   // loop starts, so the compiler sees no pending copy into a slot the loop reads.
 
-  float alpha_prev = 1.0f;  // variant 1: rescale factor of the tile whose P~V is pending
   const int G16 = lane >> 4, j16 = lane & 15;
   // transpose-read base of this lane in a V tile (variant 0)
   const int vbase_off = 128 * (4 * (G16 >> 1) * (D / 16) + (G16 & 1)) + 8 * j16;
@@ -520,9 +569,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
           }
         }
     } else {
-      // two-level accumulation: the tile's products go to a fresh fp32 accumulator, and
-      // O <- alpha(t-1) * O + inner (one fma per element; alpha(t-1) is the rescale
-      // factor the softmax of tile t-1 produced, applied here together with its tile)
+      // the FP8 MFMA accumulates in fp32, straight into O: the fp32 outer accumulator of
+      // two-level accumulation, already rescaled for this tile at the end of the last
+      // iteration
       i32x8 pb;
 #pragma unroll
       for (int w = 0; w < 8; ++w) pb[w] = (int)pkp[w];
@@ -531,13 +580,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
         const i32x4 v0 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + (4 * ct) * 512);
         const i32x4 v1 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + (4 * ct + 2) * 512);
         const i32x4 vv[2] = {v0, v1};
-        const f32x16 inner = mfma_f8(__builtin_bit_cast(i32x8, vv), pb, f32x16{});
-        // (through a temporary: the compiler then keeps O in its registers instead of
-        // producing it in the MFMA's and copying it back)
-        f32x16 r;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) r[e] = fmaf(o[ct][e], alpha_prev, inner[e]);
-        o[ct] = r;
+        o[ct] = mfma_f8(__builtin_bit_cast(i32x8, vv), pb, o[ct]);
       }
     }
   };
@@ -566,7 +609,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     cn[0] = dqs * kscale_of(kq, 0, h);                                   // tile t+1
     cn[1] = dqs * kscale_of(kq, 1, h);
     if (t + 2 < T) copy.k_tile(krs, t + 2, sKc);
-    if (SMOOTHQ && t + 1 < T) smooth_q_bias<D>(a, ksc, sKn, sQm, sBn, t + 1);
+    if (SMOOTHQ && t + 1 < T)
+      smooth_q_bias<D>(sKn, sQl, sQs, a.kscale * kscale_quarter(ksc, t + 1, wave_id(), last_key, kshift), sBn);
 
     float alpha = 1.0f;
     bool rescale = false;
@@ -585,7 +629,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
         pv_tile(sVp, pkp);
       }
       softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
-      interleave_schedule<D, VARIANT>();
+      interleave_schedule<D, VARIANT, SMOOTHQ>();
     } else {
       if (compute_next) qk_tile<D>(sKn, sQw, lane, sn);
       if (pv_prev) pv_tile(sVp, pkp);
@@ -596,13 +640,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
           softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
       }
     }
-    if constexpr (VARIANT == 0) {
-      if (rescale) {  // O already holds P~(t-1) V(t-1)
+    if (rescale) {  // O already holds P~(t-1) V(t-1)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
-      }
-    } else {
-      alpha_prev = alpha;  // applied with tile t's products in the next iteration
+      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
     }
 
     // K scales of tile t+2 for the next iteration: issued here, their latency overlaps
