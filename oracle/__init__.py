@@ -37,9 +37,9 @@ def load(path: str | None = None):
         path = _LIB
     lib = ctypes.CDLL(path)
     p, i, d, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
-    lib.oracle_attn_rows.argtypes = [p, p, p, i, i, i, i, i, d, i, i, i, i, i, i, i, i, p, p, i, p, i, p]
+    lib.oracle_attn_rows.argtypes = [p, p, p, i, i, i, i, i, d, i, i, i, i, i, i, i, i, i, p, p, i, p, i, p]
     lib.oracle_attn_rows.restype = i
-    lib.oracle_quant.argtypes = [p, p, p, i, i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
+    lib.oracle_quant.argtypes = [p, p, p, i, i, i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
     lib.oracle_quant.restype = i
     lib.oracle_qk_int32.argtypes = [p, p, i, i, i, i, i, i, p]
     lib.oracle_qk_int32.restype = i
@@ -87,14 +87,18 @@ class Oracle:
         return self.lib.oracle_pad_len(N)
 
     # ---- steps 1-3
-    def quant(self, q, k, v=None, blk_q=128, blk_k=64, smooth_k=1, smooth_q=0, with_v=False, smooth_v=0) -> dict:
+    def quant(self, q, k, v=None, blk_q=128, blk_k=64, smooth_k=1, smooth_q=0, with_v=False, smooth_v=0,
+              q_group=None) -> dict:
+        """q_group: rows per Q scale (divides blk_q; default blk_q)."""
         q = _f16(q)
         k = _f16(k)
         B, H, N, d = q.shape
         G, Np = B * H, self.pad_len(N)
-        nqb, nkb = -(-N // blk_q), -(-N // blk_k)
+        if q_group is None:
+            q_group = blk_q
+        nqb, nkb, nqg = -(-N // blk_q), -(-N // blk_k), -(-N // q_group)
         r = dict(q_i8=np.empty((B, H, Np, d), np.int8), k_i8=np.empty((B, H, Np, d), np.int8),
-                 q_scale=np.empty((B, H, nqb), np.float32), k_scale=np.empty((B, H, nkb), np.float32),
+                 q_scale=np.empty((B, H, nqg), np.float32), k_scale=np.empty((B, H, nkb), np.float32),
                  k_mean=np.empty((B, H, d), np.float32), q_mean=np.empty((B, H, nqb, d), np.float32))
         vp = 0
         if with_v:
@@ -104,7 +108,7 @@ class Oracle:
             r["v_mean"] = np.empty((B, H, d), np.float32)
             vp = v.ctypes.data
         rc = self.lib.oracle_quant(
-            q.ctypes.data, k.ctypes.data, vp, B, H, N, d, blk_q, blk_k, smooth_k, smooth_q, smooth_v,
+            q.ctypes.data, k.ctypes.data, vp, B, H, N, d, blk_q, blk_k, q_group, smooth_k, smooth_q, smooth_v,
             r["q_i8"].ctypes.data, r["k_i8"].ctypes.data, r["q_scale"].ctypes.data,
             r["k_scale"].ctypes.data, r["k_mean"].ctypes.data, r["q_mean"].ctypes.data,
             r["v_f8"].ctypes.data if with_v else None, r["v_scale"].ctypes.data if with_v else None,
@@ -125,21 +129,24 @@ class Oracle:
 
     # ---- steps 1-9 for chosen rows
     def attn_rows(self, q, k, v, heads, rows, causal=0, sm_scale=None, variant=0, blk_q=128,
-                  blk_k=64, bkv=64, smooth_k=1, smooth_q=None, smooth_v=0, exact=0, nthreads=0):
-        """O (fp64, before the fp16 rounding) for rows[i] of flat head heads[i]."""
+                  blk_k=64, bkv=64, smooth_k=1, smooth_q=None, smooth_v=0, exact=0, nthreads=0, q_group=None):
+        """O (fp64, before the fp16 rounding) for rows[i] of flat head heads[i].
+        q_group: rows per Q scale (divides blk_q; default blk_q)."""
         q, k, v = _f16(q), _f16(k), _f16(v)
         B, H, N, d = q.shape
         if sm_scale is None:
             sm_scale = 1.0 / np.sqrt(d)
         if smooth_q is None:
             smooth_q = 1 if variant == 1 else 0
+        if q_group is None:
+            q_group = blk_q
         heads = np.ascontiguousarray(heads, dtype=np.int32)
         rows = np.ascontiguousarray(rows, dtype=np.int32)
         out = np.empty((heads.size, d), np.float64)
         used = ctypes.c_int(0)
         rc = self.lib.oracle_attn_rows(
             q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d, causal, float(sm_scale), variant,
-            blk_q, blk_k, bkv, smooth_k, smooth_q, smooth_v, exact, heads.ctypes.data, rows.ctypes.data,
+            blk_q, blk_k, bkv, q_group, smooth_k, smooth_q, smooth_v, exact, heads.ctypes.data, rows.ctypes.data,
             heads.size, out.ctypes.data, nthreads, ctypes.byref(used))
         if rc:
             raise ValueError("oracle_attn_rows: bad arguments")

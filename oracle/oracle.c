@@ -13,13 +13,19 @@
  *            and Per-thread INT4 Quantization" (ICML 2025 abstract), and the
  *            arXiv 2411.10958 abstract of SageAttention2.
  *  [SA2-v]   the arXiv 2502.01776 abstract of SageAttention2 ("smooth Q and V").
+ *  [SA2-g]   the same abstracts on the granularity of the Q/K scales: "thread-level"
+ *            (ICML 2025, arXiv 2411.10958) and "warp-level" (arXiv 2502.01776); the
+ *            [SA-sum] "Key points" speak of per-token quantisation.
  *  [FA]      FlashAttention / FlashAttention-2 and "Online normalizer calculation
  *            for softmax", entries of the reference list on the [SA-sum] page.
  *
  * What it computes, per (batch b, head h), in the order of the method:
  *   1. k_mean[c] = mean over the N tokens of K[:, c]          ([SA-sum] I1)
  *   2. K' = K - k_mean (fp32); Q' = Q - q_mean(block) when Q smoothing is on ([SA2])
- *   3. per-block symmetric INT8 quantisation of Q', K' with one fp32 scale per block
+ *   3. symmetric INT8 quantisation of Q', K' with one fp32 scale per group of rows:
+ *      K per block of blk_k keys; Q per group of q_group rows, which may be finer
+ *      than the Q-smoothing block of blk_q rows ([SA2-g]; q_group divides blk_q,
+ *      q_group = 1 is per-token)
  *   4. S = Qhat Khat^T with exact integer accumulation
  *   5. s = sm_scale * dQ * dK * S  (+ sm_scale * dK * (q_mean . Khat_j) with Q smoothing)
  *   6. causal / sequence-end mask
@@ -154,15 +160,17 @@ static float quant_block_i8(const float* xs, size_t n, int8_t* out) {
   return a / 127.0f;
 }
 
-/* Quantise one head's [N][d] tensor in blocks of `blk` rows.
+/* Quantise one head's [N][d] tensor.
  *  mean_mode 0: no smoothing; 1: subtract the mean over all N tokens
- *  (k_mean[d] written); 2: subtract the mean of each block (blk_mean
- *  [nblk][d] written).  out is [Np][d] with rows >= N zero.  scale[nblk]. */
-static void quant_head(const uint16_t* x, int N, int Np, int d, int blk, int mean_mode,
+ *  (k_mean[d] written); 2: subtract the mean of each block of `blk` rows
+ *  (blk_mean[nblk][d] written).  The smoothed rows are then quantised with one
+ *  scale per group of `grp` rows (grp divides blk): scale[ceil(N / grp)].
+ *  out is [Np][d] with rows >= N zero. */
+static void quant_head(const uint16_t* x, int N, int Np, int d, int blk, int grp, int mean_mode,
                        int8_t* out, float* scale, float* k_mean, float* blk_mean) {
-  int nblk = (N + blk - 1) / blk;
+  int nblk = (N + blk - 1) / blk, ngrp = (N + grp - 1) / grp;
   float* mean = (float*)malloc(sizeof(float) * (size_t)d);
-  float* buf = (float*)malloc(sizeof(float) * (size_t)blk * d);
+  float* buf = (float*)malloc(sizeof(float) * (size_t)N * d); /* the smoothed tensor */
   if (mean_mode == 1) {
     for (int c = 0; c < d; ++c) mean[c] = exact_mean(x, d, 0, N, c);
     if (k_mean) memcpy(k_mean, mean, sizeof(float) * (size_t)d);
@@ -176,9 +184,12 @@ static void quant_head(const uint16_t* x, int N, int Np, int d, int blk, int mea
     for (int t = r0; t < r1; ++t)
       for (int c = 0; c < d; ++c) {
         float v = (float)oracle_f16_decode(x[(size_t)t * d + c]);
-        buf[(size_t)(t - r0) * d + c] = mean_mode ? v - mean[c] : v;
+        buf[(size_t)t * d + c] = mean_mode ? v - mean[c] : v;
       }
-    scale[b] = quant_block_i8(buf, (size_t)(r1 - r0) * d, out + (size_t)r0 * d);
+  }
+  for (int gi = 0; gi < ngrp; ++gi) {
+    int r0 = gi * grp, r1 = r0 + grp < N ? r0 + grp : N;
+    scale[gi] = quant_block_i8(buf + (size_t)r0 * d, (size_t)(r1 - r0) * d, out + (size_t)r0 * d);
   }
   memset(out + (size_t)N * d, 0, (size_t)(Np - N) * d);
   free(mean);
@@ -225,6 +236,7 @@ static void quant_v_head(const uint16_t* v, int N, int Np, int d, int smooth_v, 
 typedef struct {
   int B, H, N, d, causal, variant;
   int blk_q, blk_k, bkv;
+  int q_group;    /* rows per Q scale; divides blk_q */
   int smooth_k, smooth_q, smooth_v;
   int exact;      /* 1: no quantisation at all, fp64 everywhere (pins the online softmax) */
   double sm_scale;
@@ -234,7 +246,7 @@ int oracle_pad_len(int N) { return (N + 127) / 128 * 128; }
 
 typedef struct {
   int8_t *qi, *ki;   /* [Np][d] */
-  float *qs, *ks;    /* per block */
+  float *qs, *ks;    /* per Q group, per K block */
   float *kmean;      /* [d] */
   float *qmean;      /* [nqb][d] (only with smooth_q) */
   uint8_t* vt;       /* [d][Np] (variant 1) */
@@ -246,16 +258,17 @@ static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, c
                       prep_t* h) {
   int N = P->N, d = P->d, Np = oracle_pad_len(N);
   int nqb = (N + P->blk_q - 1) / P->blk_q, nkb = (N + P->blk_k - 1) / P->blk_k;
+  int nqg = (N + P->q_group - 1) / P->q_group;
   memset(h, 0, sizeof(*h));
   if (P->exact) return;
   h->qi = (int8_t*)malloc((size_t)Np * d);
   h->ki = (int8_t*)malloc((size_t)Np * d);
-  h->qs = (float*)malloc(sizeof(float) * (size_t)nqb);
+  h->qs = (float*)malloc(sizeof(float) * (size_t)nqg);
   h->ks = (float*)malloc(sizeof(float) * (size_t)nkb);
   h->kmean = (float*)calloc((size_t)d, sizeof(float));
   h->qmean = (float*)calloc((size_t)nqb * d, sizeof(float));
-  quant_head(k, N, Np, d, P->blk_k, P->smooth_k ? 1 : 0, h->ki, h->ks, h->kmean, NULL);
-  quant_head(q, N, Np, d, P->blk_q, P->smooth_q ? 2 : 0, h->qi, h->qs, NULL, h->qmean);
+  quant_head(k, N, Np, d, P->blk_k, P->blk_k, P->smooth_k ? 1 : 0, h->ki, h->ks, h->kmean, NULL);
+  quant_head(q, N, Np, d, P->blk_q, P->q_group, P->smooth_q ? 2 : 0, h->qi, h->qs, NULL, h->qmean);
   if (P->variant == 1) {
     h->vt = (uint8_t*)malloc((size_t)d * Np);
     h->vs = (float*)malloc(sizeof(float) * (size_t)d);
@@ -311,7 +324,7 @@ static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, cons
       } else {
         int32_t S = dot_i8(h->qi + (size_t)i * d, h->ki + (size_t)j * d, d);
         double dk = (double)h->ks[j / P->blk_k];
-        sj = P->sm_scale * (double)h->qs[qb] * dk * (double)S;
+        sj = P->sm_scale * (double)h->qs[i / P->q_group] * dk * (double)S;
         if (qm) {
           double ds = 0.0;
           for (int c = 0; c < d; ++c) ds += (double)qm[c] * (double)h->ki[(size_t)j * d + c];
@@ -441,6 +454,7 @@ static int pick_threads(int want) {
 static int check_params(const params_t* P) {
   if (P->B < 1 || P->H < 1 || P->N < 1 || P->d < 1) return -1;
   if (P->blk_q < 1 || P->blk_k < 1 || P->bkv < 1) return -1;
+  if (P->q_group < 1 || P->blk_q % P->q_group) return -1;
   if (P->causal != 0 && P->causal != 1) return -1;
   if (P->variant != 0 && P->variant != 1) return -1;
   if (P->smooth_v != 0 && P->smooth_v != 1) return -1;
@@ -458,9 +472,10 @@ static int check_params(const params_t* P) {
  */
 int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N,
                      int d, int causal, double sm_scale, int variant, int blk_q, int blk_k, int bkv,
-                     int smooth_k, int smooth_q, int smooth_v, int exact, const int* heads, const int* rows,
-                     int n_items, double* out, int nthreads, int* threads_used) {
-  params_t P = {B, H, N, d, causal, variant, blk_q, blk_k, bkv, smooth_k, smooth_q, smooth_v, exact, sm_scale};
+                     int q_group, int smooth_k, int smooth_q, int smooth_v, int exact, const int* heads,
+                     const int* rows, int n_items, double* out, int nthreads, int* threads_used) {
+  params_t P = {B, H, N, d, causal, variant, blk_q, blk_k, bkv, q_group, smooth_k, smooth_q, smooth_v, exact,
+                sm_scale};
   if (check_params(&P)) return -1;
   for (int i = 0; i < n_items; ++i)
     if (heads[i] < 0 || heads[i] >= B * H || rows[i] < 0 || rows[i] >= N) return -1;
@@ -495,14 +510,14 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
 
 /*
  * Quantised tensors of steps 1-3 (and the FP8 V of variant 1) for all heads.
- *  q_i8, k_i8: [G][Np][d];  q_scale [G][nqb], k_scale [G][nkb];  k_mean [G][d];
+ *  q_i8, k_i8: [G][Np][d];  q_scale [G][ceil(N/q_group)], k_scale [G][nkb];  k_mean [G][d];
  *  q_mean [G][nqb][d] (zeros unless smooth_q);  v_f8 [G][d][Np], v_scale [G][d],
  *  v_mean [G][d] (zeros unless smooth_v; may be NULL) (only when v_f8 != NULL).  Np = oracle_pad_len(N).  Heads run on a thread pool;
  *  each head is computed sequentially, so the result does not depend on threading.
  */
 typedef struct {
   const uint16_t *q, *k, *v;
-  int N, d, Np, blk_q, blk_k, smooth_k, smooth_q, smooth_v, nqb, nkb;
+  int N, d, Np, blk_q, blk_k, q_group, smooth_k, smooth_q, smooth_v, nqb, nkb, nqg;
   int8_t *q_i8, *k_i8;
   float *q_scale, *k_scale, *k_mean, *q_mean, *v_scale, *v_mean;
   uint8_t* v_f8;
@@ -521,10 +536,10 @@ static void* quant_worker(void* arg) {
     int d = J->d;
     if (J->k_mean) memset(J->k_mean + (size_t)g * d, 0, sizeof(float) * (size_t)d);
     if (J->q_mean) memset(J->q_mean + (size_t)g * J->nqb * d, 0, sizeof(float) * (size_t)J->nqb * d);
-    quant_head(J->k + g * hs, J->N, J->Np, d, J->blk_k, J->smooth_k ? 1 : 0, J->k_i8 + g * hp,
+    quant_head(J->k + g * hs, J->N, J->Np, d, J->blk_k, J->blk_k, J->smooth_k ? 1 : 0, J->k_i8 + g * hp,
                J->k_scale + (size_t)g * J->nkb, J->k_mean ? J->k_mean + (size_t)g * d : NULL, NULL);
-    quant_head(J->q + g * hs, J->N, J->Np, d, J->blk_q, J->smooth_q ? 2 : 0, J->q_i8 + g * hp,
-               J->q_scale + (size_t)g * J->nqb, NULL, J->q_mean ? J->q_mean + (size_t)g * J->nqb * d : NULL);
+    quant_head(J->q + g * hs, J->N, J->Np, d, J->blk_q, J->q_group, J->smooth_q ? 2 : 0, J->q_i8 + g * hp,
+               J->q_scale + (size_t)g * J->nqg, NULL, J->q_mean ? J->q_mean + (size_t)g * J->nqb * d : NULL);
     if (J->v_f8)
       quant_v_head(J->v + g * hs, J->N, J->Np, d, J->smooth_v, J->v_f8 + g * hp, J->v_scale + (size_t)g * d,
                    J->v_mean ? J->v_mean + (size_t)g * d : NULL);
@@ -533,13 +548,15 @@ static void* quant_worker(void* arg) {
 }
 
 int oracle_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N, int d,
-                 int blk_q, int blk_k, int smooth_k, int smooth_q, int smooth_v, int8_t* q_i8, int8_t* k_i8,
-                 float* q_scale, float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
+                 int blk_q, int blk_k, int q_group, int smooth_k, int smooth_q, int smooth_v, int8_t* q_i8,
+                 int8_t* k_i8, float* q_scale, float* k_scale, float* k_mean, float* q_mean, uint8_t* v_f8,
                  float* v_scale, float* v_mean) {
   if (B < 1 || H < 1 || N < 1 || d < 1 || blk_q < 1 || blk_k < 1) return -1;
+  if (q_group < 1 || blk_q % q_group) return -1;
   if (smooth_v != 0 && smooth_v != 1) return -1;
-  quantjob_t J = {q, k, v, N, d, oracle_pad_len(N), blk_q, blk_k, smooth_k, smooth_q, smooth_v,
-                  (N + blk_q - 1) / blk_q, (N + blk_k - 1) / blk_k, q_i8, k_i8, q_scale, k_scale,
+  quantjob_t J = {q, k, v, N, d, oracle_pad_len(N), blk_q, blk_k, q_group, smooth_k, smooth_q, smooth_v,
+                  (N + blk_q - 1) / blk_q, (N + blk_k - 1) / blk_k, (N + q_group - 1) / q_group, q_i8, k_i8,
+                  q_scale, k_scale,
                   k_mean, q_mean, v_scale, v_mean, v_f8, B * H, 0, PTHREAD_MUTEX_INITIALIZER};
   int nt = pick_threads(0);
   if (nt > J.G) nt = J.G;

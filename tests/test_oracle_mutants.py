@@ -35,8 +35,11 @@ MUTANTS = {
     "fp8 epilogue 448 dropped": ("o[c] * (double)h->vs[c] / (448.0 * l)", "o[c] * (double)h->vs[c] / l"),
     "e4m3 rounding floors": ("double q = nearbyint(ldexp(a, 3 - E));", "double q = floor(ldexp(a, 3 - E));"),
     "f16 encode exponent bias": ("((E + 15) << 10)", "((E + 14) << 10)"),
-    "dequant drops q scale": ("sj = P->sm_scale * (double)h->qs[qb] * dk * (double)S;",
+    "dequant drops q scale": ("sj = P->sm_scale * (double)h->qs[i / P->q_group] * dk * (double)S;",
                               "sj = P->sm_scale * dk * (double)S;"),
+    "q scale indexed by smoothing block": ("h->qs[i / P->q_group]", "h->qs[i / P->blk_q]"),
+    "q groups span the smoothing block": ("int r0 = gi * grp, r1 = r0 + grp < N ? r0 + grp : N;",
+                                          "int r0 = gi * grp, r1 = (r0 / blk + 1) * blk < N ? (r0 / blk + 1) * blk : N;"),
     "p~ fp8 scale dropped": ("oracle_e4m3_encode(p[j - j0] * 448.0)", "oracle_e4m3_encode(p[j - j0])"),
     "v mean not added back": ("/ (448.0 * l) + (double)h->vm[c];", "/ (448.0 * l);"),
     "v mean subtracted twice": ("      if (smooth_v) x = x - mean;\n      float y = x * r;",
@@ -52,8 +55,10 @@ def _battery(orc):
     yield "f16 encode", lambda: pins.test_f16_encode_matches_numpy_rne(orc)
     yield "e4m3 decode", lambda: pins.test_e4m3_decode_all_codes_match_torch(orc)
     yield "e4m3 encode", lambda: pins.test_e4m3_encode_rne_and_saturation(orc)
-    for a in [(7, 3, 4, 3), (10, 5, 10, 4), (5, 8, 2, 5)]:
+    for a in [(7, 3, 4, 3, 4), (10, 5, 10, 4, 10), (5, 8, 2, 5, 2), (10, 5, 10, 4, 5), (7, 3, 4, 3, 1)]:
         yield f"fraction quant {a}", lambda a=a: pins.test_quant_matches_fraction_bruteforce(orc, *a)
+    yield "per-token scale", lambda: pins.test_per_token_q_scale_is_the_row_absmax(orc)
+    yield "per-token mixed rows", lambda: pins.test_per_token_q_helps_rows_of_mixed_magnitude(orc)
     yield "roundtrip", lambda: pins.test_quant_roundtrip_bound_and_absmax(orc)
     yield "smoothing shift", lambda: pins.test_smoothing_subtracts_exact_token_mean(orc)
     yield "qk int32", lambda: pins.test_qk_int32_matches_numpy_int64(orc)

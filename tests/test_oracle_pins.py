@@ -113,11 +113,12 @@ def _frac_quant_block(vals):
     return codes, rn32(a / 127)
 
 
-@pytest.mark.parametrize("N,d,blk_q,blk_k", [(7, 3, 4, 3), (10, 5, 10, 4), (5, 8, 2, 5)])
-def test_quant_matches_fraction_bruteforce(orc, N, d, blk_q, blk_k):
+@pytest.mark.parametrize("N,d,blk_q,blk_k,q_group", [(7, 3, 4, 3, 4), (10, 5, 10, 4, 10), (5, 8, 2, 5, 2),
+                                                     (10, 5, 10, 4, 5), (7, 3, 4, 3, 1), (9, 4, 4, 2, 2)])
+def test_quant_matches_fraction_bruteforce(orc, N, d, blk_q, blk_k, q_group):
     q = _tiny(N, d, 10 + N)
     k = _tiny(N, d, 20 + N, shift=7.0)
-    r = orc.quant(q, k, blk_q=blk_q, blk_k=blk_k, smooth_k=1, smooth_q=1)
+    r = orc.quant(q, k, blk_q=blk_q, blk_k=blk_k, smooth_k=1, smooth_q=1, q_group=q_group)
     qh, kh = q[0, 0], k[0, 0]
     # K: exact token mean, rounded once to double, then to float
     kmean = [np.float32(float(_frac_mean(kh[:, c]))) for c in range(d)]
@@ -129,17 +130,61 @@ def test_quant_matches_fraction_bruteforce(orc, N, d, blk_q, blk_k):
         got = r["k_i8"][0, 0, b * blk_k:min(N, (b + 1) * blk_k)].ravel()
         assert list(got) == codes
         assert r["k_scale"][0, 0, b] == delta
-    # Q: mean per block (Q smoothing, [SA2])
+    # Q: mean per block of blk_q rows (Q smoothing, [SA2]), then one scale per group of
+    # q_group rows inside the block ([SA2] thread / warp-level granularity)
     for b in range(-(-N // blk_q)):
         rows = qh[b * blk_q:(b + 1) * blk_q]
         qm = [np.float32(float(_frac_mean(rows[:, c]))) for c in range(d)]
         assert np.array_equal(r["q_mean"][0, 0, b], np.array(qm, np.float32))
         sm = np.array([[np.float32(np.float32(x) - qm[c]) for c, x in enumerate(row)] for row in rows])
-        codes, delta = _frac_quant_block(sm.ravel())
-        assert list(r["q_i8"][0, 0, b * blk_q:b * blk_q + len(rows)].ravel()) == codes
-        assert r["q_scale"][0, 0, b] == delta
+        for g0 in range(0, len(rows), q_group):
+            codes, delta = _frac_quant_block(sm[g0:g0 + q_group].ravel())
+            t0 = b * blk_q + g0
+            assert list(r["q_i8"][0, 0, t0:t0 + len(sm[g0:g0 + q_group])].ravel()) == codes
+            assert r["q_scale"][0, 0, t0 // q_group] == delta
+    assert r["q_scale"].shape[2] == -(-N // q_group)
     # pad rows are zero
     assert not r["q_i8"][0, 0, N:].any() and not r["k_i8"][0, 0, N:].any()
+
+
+def test_per_token_q_scale_is_the_row_absmax(orc):
+    """q_group = 1 without smoothing: each row's scale is fl32(max|row| / 127), the row's
+    largest entry gets code +-127, and a zero row gets scale 0 and codes 0."""
+    q = _tiny(40, 16, 5, scale=2.0)
+    q[0, 0, ::7] *= np.float16(50)
+    q[0, 0, 3] = 0
+    r = orc.quant(q, q, blk_q=8, blk_k=8, smooth_k=0, smooth_q=0, q_group=1)
+    for t in range(40):
+        row = q[0, 0, t].astype(np.float32)
+        a = np.abs(row).max()
+        assert r["q_scale"][0, 0, t] == np.float32(a / np.float32(127))
+        codes = r["q_i8"][0, 0, t]
+        if a == 0:
+            assert not codes.any()
+        else:
+            assert np.abs(codes.astype(int)).max() == 127
+            assert codes[np.abs(row).argmax()] == (127 if row[np.abs(row).argmax()] > 0 else -127)
+
+
+def test_per_token_q_helps_rows_of_mixed_magnitude(orc):
+    """One Q row in eight is 64x larger: with one scale per 64-row block the ordinary
+    rows keep only a few code levels, with per-token scales they keep their own.  The
+    per-token oracle must sit much closer to exact attention on the ordinary rows."""
+    rng = np.random.default_rng(9)
+    N, d = 256, 64
+    q = rng.standard_normal((1, 1, N, d))
+    q[0, 0, ::8] *= 64.0
+    q = q.astype(np.float16)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float16)
+    exact = orc.attn(q, k, v, exact=1)
+    ordinary = np.ones(N, bool)
+    ordinary[::8] = False
+    err = {}
+    for g in (64, 1):
+        o = orc.attn(q, k, v, blk_q=64, blk_k=16, q_group=g)
+        err[g] = float(np.abs(o - exact)[0, 0, ordinary].mean())
+    assert err[1] < err[64] / 4, err
 
 
 def test_kmean_independent_of_token_order(orc):
