@@ -12,7 +12,8 @@ duration from HIP events on the launch stream), and the CPU oracle timed on a
 bounded sample of the same workload.
 
 --config picks another workload; --variant 1 runs the FP8 P~V variant on it
-(with Q smoothing) and --smooth-v adds V smoothing to that variant.
+(with Q smoothing) and --smooth-v adds V smoothing to that variant; --q-group 1
+uses per-token Q scales.
 """
 import argparse
 import hashlib
@@ -68,6 +69,8 @@ def main():
                     help="0: INT8 QK + FP16 P~V, 1: INT8 QK + Q smoothing + FP8 P~V (default: the workload's)")
     ap.add_argument("--smooth-v", action="store_true",
                     help="variant 1 only: subtract V's token mean before FP8 and add it back")
+    ap.add_argument("--q-group", type=int, default=0,
+                    help="rows per Q scale (0: one per Q block; 1: per token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads of the workload the oracle runs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,14 +97,16 @@ def main():
     if smooth_v and variant != 1:
         print("bench.py: --smooth-v needs the FP8 P~V variant (--variant 1, or --config 5)", file=sys.stderr)
         sys.exit(2)
-    opts = dict(causal=bool(causal), variant=variant, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_v=smooth_v)
+    q_group = args.q_group
+    opts = dict(causal=bool(causal), variant=variant, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_v=smooth_v,
+                q_group=q_group)
     ops = workloads.attention_ops(B, H, N, d, causal)
 
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v"))
     out = torch.empty_like(q)
     ws = torch.empty(sage.workspace_bytes(B, H, N, d, variant, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"],
-                                          smooth_v=smooth_v),
+                                          smooth_v=smooth_v, q_group=q_group),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -119,11 +124,12 @@ def main():
     # the attention kernel alone, as the step launches it (same stream, same launch
     # configuration): variant 0 quantises Q inside the kernel, variant 1 reads the
     # pre-quantised Q and FP8 V
-    qk = sage.quant_qk(q, k, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=variant == 1)
+    qk = sage.quant_qk(q, k, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=variant == 1, q_group=q_group)
     vq = sage.quant_v(v, smooth_v=smooth_v) if variant == 1 else None
     if variant == 0:
         def kernel():
-            sage.attn_qf16(q, qk, v, out=out, causal=bool(causal), blk_q=cfg["blk_q"], blk_k=cfg["blk_k"])
+            sage.attn_qf16(q, qk, v, out=out, causal=bool(causal), blk_q=cfg["blk_q"], blk_k=cfg["blk_k"],
+                           q_group=q_group)
     else:
         def kernel():
             sage.attn_prequant(qk, v, N, vq=vq, out=out, **opts)
@@ -149,7 +155,7 @@ def main():
     value = ops / (ms * 1e-3) / 1e12
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     # the counter summary covers the default workload's kernel only
-    traffic = read_traffic(args.config) if variant == 0 else None
+    traffic = read_traffic(args.config) if variant == 0 and q_group == 0 else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -165,7 +171,7 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller; K with per-channel offsets)",
         "config": {"workload": f"{cfg['name']} B={B} H={H} N={N} d={d}", "B": B, "H": H, "N": N, "d": d,
                    "causal": causal, "variant": variant, "blk_q": cfg["blk_q"], "blk_k": cfg["blk_k"],
-                   "smooth_v": int(smooth_v), "kv_tile": sage.kv_tile(variant, d)},
+                   "smooth_v": int(smooth_v), "q_group": q_group or cfg["blk_q"], "kv_tile": sage.kv_tile(variant, d)},
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_tops": round(attn_tops, 2),
@@ -183,7 +189,8 @@ def main():
         rows = np.tile(np.arange(N, dtype=np.int32), nh)
         t0 = time.perf_counter()
         orc.attn_rows(x["q"], x["k"], x["v"], heads, rows, causal=causal, variant=variant,
-                      blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], bkv=sage.kv_tile(variant, d), smooth_v=int(smooth_v))
+                      blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], bkv=sage.kv_tile(variant, d), smooth_v=int(smooth_v),
+                      q_group=q_group or None)
         dt = time.perf_counter() - t0
         sample_ops = workloads.attention_ops(1, nh, N, d, causal)
         result["cpu_baseline"] = {"value": round(sample_ops / dt / 1e12, 6), "unit": "TOPS",

@@ -20,8 +20,8 @@
  *  - d must be 64 or 128 (SAGE_ERR_UNSUPPORTED otherwise); N >= 1;
  *    B*H*pad_len(N)*d < 2^31.
  *  - Quantised Q/K tensors are [B, H, Np, d] int8 with Np = sage_pad_len(N);
- *    rows >= N are zero.  Q scales are [B, H, ceil(N / blk_q)] fp32, K scales
- *    [B, H, ceil(N / blk_k)] fp32.
+ *    rows >= N are zero.  Q scales are [B, H, ceil(N / q_group)] fp32 (q_group =
+ *    blk_q unless sage_params sets it), K scales [B, H, ceil(N / blk_k)] fp32.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work and returns without waiting.
  *  - Arguments are checked before anything is launched; a bad argument returns a
@@ -60,9 +60,16 @@ typedef struct {
   int smooth_k; /* subtract the token mean of K (default 1) */
   int smooth_q; /* subtract the block mean of Q and add its term back (default: variant == 1) */
   int smooth_v; /* variant 1 only: subtract the token mean of V before FP8, add it to O
-                   (SageAttention2 abstract, "smooth Q and V"; default 0).  The older
-                   five-int layout (struct_size 20) is still accepted and means 0. */
+                   (SageAttention2 abstract, "smooth Q and V"; default 0) */
+  int q_group;  /* rows per Q scale: 0 (= blk_q, default) or a power of two <= blk_q.
+                   The SageAttention2 abstracts quantise Q and K at thread- / warp-level
+                   granularity; here each lane of the attention kernel owns one query,
+                   so per-token Q scales (q_group = 1) cost nothing in the kernel.  Q
+                   smoothing keeps its mean per block of blk_q rows.  K's finest scale
+                   block, blk_k = 16, is the 16 keys a lane holds. */
 } sage_params;
+/* The older layouts (struct_size 20: no smooth_v, no q_group; 24: no q_group) are
+ * still accepted; the missing fields take their defaults. */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int sage_version(void);
@@ -87,8 +94,9 @@ size_t sage_workspace_bytes(int B, int H, int N, int d, int variant, const sage_
  *   K' = K - k_mean (fp32); per block of blk_k tokens: scale = max|K'| / 127,
  *     code = rint(K' * (127 / max|K'|)) in [-127, 127] (ties to even); a block of
  *     zeros gets scale 0 and codes 0;
- *   Q: the same per block of blk_q tokens; with smooth_q, the block's exact mean is
- *     subtracted first and written to q_mean[B,H,ceil(N/blk_q),d].
+ *   Q: the same per group of q_group tokens (q_group divides blk_q); with smooth_q,
+ *     the exact mean of each block of blk_q tokens is subtracted first and written
+ *     to q_mean[B,H,ceil(N/blk_q),d].
  * q_mean may be NULL unless smooth_q is on; k_mean may be NULL.
  */
 int sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const sage_params* p,

@@ -34,7 +34,8 @@ class SageError(RuntimeError):
 
 class _Params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_int), ("blk_q", ctypes.c_int), ("blk_k", ctypes.c_int),
-                ("smooth_k", ctypes.c_int), ("smooth_q", ctypes.c_int), ("smooth_v", ctypes.c_int)]
+                ("smooth_k", ctypes.c_int), ("smooth_q", ctypes.c_int), ("smooth_v", ctypes.c_int),
+                ("q_group", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -80,9 +81,9 @@ def _check(rc: int, what: str):
         raise SageError(f"{what} failed ({rc}): {msg}")
 
 
-def _params(blk_q=128, blk_k=64, smooth_k=True, smooth_q=False, smooth_v=False) -> _Params:
+def _params(blk_q=128, blk_k=64, smooth_k=True, smooth_q=False, smooth_v=False, q_group=0) -> _Params:
     return _Params(ctypes.sizeof(_Params), int(blk_q), int(blk_k), int(bool(smooth_k)), int(bool(smooth_q)),
-                   int(bool(smooth_v)))
+                   int(bool(smooth_v)), int(q_group))
 
 
 def _ptr(t):
@@ -116,10 +117,10 @@ def kv_tile(variant: int, d: int) -> int:
 
 
 def workspace_bytes(B, H, N, d, variant=0, blk_q=128, blk_k=64, smooth_k=True, smooth_q=None,
-                    smooth_v=False) -> int:
+                    smooth_v=False, q_group=0) -> int:
     if smooth_q is None:
         smooth_q = variant == VARIANT_FP8PV
-    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v)
+    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v, q_group)
     return _load().sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))
 
 
@@ -132,10 +133,11 @@ def _workspace(nbytes, device, workspace):
 
 
 def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128, blk_k=64,
-         smooth_k=True, smooth_q=None, smooth_v=False, out=None, workspace=None):
+         smooth_k=True, smooth_q=None, smooth_v=False, q_group=0, out=None, workspace=None):
     """o = SageAttention(q, k, v) for [B, H, N, d] fp16 tensors on the GPU.
 
-    smooth_v (variant 1 only) subtracts V's token mean before FP8 and adds it to O."""
+    smooth_v (variant 1 only) subtracts V's token mean before FP8 and adds it to O.
+    q_group: rows per Q scale (0 = blk_q; 1 = per token)."""
     B, H, N, d = _check_qkv(q, k, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -143,7 +145,7 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
         smooth_q = variant == VARIANT_FP8PV
     if out is None:
         out = torch.empty_like(q)
-    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v)
+    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v, q_group)
     lib = _load()
     nbytes = lib.sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))
     if nbytes == 0:
@@ -156,19 +158,19 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
     return out
 
 
-def quant_qk(q, k, blk_q=128, blk_k=64, smooth_k=True, smooth_q=False) -> dict:
+def quant_qk(q, k, blk_q=128, blk_k=64, smooth_k=True, smooth_q=False, q_group=0) -> dict:
     """Smoothing + per-block INT8 of Q and K.  Returns the int8 tensors, scales and means."""
     B, H, N, d = _check_qkv(q, k)
     dev = q.device
     Np = pad_len(N)
-    nqb, nkb = -(-N // blk_q), -(-N // blk_k)
+    nqb, nkb, nqg = -(-N // blk_q), -(-N // blk_k), -(-N // (q_group or blk_q))
     r = dict(q_i8=torch.empty((B, H, Np, d), dtype=torch.int8, device=dev),
              k_i8=torch.empty((B, H, Np, d), dtype=torch.int8, device=dev),
-             q_scale=torch.empty((B, H, nqb), dtype=torch.float32, device=dev),
+             q_scale=torch.empty((B, H, nqg), dtype=torch.float32, device=dev),
              k_scale=torch.empty((B, H, nkb), dtype=torch.float32, device=dev),
              k_mean=torch.zeros((B, H, d), dtype=torch.float32, device=dev),
              q_mean=torch.zeros((B, H, nqb, d), dtype=torch.float32, device=dev))
-    p = _params(blk_q, blk_k, smooth_k, smooth_q)
+    p = _params(blk_q, blk_k, smooth_k, smooth_q, False, q_group)
     lib = _load()
     ws = _workspace(lib.sage_workspace_bytes(B, H, N, d, 0, ctypes.byref(p)), dev, None)
     rc = lib.sage_quant_qk(_ptr(q), _ptr(k), B, H, N, d, ctypes.byref(p), _ptr(r["q_i8"]), _ptr(r["k_i8"]),
@@ -196,7 +198,7 @@ def quant_v(v, smooth_v=False) -> dict:
 
 
 def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_FP16PV, vq: dict | None = None,
-                  blk_q=128, blk_k=64, smooth_q=None, smooth_v=False, out=None):
+                  blk_q=128, blk_k=64, smooth_q=None, smooth_v=False, q_group=0, out=None):
     """The attention kernel alone, on quant_qk() / quant_v() outputs (quant_v(smooth_v=True) with
     smooth_v)."""
     B, H, Np, d = qk["q_i8"].shape
@@ -207,7 +209,7 @@ def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_F
     dev = qk["q_i8"].device
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
-    p = _params(blk_q, blk_k, True, smooth_q, smooth_v)
+    p = _params(blk_q, blk_k, True, smooth_q, smooth_v, q_group)
     rc = _load().sage_attn_fwd_prequant(
         _ptr(qk["q_i8"]), _ptr(qk["k_i8"]), _ptr(qk["q_scale"]), _ptr(qk["k_scale"]),
         _ptr(qk["q_mean"]) if smooth_q else None, _ptr(v) if variant == 0 else None,
@@ -217,14 +219,14 @@ def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_F
     return out
 
 
-def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, out=None):
+def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, q_group=0, out=None):
     """Variant 0 attention on fp16 q (quantised inside the kernel) and the K of quant_qk()."""
     B, H, N, d = _check_qkv(q, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    p = _params(blk_q, blk_k, True, False)
+    p = _params(blk_q, blk_k, True, False, False, q_group)
     rc = _load().sage_attn_fwd_qf16(_ptr(q), _ptr(qk["k_i8"]), _ptr(qk["k_scale"]), _ptr(v), _ptr(out), B, H, N, d,
                                     int(bool(causal)), float(sm_scale), ctypes.byref(p), _stream(q.device))
     _check(rc, "sage_attn_fwd_qf16")

@@ -40,22 +40,27 @@ bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
 struct Params {
   int blk_q = 128, blk_k = 64, smooth_k = 1, smooth_q = 0, smooth_v = 0;
+  int q_group = 0;  // rows per Q scale; resolved to blk_q when 0
 };
 
-// sage_params before smooth_v was added (library 0.1): five ints.
-constexpr int kParamsV1Size = 5 * (int)sizeof(int);
+// Earlier layouts of sage_params: five ints (library 0.1), six ints (0.2, + smooth_v).
+constexpr int kParamsV1Size = 5 * (int)sizeof(int), kParamsV2Size = 6 * (int)sizeof(int);
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int read_params(const sage_params* p, int variant, Params* out) {
   Params r;
   r.smooth_q = variant == SAGE_VARIANT_INT8QK_FP8PV ? 1 : 0;
   if (p) {
-    if (p->struct_size != (int)sizeof(sage_params) && p->struct_size != kParamsV1Size)
+    if (p->struct_size != (int)sizeof(sage_params) && p->struct_size != kParamsV1Size &&
+        p->struct_size != kParamsV2Size)
       return fail(SAGE_ERR_INVALID_ARG, "sage_params.struct_size must be %d", (int)sizeof(sage_params));
     r.blk_q = p->blk_q;
     r.blk_k = p->blk_k;
     r.smooth_k = p->smooth_k;
     r.smooth_q = p->smooth_q;
-    if (p->struct_size >= (int)sizeof(sage_params)) r.smooth_v = p->smooth_v;
+    if (p->struct_size >= kParamsV2Size) r.smooth_v = p->smooth_v;
+    if (p->struct_size >= (int)sizeof(sage_params)) r.q_group = p->q_group;
   }
   if (r.blk_q != 32 && r.blk_q != 64 && r.blk_q != 128)
     return fail(SAGE_ERR_UNSUPPORTED, "blk_q must be 32, 64 or 128 (got %d)", r.blk_q);
@@ -66,6 +71,9 @@ int read_params(const sage_params* p, int variant, Params* out) {
     return fail(SAGE_ERR_INVALID_ARG, "smooth_k / smooth_q / smooth_v must be 0 or 1");
   if (r.smooth_v && variant != SAGE_VARIANT_INT8QK_FP8PV)
     return fail(SAGE_ERR_UNSUPPORTED, "smooth_v applies to the FP8 P~V variant only");
+  if (r.q_group == 0) r.q_group = r.blk_q;
+  if (!pow2(r.q_group) || r.q_group > r.blk_q)
+    return fail(SAGE_ERR_UNSUPPORTED, "q_group must be 0 or a power of two <= blk_q (got %d)", r.q_group);
   *out = r;
   return SAGE_OK;
 }
@@ -96,7 +104,7 @@ size_t up(size_t x) { return (x + 255) / 256 * 256; }
 
 Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   const size_t G = (size_t)B * H, Np = pad_len(N), ns = ceil_div(N, sage::kStatRows);
-  const size_t nqb = ceil_div(N, p.blk_q), nkb = ceil_div(N, p.blk_k);
+  const size_t nqb = ceil_div(N, p.blk_q), nkb = ceil_div(N, p.blk_k), nqg = ceil_div(N, p.q_group);
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
@@ -107,7 +115,7 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   const bool fq = fuse_q(variant, p);
   L.q_i8 = take(fq ? 0 : G * Np * d);
   L.k_i8 = take(G * Np * d);
-  L.q_scale = take(fq ? 0 : G * nqb * sizeof(float));
+  L.q_scale = take(fq ? 0 : G * nqg * sizeof(float));
   L.k_scale = take(G * nkb * sizeof(float));
   L.k_mean = take(G * d * sizeof(float));
   L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
@@ -155,6 +163,8 @@ sage::QuantArgs quant_args(const void* q, const void* k, int B, int H, int N, in
   a.nsplit = ceil_div(N, sage::kStatRows);
   a.smooth_k = p.smooth_k;
   a.smooth_q = p.smooth_q;
+  a.q_group = p.q_group;
+  a.nqg = ceil_div(N, p.q_group);
   a.with_q = 1;
   return a;
 }
@@ -168,6 +178,8 @@ sage::AttnArgs attn_args(int B, int H, int N, const Params& p, float sm_scale) {
   a.blk_k = p.blk_k;
   a.nqb = ceil_div(N, p.blk_q);
   a.nkb = ceil_div(N, p.blk_k);
+  a.q_group = p.q_group;
+  a.nqg = ceil_div(N, p.q_group);
   a.kscale = sm_scale * 1.4426950408889634f;
   return a;
 }
@@ -244,7 +256,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
 
 extern "C" {
 
-int sage_version(void) { return 200; }
+int sage_version(void) { return 300; }
 
 int sage_pad_len(int N) { return N < 1 ? -1 : pad_len(N); }
 

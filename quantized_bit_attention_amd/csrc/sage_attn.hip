@@ -380,8 +380,8 @@ __device__ __forceinline__ void interleave_schedule() {
 }
 
 // FUSEQ (variant 0 without Q smoothing): Q arrives as fp16 and each workgroup quantises
-// its own rows into the LDS operand tile, with the per-block scale of the quantisation
-// pass (the workgroup's 128 rows are whole Q blocks of 32, 64 or 128 rows).
+// its own rows into the LDS operand tile, with the per-group scale of the quantisation
+// pass (the workgroup's 128 rows are whole groups of q_group = 1 .. 128 rows).
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   static_assert(!FUSEQ || (VARIANT == 0 && !SMOOTHQ), "in-kernel Q quantisation: variant 0, no Q smoothing");
@@ -445,10 +445,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
     if (wave_active) load_q_tile<D>(make_rsrc(qh, (size_t)a.Np * D), qw, sQw);
   }
-  // block sizes are powers of two
+  // block and group sizes are powers of two
   const int kshift = __builtin_ctz(a.blk_k), qshift = __builtin_ctz(a.blk_q);
-  // Q scale of this wave's block (FUSEQ: set once the block's |Q| max is known)
-  float dq = (!FUSEQ && wave_active) ? a.q_scale[(size_t)g * a.nqb + (qw >> qshift)] : 0.0f;
+  // Q scale of this lane's row: one per group of q_group rows, so uniform over the wave
+  // for groups of 32 rows or more (FUSEQ: set once the group's |Q| max is known)
+  float dq = (!FUSEQ && wave_active) ? a.q_scale[(size_t)g * a.nqg + (min(qi, N - 1) >> __builtin_ctz(a.q_group))]
+                                     : 0.0f;
 
   if constexpr (SMOOTHQ) {
     // wave sb splits the mean of the workgroup's Q block sb (up to 4 blocks; the others
@@ -494,16 +496,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       for (int j = 0; j < 4; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
     }
     const u16x2 mb = {__builtin_elementwise_max(mx[0], mx[1]), 0};
-    const float am = wave_max((float)__builtin_bit_cast(f16x2, mb)[0]);
+    const float lm = (float)__builtin_bit_cast(f16x2, mb)[0];  // this lane's half of row qi
+    const float am = wave_max(lm);
     if (lane == 0) sAmax[wave] = am;
+    if (a.q_group < 32) {
+      // groups inside the wave: the row's max over the lane pair, then over the group's
+      // q_group consecutive rows (lanes)
+      float gm = pair_max(lm);
+      for (int off = 1; off < a.q_group; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      dq = gm;  // the group's |Q| max until the scale is formed below
+    }
   }
   wait_copies();
   __syncthreads();
   if constexpr (FUSEQ) {
-    // the Q block of this wave spans waves w0 .. w0 + blk_q/32 - 1
-    const int wpb = a.blk_q >> 5, w0 = wave & ~(wpb - 1);
-    float amax = sAmax[w0];
-    for (int w = 1; w < wpb; ++w) amax = fmaxf(amax, sAmax[w0 + w]);
+    // a group of 32 rows or more spans waves w0 .. w0 + q_group/32 - 1
+    float amax = dq;
+    if (a.q_group >= 32) {
+      const int wpb = a.q_group >> 5, w0 = wave & ~(wpb - 1);
+      amax = sAmax[w0];
+      for (int w = 1; w < wpb; ++w) amax = fmaxf(amax, sAmax[w0 + w]);
+    }
     dq = i8_scale(amax);
     const float r = i8_factor(amax);
 #pragma unroll

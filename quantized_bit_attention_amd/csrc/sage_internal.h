@@ -11,12 +11,13 @@ struct QuantArgs {
   const uint16_t* k;
   int8_t* q_i8;       // [G][Np][D]
   int8_t* k_i8;
-  float* q_scale;     // [G][nqb]
+  float* q_scale;     // [G][nqg]
   float* k_scale;     // [G][nkb]
   float* k_mean;      // [G][D] or null
   float* q_mean;      // [G][nqb][D] or null
   const long long* ksum_part;  // [G][nsplit][D] from the statistics pass
   int G, N, Np, blk_q, blk_k, nqb, nkb, nsplit, smooth_k, smooth_q;
+  int q_group, nqg;   // rows per Q scale (divides blk_q) and Q scales per head
   int with_q;         // 0: quantise only K
 };
 
@@ -24,7 +25,7 @@ struct AttnArgs {
   const uint16_t* q;      // [G][N][D] fp16 (Q quantised in the kernel) or null
   const int8_t* q_i8;     // [G][Np][D] (pre-quantised Q)
   const int8_t* k_i8;     // [G][Np][D]
-  const float* q_scale;   // [G][nqb]
+  const float* q_scale;   // [G][nqg]
   const float* k_scale;   // [G][nkb]
   const float* q_mean;    // [G][nqb][D] (variant 1 with Q smoothing)
   const uint16_t* v;      // [G][N][D] fp16 (variant 0)
@@ -33,6 +34,7 @@ struct AttnArgs {
   const float* v_mean;    // [G][D] (variant 1 with V smoothing) or null
   uint16_t* o;            // [G][N][D] fp16
   int G, N, Np, blk_q, blk_k, nqb, nkb;
+  int q_group, nqg;       // rows per Q scale (a power of two dividing blk_q), scales per head
   float kscale;           // sm_scale * log2(e)
 };
 

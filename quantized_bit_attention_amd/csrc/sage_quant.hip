@@ -170,6 +170,7 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 //   blockIdx.x < G * nkb: K block (mean from the pass-1 partial sums when smooth_k);
 //   otherwise a Q block (its own exact block mean when smooth_q).  With with_q = 0 the
 //   grid holds only the K blocks (the attention kernel then quantises Q itself).
+//   K has one scale per block; Q one per group of q_group rows (q_group divides blk_q).
 // MAXR: rows per block rounded up to a multiple of kThreads / (D/8).
 template <int D, int MAXR>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   __shared__ float s_mean[D];
   __shared__ long long s_sum[kThreads][8];
   __shared__ float s_red[4];
+  __shared__ float s_row[MAXR], s_grp[MAXR];  // Q groups finer than the block
 
   const int tid = threadIdx.x, cg = tid % TPR, r0 = tid / TPR;
   const int nk_blocks = a.G * a.nkb;
@@ -242,8 +244,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) mean[j] = s_mean[cg * 8 + j];
 
-  // smoothed values and the block absmax
+  // smoothed values and their absmax (per row, over this thread's 8 channels)
   float x[NIT][8];
+  float ramax[NIT];
   float amax = 0.0f;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -256,12 +259,40 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       if (smooth) { x0 = x0 - mean[2 * j]; x1 = x1 - mean[2 * j + 1]; }
       x[it][2 * j] = valid ? x0 : 0.0f;
       x[it][2 * j + 1] = valid ? x1 : 0.0f;
-      amax = fmaxf(amax, fmaxf(fabsf(x[it][2 * j]), fabsf(x[it][2 * j + 1])));
     }
+    ramax[it] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ramax[it] = fmaxf(ramax[it], fabsf(x[it][j]));
+    amax = fmaxf(amax, ramax[it]);
   }
-  amax = block_max(amax, s_red);
-  const float r = i8_factor(amax);
-  if (tid == 0) (is_k ? a.k_scale : a.q_scale)[(size_t)g * nb + b] = i8_scale(amax);
+  const int grp = is_k ? blk : a.q_group;
+  float* const scale = is_k ? a.k_scale + (size_t)g * a.nkb : a.q_scale + (size_t)g * a.nqg;
+  float r[NIT];
+  if (grp >= blk) {  // one scale for the block
+    amax = block_max(amax, s_red);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) r[it] = i8_factor(amax);
+    if (tid == 0) scale[b] = i8_scale(amax);
+  } else {
+    // each row's absmax over the TPR threads that hold it, then each group's over its rows
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      float v = ramax[it];
+      for (int off = 1; off < TPR; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+      if (cg == 0) s_row[r0 + RPI * it] = v;
+    }
+    __syncthreads();
+    const int ngr = (rows + grp - 1) / grp;
+    if (tid < ngr) {
+      float m = 0.0f;
+      for (int i = tid * grp; i < min(rows, (tid + 1) * grp); ++i) m = fmaxf(m, s_row[i]);
+      s_grp[tid] = m;
+      scale[t0 / grp + tid] = i8_scale(m);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) r[it] = i8_factor(s_grp[min((r0 + RPI * it) / grp, MAXR - 1)]);
+  }
 
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     if (row < rows) {
       uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) packed[j / 4] |= i8_code(x[it][j], r) << (8 * (j % 4));
+      for (int j = 0; j < 8; ++j) packed[j / 4] |= i8_code(x[it][j], r[it]) << (8 * (j % 4));
       *reinterpret_cast<uint2*>(dst + (size_t)(t0 + row) * D + cg * 8) = make_uint2(packed[0], packed[1]);
     }
   }

@@ -52,13 +52,13 @@ def host(t):
 
 def cfg_kw(c):
     return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"],
-                smooth_v=bool(c.get("smooth_v", 0)))
+                smooth_v=bool(c.get("smooth_v", 0)), q_group=c.get("q_group", 0))
 
 
 def oracle_kw(c, bkv=64):
     return dict(causal=c["causal"], variant=c["variant"], blk_q=c["blk_q"], blk_k=c["blk_k"], bkv=bkv,
                 smooth_k=c.get("smooth_k", 1), smooth_q=c.get("smooth_q", 1 if c["variant"] == 1 else 0),
-                smooth_v=c.get("smooth_v", 0))
+                smooth_v=c.get("smooth_v", 0), q_group=c.get("q_group", 0) or None)
 
 
 def check_o(name, g16, o64):
@@ -98,6 +98,37 @@ def test_quant_qk_bitexact(sage, orc, cfg):
     for key in ("q_i8", "k_i8", "q_scale", "k_scale", "k_mean") + (("q_mean",) if sq else ()):
         same = np.array_equal(g[key].view(np.uint8) if g[key].dtype == np.int8 else g[key].view(np.uint32),
                               r[key].view(np.uint8) if r[key].dtype == np.int8 else r[key].view(np.uint32))
+        if not same:
+            diff = np.nonzero(g[key] != r[key])
+            say(f"  {key}: {len(diff[0])} mismatches, first at {[d[0] for d in diff]}")
+        assert same, key
+
+
+QGROUP_QUANT = [
+    # recipe cfg, shape overrides, blk_q, blk_k, q_group, smooth_q
+    (1, dict(N=333, B=1, H=2), 64, 64, 1, 0),
+    (2, dict(N=1000, B=1, H=2), 128, 64, 16, 1),
+    (3, dict(N=200, B=1, H=3), 32, 16, 4, 0),
+    (5, dict(N=4096, B=1, H=2), 128, 64, 1, 1),
+    (2, dict(N=129, B=2, H=1), 64, 32, 2, 1),
+]
+
+
+@pytest.mark.parametrize("cfg,shape,blk_q,blk_k,q_group,sq", QGROUP_QUANT)
+def test_quant_qk_q_group_bitexact(sage, orc, cfg, shape, blk_q, blk_k, q_group, sq):
+    """Q scales per group of q_group rows inside the smoothing block: codes, scales and
+    means bit-exact.  One row is all zeros, so with per-token scales its scale is 0."""
+    c = workloads.make_inputs(cfg, **shape)
+    q = c["q"].copy()
+    q[0, 0, 5] = 0
+    say(f"quant_qk q_group={q_group} {q.shape} blk_q={blk_q} smooth_q={sq}")
+    g = sage.quant_qk(dev(q), dev(c["k"]), blk_q=blk_q, blk_k=blk_k, smooth_q=bool(sq), q_group=q_group)
+    g = {k: host(v) for k, v in g.items()}
+    r = orc.quant(q, c["k"], blk_q=blk_q, blk_k=blk_k, smooth_k=1, smooth_q=sq, q_group=q_group)
+    assert g["q_scale"].shape == r["q_scale"].shape
+    for key in ("q_i8", "k_i8", "q_scale", "k_scale", "k_mean") + (("q_mean",) if sq else ()):
+        view = np.uint8 if g[key].dtype == np.int8 else np.uint32
+        same = np.array_equal(g[key].view(view), r[key].view(view))
         if not same:
             diff = np.nonzero(g[key] != r[key])
             say(f"  {key}: {len(diff[0])} mismatches, first at {[d[0] for d in diff]}")
@@ -239,6 +270,14 @@ EDGE = [
     ("n333_v1_causal_smoothv", 5, dict(N=333, B=1, H=2), dict(causal=1, variant=1, smooth_v=1)),
     ("blk32_v1_smoothqv", 5, dict(N=400, B=1, H=2), dict(causal=0, variant=1, blk_q=32, blk_k=32, smooth_v=1)),
     ("v1_smoothv_no_smoothq", 5, dict(N=256, B=1, H=2), dict(causal=1, variant=1, smooth_q=0, smooth_v=1)),
+    # Q scales finer than the block (q_group rows per scale; 1 = per token)
+    ("qg1_v0_d64", 1, dict(N=200, B=1, H=2), dict(causal=0, variant=0, blk_q=64, q_group=1)),
+    ("qg4_causal_d128", 2, dict(N=300, B=1, H=2), dict(causal=1, variant=0, q_group=4)),
+    ("qg16_blk64_d64", 3, dict(N=520, B=1, H=2), dict(causal=0, variant=0, blk_q=64, blk_k=16, q_group=16)),
+    ("qg1_v1_smoothq", 5, dict(N=333, B=1, H=2), dict(causal=1, variant=1, q_group=1)),
+    ("qg2_v0_smoothq", 2, dict(N=256, B=1, H=2), dict(causal=1, variant=0, smooth_q=1, q_group=2)),
+    ("qg8_v1_smoothqv_d64", 1, dict(N=257, B=1, H=2), dict(causal=0, variant=1, blk_q=32, q_group=8,
+                                                           smooth_v=1)),
 ]
 
 
@@ -264,6 +303,49 @@ def test_attn_q_offset_stress_variant1(sage, orc):
     g = run_gpu(sage, c)
     o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
     check_o("q_offset_v1", g, o)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_attn_full_size_per_token_q_sampled_rows(sage, orc, cfg):
+    """Per-token Q scales (q_group = 1) on each workload's full shape (sampled rows)."""
+    c = dict(inputs(cfg))
+    c.update(q_group=1)
+    B, H, N, d = c["q"].shape
+    G = B * H
+    say(f"attn q_group=1 cfg{cfg} full size {c['q'].shape} causal={c['causal']} variant={c['variant']}")
+    g = run_gpu(sage, c).reshape(G, N, d)
+    rng = np.random.default_rng(200 + cfg)
+    heads, rows = [], []
+    for hd in (0, G // 2, G - 1):
+        for r in sample_rows(N, c["causal"], rng):
+            heads.append(hd)
+            rows.append(r)
+    o = orc.attn_rows(c["q"], c["k"], c["v"], heads, rows, **oracle_kw(c))
+    check_o(f"q_group=1 cfg{cfg} sampled {len(rows)} rows", g[heads, rows], o)
+
+
+def test_attn_per_token_q_mixed_row_magnitudes(sage, orc):
+    """One Q row in eight 64x larger: parity per block and per token, and the per-token
+    GPU output is the closer one to exact attention on the ordinary rows."""
+    rng = np.random.default_rng(9)
+    N, d = 512, 128
+    q = rng.standard_normal((1, 2, N, d))
+    q[:, :, ::8] *= 64.0
+    q = q.astype(np.float16)
+    k = rng.standard_normal((1, 2, N, d)).astype(np.float16)
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float16)
+    exact = orc.attn(q, k, v, exact=1)
+    ordinary = np.ones(N, bool)
+    ordinary[::8] = False
+    err = {}
+    for qg in (0, 1):
+        say(f"attn mixed-magnitude Q rows q_group={qg}")
+        g = host(sage.attn(dev(q), dev(k), dev(v), q_group=qg))
+        o = orc.attn(q, k, v, q_group=qg or None)
+        check_o(f"mixed rows q_group={qg}", g, o)
+        err[qg] = float(np.abs(g.astype(np.float64) - exact)[:, :, ordinary].mean())
+    say(f"  mean |O - exact| on ordinary rows: per block {err[0]:.3e}, per token {err[1]:.3e}")
+    assert err[1] < err[0] / 4
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
@@ -348,29 +430,34 @@ def test_prequant_matches_whole_call_and_is_deterministic(sage):
 
 
 FUSED = [
-    # recipe cfg, shape overrides, blk_q, blk_k, causal
-    (2, dict(N=333, B=1, H=3), 128, 64, 1),
-    (2, dict(N=1000, B=2, H=1), 64, 16, 0),
-    (3, dict(N=200, B=1, H=2), 32, 64, 1),
-    (3, dict(N=4096, B=1, H=2), 128, 128, 0),
-    (1, dict(N=65, B=1, H=1), 32, 32, 0),
+    # recipe cfg, shape overrides, blk_q, blk_k, causal, q_group
+    (2, dict(N=333, B=1, H=3), 128, 64, 1, 0),
+    (2, dict(N=1000, B=2, H=1), 64, 16, 0, 0),
+    (3, dict(N=200, B=1, H=2), 32, 64, 1, 0),
+    (3, dict(N=4096, B=1, H=2), 128, 128, 0, 0),
+    (1, dict(N=65, B=1, H=1), 32, 32, 0, 0),
+    (2, dict(N=333, B=1, H=2), 128, 64, 1, 1),
+    (3, dict(N=300, B=1, H=2), 64, 64, 0, 2),
+    (2, dict(N=257, B=1, H=2), 128, 16, 1, 8),
+    (3, dict(N=129, B=1, H=1), 32, 32, 0, 16),
+    (2, dict(N=500, B=1, H=2), 128, 64, 0, 64),
 ]
 
 
-@pytest.mark.parametrize("cfg,shape,blk_q,blk_k,causal", FUSED)
-def test_fused_q_quantisation_matches_quant_pass(sage, cfg, shape, blk_q, blk_k, causal):
+@pytest.mark.parametrize("cfg,shape,blk_q,blk_k,causal,q_group", FUSED)
+def test_fused_q_quantisation_matches_quant_pass(sage, cfg, shape, blk_q, blk_k, causal, q_group):
     """Variant 0 quantises Q inside the attention kernel: the whole call, the fused kernel
     alone and the quantisation pass + pre-quantised kernel give the same bits.  One Q block
     is all zeros (scale 0, codes 0)."""
     c = workloads.make_inputs(cfg, **shape)
     q = c["q"].copy()
     q[0, 0, :blk_q] = 0
-    say(f"fused Q {q.shape} blk_q={blk_q} blk_k={blk_k} causal={causal}")
+    say(f"fused Q {q.shape} blk_q={blk_q} blk_k={blk_k} causal={causal} q_group={q_group}")
     qd, kd, vd = dev(q), dev(c["k"]), dev(c["v"])
     N = q.shape[2]
-    kw = dict(causal=bool(causal), blk_q=blk_q, blk_k=blk_k)
+    kw = dict(causal=bool(causal), blk_q=blk_q, blk_k=blk_k, q_group=q_group)
     whole = sage.attn(qd, kd, vd, variant=0, **kw)
-    qk = sage.quant_qk(qd, kd, blk_q=blk_q, blk_k=blk_k)
+    qk = sage.quant_qk(qd, kd, blk_q=blk_q, blk_k=blk_k, q_group=q_group)
     fused = sage.attn_qf16(qd, qk, vd, **kw)
     pre = sage.attn_prequant(qk, vd, N, variant=0, **kw)
     torch.cuda.synchronize()

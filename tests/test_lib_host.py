@@ -70,6 +70,10 @@ def test_workspace_size(lib):
     # V smoothing adds the [G, d] fp32 means; it has no meaning for the fp16 P~V variant
     assert sage.workspace_bytes(B, H, N, d, 1, smooth_v=True) == v1 + up(G * d * 4)
     assert sage.workspace_bytes(B, H, N, d, 0, smooth_v=True) == 0
+    # per-token Q scales: the quantisation pass writes one scale per row
+    assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True, q_group=1) == (
+        sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) - up(G * 32 * 4) + up(G * N * 4))
+    assert sage.workspace_bytes(B, H, N, d, 0, q_group=3) == 0
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
     assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
 
@@ -122,13 +126,23 @@ def test_params_rejected(lib):
     assert attn(lib, params=p, variant=0) == -2 and b"smooth_v" in lib.sage_last_error()
 
 
-def test_older_params_layout_is_accepted(lib):
-    # the five-int sage_params of library 0.1 (no smooth_v) still parses: the call gets
-    # past the parameters and fails on the NULL q instead
-    p = sage._params(smooth_v=True)
-    p.struct_size = 5 * ctypes.sizeof(ctypes.c_int)
-    assert attn(lib, params=p, q=None) == -1 and b"q is NULL" in lib.sage_last_error()
-    assert lib.sage_version() >= 200
+def test_older_params_layouts_are_accepted(lib):
+    # the five- and six-int sage_params of libraries 0.1 and 0.2 still parse: the call
+    # gets past the parameters and fails on the NULL q instead
+    for n in (5, 6):
+        p = sage._params(smooth_v=True, q_group=3)  # fields past struct_size are not read
+        p.struct_size = n * ctypes.sizeof(ctypes.c_int)
+        assert attn(lib, params=p, q=None, variant=1) == -1 and b"q is NULL" in lib.sage_last_error()
+    assert lib.sage_version() >= 300
+
+
+@pytest.mark.parametrize("blk_q,q_group,code", [(128, 0, -1), (128, 1, -1), (64, 16, -1), (32, 32, -1),
+                                                (128, 3, -2), (64, 128, -2), (128, -1, -2)])
+def test_q_group_validation(lib, blk_q, q_group, code):
+    # accepted values fail later, on the NULL q; rejected ones name q_group
+    p = sage._params(blk_q=blk_q, q_group=q_group)
+    assert attn(lib, params=p, q=None) == code
+    assert (b"q_group" in lib.sage_last_error()) == (code == -2)
 
 
 def test_other_entry_points_reject(lib):
