@@ -41,12 +41,14 @@ def load(path: str | None = None):
     lib.oracle_attn_rows.restype = i
     lib.oracle_quant.argtypes = [p, p, p, i, i, i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
     lib.oracle_quant.restype = i
+    lib.oracle_quant_mx.argtypes = [p, p, i, i, i, i, i, p, p, p, p, p]
+    lib.oracle_quant_mx.restype = i
     lib.oracle_qk_int32.argtypes = [p, p, i, i, i, i, i, i, p]
     lib.oracle_qk_int32.restype = i
     lib.oracle_pad_len.argtypes = [i]
     lib.oracle_pad_len.restype = i
     for name in ("oracle_f16_decode_n", "oracle_f16_encode_n", "oracle_e4m3_decode_n",
-                 "oracle_e4m3_encode_n"):
+                 "oracle_e4m3_encode_n", "oracle_e2m1_decode_n", "oracle_e2m1_encode_n"):
         getattr(lib, name).argtypes = [p, sz, p]
         getattr(lib, name).restype = None
     return lib
@@ -75,6 +77,18 @@ class Oracle:
         c = np.ascontiguousarray(codes, dtype=np.uint8)
         out = np.empty(c.shape, dtype=np.float64)
         self.lib.oracle_e4m3_decode_n(c.ctypes.data, c.size, out.ctypes.data)
+        return out
+
+    def e2m1_decode(self, codes: np.ndarray) -> np.ndarray:
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_e2m1_decode_n(c.ctypes.data, c.size, out.ctypes.data)
+        return out
+
+    def e2m1_encode(self, x: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint8)
+        self.lib.oracle_e2m1_encode_n(a.ctypes.data, a.size, out.ctypes.data)
         return out
 
     def e4m3_encode(self, x: np.ndarray) -> np.ndarray:
@@ -115,6 +129,23 @@ class Oracle:
             r["v_mean"].ctypes.data if with_v else None)
         if rc:
             raise ValueError("oracle_quant: bad arguments")
+        return r
+
+    def quant_mx(self, q, k, smooth_k=1) -> dict:
+        """Variant 2 (MXFP4) tensors: E2M1 codes one per byte [B, H, Np, d], E8M0 block
+        scales [B, H, Np, d/32], k_mean [B, H, d]."""
+        q = _f16(q)
+        k = _f16(k)
+        B, H, N, d = q.shape
+        Np = self.pad_len(N)
+        r = dict(q_codes=np.empty((B, H, Np, d), np.uint8), k_codes=np.empty((B, H, Np, d), np.uint8),
+                 q_e8=np.empty((B, H, Np, d // 32), np.uint8), k_e8=np.empty((B, H, Np, d // 32), np.uint8),
+                 k_mean=np.empty((B, H, d), np.float32))
+        rc = self.lib.oracle_quant_mx(q.ctypes.data, k.ctypes.data, B, H, N, d, smooth_k, r["q_codes"].ctypes.data,
+                                      r["k_codes"].ctypes.data, r["q_e8"].ctypes.data, r["k_e8"].ctypes.data,
+                                      r["k_mean"].ctypes.data)
+        if rc:
+            raise ValueError("oracle_quant_mx: bad arguments")
         return r
 
     # ---- step 4

@@ -16,6 +16,10 @@
  *  [SA2-g]   the same abstracts on the granularity of the Q/K scales: "thread-level"
  *            (ICML 2025, arXiv 2411.10958) and "warp-level" (arXiv 2502.01776); the
  *            [SA-sum] "Key points" speak of per-token quantisation.
+ *  [SA3]     the SageAttention3 abstract (ICLR 2025 page): FP4 attention on matrix
+ *            units with microscaling.  The pages give no block format; variant 2 reads
+ *            it as OCP MXFP4 (Microscaling Formats v1.0): E2M1 elements, one E8M0
+ *            scale per 32 consecutive values.
  *  [FA]      FlashAttention / FlashAttention-2 and "Online normalizer calculation
  *            for softmax", entries of the reference list on the [SA-sum] page.
  *
@@ -36,6 +40,9 @@
  *      V' = V - v_mean (token mean per channel)
  *   9. O / l (variant 1 also * dV / 448, plus v_mean with V smoothing: the rows
  *      of P~ / l sum to one, so the mean comes back out unchanged)
+ * Variant 2 ([SA3]) replaces steps 3-5: Q and K' are quantised per token to MXFP4
+ * (blocks of 32 channels), S = sum over blocks of 2^(eq + ek) * (E2M1 dot product),
+ * s = sm_scale * S (no Q smoothing); steps 6-9 are those of variant 1.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - means are exact: fp16 inputs are integer multiples of 2^-24, so the token
@@ -128,6 +135,47 @@ uint8_t oracle_e4m3_encode(double x) {
   return (uint8_t)(s | ((E + 7) << 3) | ((int)q - 8));
 }
 
+/* OCP FP4 E2M1 (the MX element format): sign, 2 exponent bits (bias 1), 1 mantissa
+ * bit; exponent 0 is subnormal (m * 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_decode(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* double -> E2M1: the nearest of the eight magnitudes, a tie going to the even code,
+ * saturating at 6; the sign is kept (also of zero). */
+uint8_t oracle_e2m1_encode(double x) {
+  uint8_t s = signbit(x) ? 8 : 0;
+  double a = fabs(x);
+  if (a >= 6.0) return (uint8_t)(s | 7); /* saturate (distances to huge values all round alike) */
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    double dc = fabs(oracle_e2m1_decode((uint8_t)c) - a), db = fabs(oracle_e2m1_decode((uint8_t)best) - a);
+    if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)(s | best);
+}
+
+/* One MX block of n values (MXFP4): shared exponent E = floor(log2(max |x|)) - 2 (2 is
+ * the largest exponent of E2M1), E8M0 code E + 127 clamped to [0, 254], elements
+ * E2M1(x / 2^(code - 127)).  An all-zero block gets code 0 and zero elements.
+ * Returns the E8M0 code. */
+static uint8_t mx_block(const float* x, int n, uint8_t* codes) {
+  float a = 0.0f;
+  for (int i = 0; i < n; ++i) a = fmaxf(a, fabsf(x[i]));
+  int code = 0;
+  if (a > 0.0f) {
+    int e;
+    frexp((double)a, &e); /* a in [2^(e-1), 2^e) */
+    code = (e - 1) - 2 + 127;
+    if (code < 0) code = 0;
+    if (code > 254) code = 254;
+  }
+  for (int i = 0; i < n; ++i) codes[i] = oracle_e2m1_encode(ldexp((double)x[i], 127 - code));
+  return (uint8_t)code;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Step 1-3: means, smoothing, per-block INT8 quantisation                  */
 /* ------------------------------------------------------------------------ */
@@ -196,6 +244,31 @@ static void quant_head(const uint16_t* x, int N, int Np, int d, int blk, int grp
   free(buf);
 }
 
+/* Variant 2: one head's [N][d] tensor to MXFP4 per token (d / 32 blocks of 32
+ * channels), after subtracting the token mean when mean_mode == 1 (k_mean[d]
+ * written).  codes [Np][d] (one E2M1 code per byte), e8 [Np][d/32]; rows >= N zero. */
+static void quant_head_mx(const uint16_t* x, int N, int Np, int d, int mean_mode, uint8_t* codes, uint8_t* e8,
+                          float* k_mean) {
+  float* mean = (float*)calloc((size_t)d, sizeof(float));
+  float* row = (float*)malloc(sizeof(float) * (size_t)d);
+  if (mean_mode == 1) {
+    for (int c = 0; c < d; ++c) mean[c] = exact_mean(x, d, 0, N, c);
+    if (k_mean) memcpy(k_mean, mean, sizeof(float) * (size_t)d);
+  }
+  for (int t = 0; t < N; ++t) {
+    for (int c = 0; c < d; ++c) {
+      float v = (float)oracle_f16_decode(x[(size_t)t * d + c]);
+      row[c] = mean_mode ? v - mean[c] : v;
+    }
+    for (int b = 0; b < d / 32; ++b)
+      e8[(size_t)t * (d / 32) + b] = mx_block(row + 32 * b, 32, codes + (size_t)t * d + 32 * b);
+  }
+  memset(codes + (size_t)N * d, 0, (size_t)(Np - N) * d);
+  memset(e8 + (size_t)N * (d / 32), 0, (size_t)(Np - N) * (d / 32));
+  free(mean);
+  free(row);
+}
+
 /* V in FP8 for one head: per-channel scale absmax / 448, codes transposed to
  * vt[d][Np] (columns >= N zero).  With smooth_v, each channel first loses its
  * exact token mean (written to vmean[d]); otherwise vmean (when non-NULL) is 0. */
@@ -252,6 +325,8 @@ typedef struct {
   uint8_t* vt;       /* [d][Np] (variant 1) */
   float* vs;         /* [d] (variant 1) */
   float* vm;         /* [d] (variant 1): v_mean, zeros without V smoothing */
+  uint8_t *qc, *kc;  /* [Np][d] E2M1 codes (variant 2) */
+  uint8_t *qe, *ke;  /* [Np][d/32] E8M0 block scales (variant 2) */
 } prep_t;
 
 static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -261,15 +336,25 @@ static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, c
   int nqg = (N + P->q_group - 1) / P->q_group;
   memset(h, 0, sizeof(*h));
   if (P->exact) return;
-  h->qi = (int8_t*)malloc((size_t)Np * d);
-  h->ki = (int8_t*)malloc((size_t)Np * d);
-  h->qs = (float*)malloc(sizeof(float) * (size_t)nqg);
-  h->ks = (float*)malloc(sizeof(float) * (size_t)nkb);
-  h->kmean = (float*)calloc((size_t)d, sizeof(float));
-  h->qmean = (float*)calloc((size_t)nqb * d, sizeof(float));
-  quant_head(k, N, Np, d, P->blk_k, P->blk_k, P->smooth_k ? 1 : 0, h->ki, h->ks, h->kmean, NULL);
-  quant_head(q, N, Np, d, P->blk_q, P->q_group, P->smooth_q ? 2 : 0, h->qi, h->qs, NULL, h->qmean);
-  if (P->variant == 1) {
+  if (P->variant == 2) {
+    h->qc = (uint8_t*)malloc((size_t)Np * d);
+    h->kc = (uint8_t*)malloc((size_t)Np * d);
+    h->qe = (uint8_t*)malloc((size_t)Np * (d / 32));
+    h->ke = (uint8_t*)malloc((size_t)Np * (d / 32));
+    h->kmean = (float*)calloc((size_t)d, sizeof(float));
+    quant_head_mx(k, N, Np, d, P->smooth_k ? 1 : 0, h->kc, h->ke, h->kmean);
+    quant_head_mx(q, N, Np, d, 0, h->qc, h->qe, NULL);
+  } else {
+    h->qi = (int8_t*)malloc((size_t)Np * d);
+    h->ki = (int8_t*)malloc((size_t)Np * d);
+    h->qs = (float*)malloc(sizeof(float) * (size_t)nqg);
+    h->ks = (float*)malloc(sizeof(float) * (size_t)nkb);
+    h->kmean = (float*)calloc((size_t)d, sizeof(float));
+    h->qmean = (float*)calloc((size_t)nqb * d, sizeof(float));
+    quant_head(k, N, Np, d, P->blk_k, P->blk_k, P->smooth_k ? 1 : 0, h->ki, h->ks, h->kmean, NULL);
+    quant_head(q, N, Np, d, P->blk_q, P->q_group, P->smooth_q ? 2 : 0, h->qi, h->qs, NULL, h->qmean);
+  }
+  if (P->variant >= 1) {
     h->vt = (uint8_t*)malloc((size_t)d * Np);
     h->vs = (float*)malloc(sizeof(float) * (size_t)d);
     h->vm = (float*)malloc(sizeof(float) * (size_t)d);
@@ -280,6 +365,7 @@ static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, c
 static void free_prep(prep_t* h) {
   free(h->qi); free(h->ki); free(h->qs); free(h->ks); free(h->kmean); free(h->qmean);
   free(h->vt); free(h->vs); free(h->vm);
+  free(h->qc); free(h->kc); free(h->qe); free(h->ke);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -320,6 +406,17 @@ static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, cons
         double acc = 0.0;
         for (int c = 0; c < d; ++c)
           acc += oracle_f16_decode(q[(size_t)i * d + c]) * oracle_f16_decode(k[(size_t)j * d + c]);
+        sj = P->sm_scale * acc;
+      } else if (P->variant == 2) {
+        /* per 32-channel block: exact E2M1 dot product times both block scales */
+        const int nb = d / 32;
+        double acc = 0.0;
+        for (int b = 0; b < nb; ++b) {
+          double blk = 0.0;
+          for (int c = 32 * b; c < 32 * b + 32; ++c)
+            blk += oracle_e2m1_decode(h->qc[(size_t)i * d + c]) * oracle_e2m1_decode(h->kc[(size_t)j * d + c]);
+          acc += ldexp(blk, (int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb + b] - 254);
+        }
         sj = P->sm_scale * acc;
       } else {
         int32_t S = dot_i8(h->qi + (size_t)i * d, h->ki + (size_t)j * d, d);
@@ -456,7 +553,8 @@ static int check_params(const params_t* P) {
   if (P->blk_q < 1 || P->blk_k < 1 || P->bkv < 1) return -1;
   if (P->q_group < 1 || P->blk_q % P->q_group) return -1;
   if (P->causal != 0 && P->causal != 1) return -1;
-  if (P->variant != 0 && P->variant != 1) return -1;
+  if (P->variant < 0 || P->variant > 2) return -1;
+  if (P->variant == 2 && (P->d % 32 || P->smooth_q)) return -1; /* MX blocks of 32; no Q smoothing */
   if (P->smooth_v != 0 && P->smooth_v != 1) return -1;
   if (!(P->sm_scale > 0.0) || !isfinite(P->sm_scale)) return -1;
   if ((int64_t)P->d * 127 * 127 > 2147483647LL) return -1; /* int32 bound of S */
@@ -580,7 +678,30 @@ int oracle_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int Np, int d, int r
   return 0;
 }
 
+/*
+ * Variant 2 tensors for all heads: q_codes, k_codes [G][Np][d] (one E2M1 code per
+ * byte), q_e8, k_e8 [G][Np][d/32] E8M0, k_mean [G][d] (zeros unless smooth_k).
+ */
+int oracle_quant_mx(const uint16_t* q, const uint16_t* k, int B, int H, int N, int d, int smooth_k,
+                    uint8_t* q_codes, uint8_t* k_codes, uint8_t* q_e8, uint8_t* k_e8, float* k_mean) {
+  if (B < 1 || H < 1 || N < 1 || d < 32 || d % 32) return -1;
+  const int Np = oracle_pad_len(N), G = B * H;
+  const size_t hs = (size_t)N * d, hp = (size_t)Np * d, he = (size_t)Np * (d / 32);
+  for (int g = 0; g < G; ++g) {
+    memset(k_mean + (size_t)g * d, 0, sizeof(float) * (size_t)d);
+    quant_head_mx(k + g * hs, N, Np, d, smooth_k ? 1 : 0, k_codes + g * hp, k_e8 + g * he, k_mean + (size_t)g * d);
+    quant_head_mx(q + g * hs, N, Np, d, 0, q_codes + g * hp, q_e8 + g * he, NULL);
+  }
+  return 0;
+}
+
 /* Array forms of the codecs (for tests). */
+void oracle_e2m1_decode_n(const uint8_t* c, size_t n, double* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = oracle_e2m1_decode(c[i]);
+}
+void oracle_e2m1_encode_n(const double* x, size_t n, uint8_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(x[i]);
+}
 void oracle_f16_decode_n(const uint16_t* h, size_t n, double* out) {
   for (size_t i = 0; i < n; ++i) out[i] = oracle_f16_decode(h[i]);
 }

@@ -44,6 +44,11 @@ MUTANTS = {
     "v mean not added back": ("/ (448.0 * l) + (double)h->vm[c];", "/ (448.0 * l);"),
     "v mean subtracted twice": ("      if (smooth_v) x = x - mean;\n      float y = x * r;",
                                 "      if (smooth_v) x = x - mean - mean;\n      float y = x * r;"),
+    "mx exponent off by one": ("code = (e - 1) - 2 + 127;", "code = (e - 1) - 1 + 127;"),
+    "e2m1 ties to odd": ("(dc == db && (c & 1) == 0)", "(dc == db && (c & 1) == 1)"),
+    "mx score drops the k block scale": ("(int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb + b] - 254",
+                                         "(int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb] - 254"),
+    "mx k not smoothed": ("quant_head_mx(k, N, Np, d, P->smooth_k ? 1 : 0,", "quant_head_mx(k, N, Np, d, 0,"),
     "v absmax before smoothing": ("      if (smooth_v) x = x - mean;\n      a = fmaxf(a, fabsf(x));",
                                   "      a = fmaxf(a, fabsf(x));"),
 }
@@ -77,6 +82,12 @@ def _battery(orc):
         yield f"v smoothing constant c{causal}", (
             lambda causal=causal: pins.test_v_smoothing_constant_v_is_returned_exactly(orc, causal))
     yield "v smoothing offset", lambda: pins.test_v_smoothing_removes_the_channel_offset_error(orc)
+    yield "e2m1 decode", lambda: pins.test_e2m1_decode_matches_the_ocp_table(orc)
+    yield "e2m1 encode", lambda: pins.test_e2m1_encode_rne_and_saturation(orc)
+    yield "mx block", lambda: pins.test_mx_block_matches_bruteforce(orc)
+    for causal in (0, 1):
+        yield f"mx lossless c{causal}", lambda causal=causal: pins.test_mx_lossless_inputs_match_exact_attention(orc, causal)
+    yield "mx k smoothing", lambda: pins.test_mx_k_smoothing_removes_the_channel_offset_error(orc)
 
 
 @pytest.fixture(scope="module")

@@ -86,6 +86,114 @@ def test_e4m3_encode_rne_and_saturation(orc):
     assert list(big) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x80]
 
 
+# MXFP4 (variant 2, [SA3] read as OCP Microscaling v1.0): E2M1 elements, E8M0 scales
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # the OCP MX element table, codes 0..7
+
+
+def test_e2m1_decode_matches_the_ocp_table(orc):
+    got = orc.e2m1_decode(np.arange(16, dtype=np.uint8))
+    assert list(got[:8]) == E2M1_TABLE
+    assert list(got[8:]) == [-v for v in E2M1_TABLE]
+    assert math.copysign(1.0, got[8]) == -1.0          # code 8 is -0
+
+
+def _e2m1_by_thresholds(x):
+    """E2M1 code of x from the rounding thresholds: a midpoint goes to the even code
+    (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), above 6
+    saturates."""
+    a = abs(x)
+    c = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0)
+    return int(c) | (8 if math.copysign(1.0, x) < 0 else 0)
+
+
+def test_e2m1_encode_rne_and_saturation(orc):
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    xs = E2M1_TABLE + mids + [np.nextafter(m, 0.0) for m in mids] + [np.nextafter(m, 9.0) for m in mids]
+    xs += [6.0, 6.5, 7.9, 100.0, 1e30, 1e-30, 0.1, 0.0]
+    xs += list(np.random.default_rng(3).uniform(0, 8, 2000))
+    xs = np.array(xs + [-x for x in xs])
+    got = orc.e2m1_encode(xs)
+    assert [int(c) for c in got] == [_e2m1_by_thresholds(float(x)) for x in xs]
+    # every tie goes to the even code; nothing but 6 lies above 5
+    assert all(c % 2 == 0 for c in orc.e2m1_encode(np.array(mids)))
+
+
+def test_mx_block_matches_bruteforce(orc):
+    """Per-token MXFP4 blocks of 32 channels: E8M0 code = floor(log2(max|x|)) - 2 + 127,
+    elements = E2M1(x / 2^(code - 127)); an all-zero block gets code 0.  The scale is
+    decoded by torch's float8_e8m0fnu, the elements by the threshold rule."""
+    rng = np.random.default_rng(4)
+    N, d = 40, 64
+    x = rng.standard_normal((1, 1, N, d)) * 2.0 ** rng.integers(-12, 10, (1, 1, N, 1))
+    x[0, 0, 3, :32] = 0                    # an all-zero block
+    x[0, 0, 4, 5] = 8.0                    # amax a power of two: element 4
+    x[0, 0, 6, 40] = 7.99                  # amax just below 8: the top elements saturate to 6
+    x = x.astype(np.float16)
+    r = orc.quant_mx(x, x, smooth_k=0)
+    codes, e8 = r["q_codes"][0, 0], r["q_e8"][0, 0]
+    for t in range(N):
+        for b in range(d // 32):
+            blk = x[0, 0, t, 32 * b:32 * b + 32].astype(np.float32)
+            a = float(np.abs(blk).max())
+            want_e8 = 0 if a == 0 else math.frexp(a)[1] - 1 - 2 + 127
+            assert e8[t, b] == want_e8, (t, b)
+            X = torch.tensor([int(e8[t, b])], dtype=torch.uint8).view(torch.float8_e8m0fnu).float().item()
+            want = [_e2m1_by_thresholds(float(v) / X) if a else 0 for v in blk]
+            want = [w if a else (8 if math.copysign(1.0, float(v)) < 0 else 0) for w, v in zip(want, blk)]
+            assert [int(c) for c in codes[t, 32 * b:32 * b + 32]] == want, (t, b)
+    assert codes[4, 5] == 6 and codes[6, 40] == 7
+    assert not r["q_codes"][0, 0, N:].any() and not r["q_e8"][0, 0, N:].any()
+
+
+def _mx_lossless_case(N=64, d=64, seed=31):
+    """Q, K with entries in {0, +-1, +-2, +-4}: every 32-channel block is exact in MXFP4
+    (its max m in {1, 2, 4} gives scale m/4 and elements v * 4/m).  Scores are integers
+    with a row range <= 12; V as in _lossless_case (exact in FP8)."""
+    rng = np.random.default_rng(seed)
+    q = np.zeros((N, d))
+    for i in range(N):
+        q[i, rng.choice(d, 3, replace=False)] = rng.choice([-1.0, 1.0], 3)
+    k = rng.choice([0.0, 0.0, 0.0, 1.0, -1.0, 2.0, -2.0], (N, d))
+    k[:, 0] = 4.0
+    k[:, 32] = 2.0
+    S = q @ k.T
+    assert np.all(S.max(1) - S.min(1) <= 15)
+    v = rng.integers(-7, 8, (N, d)).astype(np.float64)
+    v[0] = 7
+    f = lambda a: a.astype(np.float16)[None, None]
+    return f(q), f(k), f(v)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_mx_lossless_inputs_match_exact_attention(orc, causal):
+    """Variant 2 with exactly representable Q and K (K unsmoothed) equals base-2 softmax
+    attention: pins the block scales in the score, the block index, and the FP8 P~V."""
+    q, k, v = _mx_lossless_case()
+    r = orc.quant_mx(q, k, smooth_k=0)
+    dec = orc.e2m1_decode
+    for name, x in (("q", q), ("k", k)):
+        codes, e8 = r[f"{name}_codes"][0, 0, :64], r[f"{name}_e8"][0, 0, :64]
+        back = dec(codes) * np.repeat(2.0 ** (e8.astype(np.int64) - 127), 32, axis=1)
+        assert np.array_equal(back, x[0, 0].astype(np.float64))
+    o = orc.attn(q, k, v, causal=causal, variant=2, smooth_k=0, bkv=16, sm_scale=math.log(2.0))
+    S = q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T
+    w = np.exp2(S - S.max(1, keepdims=True))
+    if causal:
+        w = np.tril(w)
+    ref = (w @ v[0, 0].astype(np.float64)) / w.sum(1, keepdims=True)
+    assert np.max(np.abs(o[0, 0] - ref)) < 1e-12
+
+
+def test_mx_k_smoothing_removes_the_channel_offset_error(orc):
+    """Per-token MXFP4 blocks share one scale across 32 channels, so a channel offset of
+    K swamps the other channels of its block; subtracting K's token mean ([SA-sum] I1)
+    restores them."""
+    x = workloads.make_inputs(1, N=256, B=1, H=1)
+    exact = orc.attn(x["q"], x["k"], x["v"], exact=1)
+    e = {sk: float(np.abs(orc.attn(x["q"], x["k"], x["v"], variant=2, smooth_k=sk) - exact).mean()) for sk in (0, 1)}
+    assert e[1] < e[0] / 2.5, e   # measured 0.0133 against 0.0415
+
+
 # --------------------------------------------------------------------------
 # steps 1-3: mean, smoothing, quantisation  ([SA-sum] Summary, I1)
 # --------------------------------------------------------------------------
