@@ -12,8 +12,8 @@ duration from HIP events on the launch stream), and the CPU oracle timed on a
 bounded sample of the same workload.
 
 --config picks another workload; --variant 1 runs the FP8 P~V variant on it
-(with Q smoothing) and --smooth-v adds V smoothing to that variant; --q-group 1
-uses per-token Q scales.
+(with Q smoothing), --variant 2 the MXFP4 Q K^T variant, --smooth-v adds V
+smoothing to either; --q-group 1 uses per-token INT8 Q scales.
 """
 import argparse
 import hashlib
@@ -65,8 +65,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = the headline workload)")
-    ap.add_argument("--variant", type=int, choices=(0, 1), default=None,
-                    help="0: INT8 QK + FP16 P~V, 1: INT8 QK + Q smoothing + FP8 P~V (default: the workload's)")
+    ap.add_argument("--variant", type=int, choices=(0, 1, 2), default=None,
+                    help="0: INT8 QK + FP16 P~V, 1: INT8 QK + Q smoothing + FP8 P~V, 2: MXFP4 QK + FP8 P~V "
+                         "(default: the workload's)")
     ap.add_argument("--smooth-v", action="store_true",
                     help="variant 1 only: subtract V's token mean before FP8 and add it back")
     ap.add_argument("--q-group", type=int, default=0,
@@ -94,8 +95,8 @@ def main():
     causal = cfg["causal"]
     variant = cfg["variant"] if args.variant is None else args.variant
     smooth_v = bool(args.smooth_v)
-    if smooth_v and variant != 1:
-        print("bench.py: --smooth-v needs the FP8 P~V variant (--variant 1, or --config 5)", file=sys.stderr)
+    if smooth_v and variant == 0:
+        print("bench.py: --smooth-v needs an FP8 P~V variant (--variant 1 or 2, or --config 5)", file=sys.stderr)
         sys.exit(2)
     q_group = args.q_group
     opts = dict(causal=bool(causal), variant=variant, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_v=smooth_v,
@@ -124,9 +125,15 @@ def main():
     # the attention kernel alone, as the step launches it (same stream, same launch
     # configuration): variant 0 quantises Q inside the kernel, variant 1 reads the
     # pre-quantised Q and FP8 V
-    qk = sage.quant_qk(q, k, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=variant == 1, q_group=q_group)
-    vq = sage.quant_v(v, smooth_v=smooth_v) if variant == 1 else None
-    if variant == 0:
+    if variant == 2:
+        qk = sage.quant_qk_mx(q, k)
+    else:
+        qk = sage.quant_qk(q, k, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=variant == 1, q_group=q_group)
+    vq = sage.quant_v(v, smooth_v=smooth_v) if variant != 0 else None
+    if variant == 2:
+        def kernel():
+            sage.attn_prequant_mx(qk, vq, N, causal=bool(causal), smooth_v=smooth_v, out=out)
+    elif variant == 0:
         def kernel():
             sage.attn_qf16(q, qk, v, out=out, causal=bool(causal), blk_q=cfg["blk_q"], blk_k=cfg["blk_k"],
                            q_group=q_group)
@@ -167,7 +174,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp16" if variant == 0 else "int8+fp8",
+        "dtype": ("int8+fp16", "int8+fp8", "mxfp4+fp8")[variant],
         "data": "synthetic (seeded SplitMix64/Box-Muller; K with per-channel offsets)",
         "config": {"workload": f"{cfg['name']} B={B} H={H} N={N} d={d}", "B": B, "H": H, "N": N, "d": d,
                    "causal": causal, "variant": variant, "blk_q": cfg["blk_q"], "blk_k": cfg["blk_k"],

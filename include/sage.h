@@ -49,7 +49,10 @@ enum {
 
 enum {
   SAGE_VARIANT_INT8QK_FP16PV = 0, /* SageAttention: INT8 Q K^T, FP16 P~ V (fp32 accumulation) */
-  SAGE_VARIANT_INT8QK_FP8PV = 1   /* SageAttention2-style: + Q smoothing, FP8 P~ and V, two-level accumulation */
+  SAGE_VARIANT_INT8QK_FP8PV = 1,  /* SageAttention2-style: + Q smoothing, FP8 P~ and V, two-level accumulation */
+  SAGE_VARIANT_MXFP4QK_FP8PV = 2  /* SageAttention3-style FP4 scores: per-token MXFP4 Q and K' (OCP
+                                     microscaling, blocks of 32 channels), P~ V as variant 1; no Q
+                                     smoothing */
 };
 
 /* Optional knobs.  Pass NULL for the defaults; set struct_size = sizeof(sage_params). */
@@ -153,6 +156,33 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
                            const uint8_t* v_f8, const float* v_scale, const float* v_mean, void* o,
                            int B, int H, int N, int d, int causal, float sm_scale, int variant,
                            const sage_params* p, void* stream);
+
+/*
+ * Per-token MXFP4 of Q and K for the MXFP4 variant (SageAttention3 abstract: FP4
+ * attention; the block format is read as OCP Microscaling MXFP4):
+ *   K' = K - k_mean with smooth_k (the sage_quant_qk rule for k_mean), Q unsmoothed;
+ *   each token's d channels form d/32 blocks of 32; per block the E8M0 scale code
+ *   s = floor(log2(max |x|)) - 2 + 127 clamped to [0, 254] (0 for an all-zero block)
+ *   and E2M1 elements E2M1(x / 2^(s - 127)): round to nearest, ties to the even code,
+ *   saturating at 6, sign kept.
+ *   q_f4, k_f4 [B,H,Np,d/2]: two codes per byte, the lower channel in the low nibble;
+ *   q_e8, k_e8 [B,H,Np,d/32]: the scale codes; rows >= N zero.
+ * ws: sage_workspace_bytes(..., 2, NULL) bytes suffice (only the K sums are used).
+ */
+int sage_quant_qk_mx(const void* q, const void* k, int B, int H, int N, int d, int smooth_k,
+                     uint8_t* q_f4, uint8_t* k_f4, uint8_t* q_e8, uint8_t* k_e8, float* k_mean,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The MXFP4 variant's attention kernel alone, on sage_quant_qk_mx and
+ * sage_quant_v(_ex) outputs: S = sum over blocks of 2^(sq + sk - 254) times the E2M1
+ * dot product (fp32 matrix-unit accumulation), then the online softmax and FP8 P~ V
+ * of variant 1.  v_mean is read only with p->smooth_v (16-byte aligned).
+ */
+int sage_attn_fwd_prequant_mx(const uint8_t* q_f4, const uint8_t* k_f4, const uint8_t* q_e8,
+                              const uint8_t* k_e8, const uint8_t* v_f8, const float* v_scale,
+                              const float* v_mean, void* o, int B, int H, int N, int d, int causal,
+                              float sm_scale, const sage_params* p, void* stream);
 
 /*
  * The attention kernel that sage_attn_fwd runs for variant 0 without Q smoothing: Q

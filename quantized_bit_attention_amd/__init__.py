@@ -17,11 +17,13 @@ import os
 
 import torch
 
-__all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "debug_qk_int32", "workspace_bytes",
-           "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV"]
+__all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
+           "debug_qk_int32", "workspace_bytes",
+           "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4"]
 
 VARIANT_FP16PV = 0
 VARIANT_FP8PV = 1
+VARIANT_MXFP4 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsage.so")
@@ -64,6 +66,8 @@ def _load():
         "sage_attn_fwd_ex": ([P, P, P, P, I, I, I, I, I, F, I, PP, P, S, P], I),
         "sage_attn_fwd_prequant": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
         "sage_attn_fwd_qf16": ([P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
+        "sage_quant_qk_mx": ([P, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
+        "sage_attn_fwd_prequant_mx": ([P, P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
         "sage_last_error": ([], ctypes.c_char_p),
     }
@@ -230,6 +234,43 @@ def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, 
     rc = _load().sage_attn_fwd_qf16(_ptr(q), _ptr(qk["k_i8"]), _ptr(qk["k_scale"]), _ptr(v), _ptr(out), B, H, N, d,
                                     int(bool(causal)), float(sm_scale), ctypes.byref(p), _stream(q.device))
     _check(rc, "sage_attn_fwd_qf16")
+    return out
+
+
+def quant_qk_mx(q, k, smooth_k=True) -> dict:
+    """Per-token MXFP4 of Q and K' (variant 2): q_f4 / k_f4 [B, H, Np, d/2] (two E2M1 codes per
+    byte), q_e8 / k_e8 [B, H, Np, d/32] (E8M0 block scales), k_mean [B, H, d]."""
+    B, H, N, d = _check_qkv(q, k)
+    dev = q.device
+    Np = pad_len(N)
+    r = dict(q_f4=torch.empty((B, H, Np, d // 2), dtype=torch.uint8, device=dev),
+             k_f4=torch.empty((B, H, Np, d // 2), dtype=torch.uint8, device=dev),
+             q_e8=torch.empty((B, H, Np, d // 32), dtype=torch.uint8, device=dev),
+             k_e8=torch.empty((B, H, Np, d // 32), dtype=torch.uint8, device=dev),
+             k_mean=torch.zeros((B, H, d), dtype=torch.float32, device=dev))
+    lib = _load()
+    ws = _workspace(lib.sage_workspace_bytes(B, H, N, d, VARIANT_MXFP4, None), dev, None)
+    rc = lib.sage_quant_qk_mx(_ptr(q), _ptr(k), B, H, N, d, int(bool(smooth_k)), _ptr(r["q_f4"]), _ptr(r["k_f4"]),
+                              _ptr(r["q_e8"]), _ptr(r["k_e8"]), _ptr(r["k_mean"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "sage_quant_qk_mx")
+    return r
+
+
+def attn_prequant_mx(qk: dict, vq: dict, N, causal=False, sm_scale=None, smooth_v=False, out=None):
+    """The variant-2 attention kernel alone, on quant_qk_mx() and quant_v() outputs."""
+    B, H, Np, dh = qk["q_f4"].shape
+    d = 2 * dh
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    dev = qk["q_f4"].device
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
+    p = _params(128, 64, True, False, smooth_v)
+    rc = _load().sage_attn_fwd_prequant_mx(
+        _ptr(qk["q_f4"]), _ptr(qk["k_f4"]), _ptr(qk["q_e8"]), _ptr(qk["k_e8"]), _ptr(vq["v_f8"]), _ptr(vq["v_scale"]),
+        _ptr(vq["v_mean"]) if smooth_v else None, _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale),
+        ctypes.byref(p), _stream(dev))
+    _check(rc, "sage_attn_fwd_prequant_mx")
     return out
 
 

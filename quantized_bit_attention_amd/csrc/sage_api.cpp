@@ -69,8 +69,10 @@ int read_params(const sage_params* p, int variant, Params* out) {
   if ((r.smooth_k != 0 && r.smooth_k != 1) || (r.smooth_q != 0 && r.smooth_q != 1) ||
       (r.smooth_v != 0 && r.smooth_v != 1))
     return fail(SAGE_ERR_INVALID_ARG, "smooth_k / smooth_q / smooth_v must be 0 or 1");
-  if (r.smooth_v && variant != SAGE_VARIANT_INT8QK_FP8PV)
-    return fail(SAGE_ERR_UNSUPPORTED, "smooth_v applies to the FP8 P~V variant only");
+  if (r.smooth_v && variant == SAGE_VARIANT_INT8QK_FP16PV)
+    return fail(SAGE_ERR_UNSUPPORTED, "smooth_v applies to the FP8 P~V variants only");
+  if (r.smooth_q && variant == SAGE_VARIANT_MXFP4QK_FP8PV)
+    return fail(SAGE_ERR_UNSUPPORTED, "the MXFP4 variant quantises Q per token without smoothing (smooth_q must be 0)");
   if (r.q_group == 0) r.q_group = r.blk_q;
   if (!pow2(r.q_group) || r.q_group > r.blk_q)
     return fail(SAGE_ERR_UNSUPPORTED, "q_group must be 0 or a power of two <= blk_q (got %d)", r.q_group);
@@ -95,9 +97,13 @@ int check_ptr(const void* p, size_t align, const char* name) {
 // Variant 0 without Q smoothing quantises Q inside the attention kernel.
 bool fuse_q(int variant, const Params& p) { return variant == 0 && !p.smooth_q; }
 
-// Workspace layout (each piece 256-byte aligned).
+bool valid_variant(int variant) { return variant >= 0 && variant <= 2; }
+
+// Workspace layout (each piece 256-byte aligned).  Variant 2 keeps its packed E2M1
+// codes in q_i8 / k_i8 (d/2 bytes per row) and its E8M0 scales in q_e8 / k_e8.
 struct Layout {
-  size_t ksum, vsum, vmax, vmin, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, v_mean, total;
+  size_t ksum, vsum, vmax, vmin, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, v_mean, q_e8, k_e8,
+      total;
 };
 
 size_t up(size_t x) { return (x + 255) / 256 * 256; }
@@ -108,20 +114,23 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  const bool fp8v = variant != 0, mx = variant == 2;
   L.ksum = take(G * ns * d * sizeof(long long));
-  L.vsum = take(variant == 1 ? G * ns * d * sizeof(long long) : 0);
-  L.vmax = take(variant == 1 ? G * ns * d * sizeof(float) : 0);
-  L.vmin = take(variant == 1 ? G * ns * d * sizeof(float) : 0);
+  L.vsum = take(fp8v ? G * ns * d * sizeof(long long) : 0);
+  L.vmax = take(fp8v ? G * ns * d * sizeof(float) : 0);
+  L.vmin = take(fp8v ? G * ns * d * sizeof(float) : 0);
   const bool fq = fuse_q(variant, p);
-  L.q_i8 = take(fq ? 0 : G * Np * d);
-  L.k_i8 = take(G * Np * d);
-  L.q_scale = take(fq ? 0 : G * nqg * sizeof(float));
-  L.k_scale = take(G * nkb * sizeof(float));
+  L.q_i8 = take(fq ? 0 : G * Np * (mx ? d / 2 : d));
+  L.k_i8 = take(G * Np * (mx ? d / 2 : d));
+  L.q_scale = take(fq || mx ? 0 : G * nqg * sizeof(float));
+  L.k_scale = take(mx ? 0 : G * nkb * sizeof(float));
   L.k_mean = take(G * d * sizeof(float));
   L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
-  L.v_f8 = take(variant == 1 ? G * d * Np : 0);
-  L.v_scale = take(variant == 1 ? G * d * sizeof(float) : 0);
+  L.v_f8 = take(fp8v ? G * d * Np : 0);
+  L.v_scale = take(fp8v ? G * d * sizeof(float) : 0);
   L.v_mean = take(p.smooth_v ? G * d * sizeof(float) : 0);
+  L.q_e8 = take(mx ? G * Np * (d / 32) : 0);
+  L.k_e8 = take(mx ? G * Np * (d / 32) : 0);
   L.total = off;
   return L;
 }
@@ -202,7 +211,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   int rc;
   if ((rc = check_shape(B, H, N, d))) return rc;
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (variant != 0 && variant != 1) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0 or 1");
+  if (!valid_variant(variant)) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0, 1 or 2");
   if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   Params p;
@@ -218,19 +227,28 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   hipError_t e;
   const sage::StatsOut stats{at<long long>(ws, L.ksum), at<long long>(ws, L.vsum), at<float>(ws, L.vmax),
                              at<float>(ws, L.vmin)};
-  if (p.smooth_k || variant == 1) {
-    e = sage::launch_stats(d, k, variant == 1 ? v : nullptr, G, N, stats, st);
+  if (p.smooth_k || variant != 0) {
+    e = sage::launch_stats(d, k, variant != 0 ? v : nullptr, G, N, stats, st);
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
   const bool fq = fuse_q(variant, p);
-  sage::QuantArgs qa = quant_args(q, k, B, H, N, d, p, fq ? nullptr : at<int8_t>(ws, L.q_i8), at<int8_t>(ws, L.k_i8),
-                                  fq ? nullptr : at<float>(ws, L.q_scale), at<float>(ws, L.k_scale),
-                                  at<float>(ws, L.k_mean), p.smooth_q ? at<float>(ws, L.q_mean) : nullptr,
-                                  at<long long>(ws, L.ksum));
-  qa.with_q = fq ? 0 : 1;
-  e = sage::launch_quant(d, qa, st);
-  if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
-  if (variant == 1) {
+  if (variant == 2) {
+    e = sage::launch_quant_mx(d, k, G, N, Np, at<long long>(ws, L.ksum), p.smooth_k, at<uint8_t>(ws, L.k_i8),
+                              at<uint8_t>(ws, L.k_e8), at<float>(ws, L.k_mean), st);
+    if (e == hipSuccess)
+      e = sage::launch_quant_mx(d, q, G, N, Np, nullptr, 0, at<uint8_t>(ws, L.q_i8), at<uint8_t>(ws, L.q_e8), nullptr,
+                                st);
+    if (e != hipSuccess) return hip_fail(e, "MXFP4 quantisation kernel");
+  } else {
+    sage::QuantArgs qa = quant_args(q, k, B, H, N, d, p, fq ? nullptr : at<int8_t>(ws, L.q_i8),
+                                    at<int8_t>(ws, L.k_i8), fq ? nullptr : at<float>(ws, L.q_scale),
+                                    at<float>(ws, L.k_scale), at<float>(ws, L.k_mean),
+                                    p.smooth_q ? at<float>(ws, L.q_mean) : nullptr, at<long long>(ws, L.ksum));
+    qa.with_q = fq ? 0 : 1;
+    e = sage::launch_quant(d, qa, st);
+    if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
+  }
+  if (variant != 0) {
     e = sage::launch_quant_v(d, v, G, N, Np, stats, p.smooth_v, at<uint8_t>(ws, L.v_f8), at<float>(ws, L.v_scale),
                              p.smooth_v ? at<float>(ws, L.v_mean) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
@@ -239,12 +257,14 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   a.q = fq ? (const uint16_t*)q : nullptr;
   a.q_i8 = fq ? nullptr : at<int8_t>(ws, L.q_i8);
   a.k_i8 = at<int8_t>(ws, L.k_i8);
-  a.q_scale = fq ? nullptr : at<float>(ws, L.q_scale);
-  a.k_scale = at<float>(ws, L.k_scale);
+  a.q_scale = fq || variant == 2 ? nullptr : at<float>(ws, L.q_scale);
+  a.k_scale = variant == 2 ? nullptr : at<float>(ws, L.k_scale);
   a.q_mean = p.smooth_q ? at<float>(ws, L.q_mean) : nullptr;
+  a.q_e8 = variant == 2 ? at<uint8_t>(ws, L.q_e8) : nullptr;
+  a.k_e8 = variant == 2 ? at<uint8_t>(ws, L.k_e8) : nullptr;
   a.v = (const uint16_t*)v;
-  a.v_f8 = variant == 1 ? at<uint8_t>(ws, L.v_f8) : nullptr;
-  a.v_scale = variant == 1 ? at<float>(ws, L.v_scale) : nullptr;
+  a.v_f8 = variant != 0 ? at<uint8_t>(ws, L.v_f8) : nullptr;
+  a.v_scale = variant != 0 ? at<float>(ws, L.v_scale) : nullptr;
   a.v_mean = p.smooth_v ? at<float>(ws, L.v_mean) : nullptr;
   a.o = (uint16_t*)o;
   e = sage::launch_attn(d, variant, causal, p.smooth_q, a, st);
@@ -256,17 +276,17 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
 
 extern "C" {
 
-int sage_version(void) { return 300; }
+int sage_version(void) { return 400; }
 
 int sage_pad_len(int N) { return N < 1 ? -1 : pad_len(N); }
 
 int sage_kv_tile(int variant, int d) {
-  if ((variant != 0 && variant != 1) || (d != 64 && d != 128)) return -1;
+  if (!valid_variant(variant) || (d != 64 && d != 128)) return -1;
   return 64;
 }
 
 size_t sage_workspace_bytes(int B, int H, int N, int d, int variant, const sage_params* pp) {
-  if (check_shape(B, H, N, d) || (variant != 0 && variant != 1)) return 0;
+  if (check_shape(B, H, N, d) || !valid_variant(variant)) return 0;
   Params p;
   if (read_params(pp, variant, &p)) return 0;
   return layout(B, H, N, d, variant, p).total;
@@ -337,7 +357,8 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
   int rc;
   if ((rc = check_shape(B, H, N, d))) return rc;
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (variant != 0 && variant != 1) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0 or 1");
+  if (variant != 0 && variant != 1)
+    return fail(SAGE_ERR_INVALID_ARG, "variant must be 0 or 1 (the MXFP4 variant: sage_attn_fwd_prequant_mx)");
   if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   Params p;
@@ -386,6 +407,58 @@ int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, 
   a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o;
   hipError_t e = sage::launch_attn(d, 0, causal, 0, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+int sage_quant_qk_mx(const void* q, const void* k, int B, int H, int N, int d, int smooth_k, uint8_t* q_f4,
+                     uint8_t* k_f4, uint8_t* q_e8, uint8_t* k_e8, float* k_mean, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (smooth_k != 0 && smooth_k != 1) return fail(SAGE_ERR_INVALID_ARG, "smooth_k must be 0 or 1");
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k, 16, "k")) || (rc = check_ptr(q_f4, 16, "q_f4")) ||
+      (rc = check_ptr(k_f4, 16, "k_f4")) || (rc = check_ptr(q_e8, 4, "q_e8")) || (rc = check_ptr(k_e8, 4, "k_e8")))
+    return rc;
+  if (k_mean && !aligned(k_mean, 4)) return fail(SAGE_ERR_INVALID_ARG, "k_mean must be 4-byte aligned");
+  const size_t need = smooth_k ? up((size_t)B * H * ceil_div(N, sage::kStatRows) * d * sizeof(long long)) : 0;
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int G = B * H, Np = pad_len(N);
+  hipError_t e = hipSuccess;
+  if (smooth_k) e = sage::launch_stats(d, k, nullptr, G, N, sage::StatsOut{(long long*)ws, nullptr, nullptr, nullptr}, st);
+  if (e != hipSuccess) return hip_fail(e, "statistics kernel");
+  e = sage::launch_quant_mx(d, k, G, N, Np, (const long long*)ws, smooth_k, k_f4, k_e8, k_mean, st);
+  if (e == hipSuccess) e = sage::launch_quant_mx(d, q, G, N, Np, nullptr, 0, q_f4, q_e8, nullptr, st);
+  if (e != hipSuccess) return hip_fail(e, "MXFP4 quantisation kernel");
+  return ok();
+}
+
+int sage_attn_fwd_prequant_mx(const uint8_t* q_f4, const uint8_t* k_f4, const uint8_t* q_e8, const uint8_t* k_e8,
+                              const uint8_t* v_f8, const float* v_scale, const float* v_mean, void* o, int B, int H,
+                              int N, int d, int causal, float sm_scale, const sage_params* pp, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, SAGE_VARIANT_MXFP4QK_FP8PV, &p))) return rc;
+  if ((rc = check_ptr(q_f4, 16, "q_f4")) || (rc = check_ptr(k_f4, 16, "k_f4")) || (rc = check_ptr(q_e8, 4, "q_e8")) ||
+      (rc = check_ptr(k_e8, 4, "k_e8")) || (rc = check_ptr(v_f8, 16, "v_f8")) ||
+      (rc = check_ptr(v_scale, 16, "v_scale")) || (rc = check_ptr(o, 16, "o")))
+    return rc;
+  if (p.smooth_v && (rc = check_ptr(v_mean, 16, "v_mean (required with smooth_v)"))) return rc;
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
+  a.q_i8 = (const int8_t*)q_f4;
+  a.k_i8 = (const int8_t*)k_f4;
+  a.q_e8 = q_e8;
+  a.k_e8 = k_e8;
+  a.v_f8 = v_f8;
+  a.v_scale = v_scale;
+  a.v_mean = p.smooth_v ? v_mean : nullptr;
+  a.o = (uint16_t*)o;
+  hipError_t e = sage::launch_attn(d, 2, causal, 0, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
 }

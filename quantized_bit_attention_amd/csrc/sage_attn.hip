@@ -42,9 +42,13 @@ constexpr int kDbgWaves = 4;
 // (8 lanes of ds_read_b128, 16 lanes of ds_read_b64_tr_b16) covers one contiguous
 // 128-byte run, which is free of bank conflicts, and every operand address is the
 // lane's base plus a compile-time offset.
+// Bytes per Q / K row: D int8 codes, or D/2 bytes of two E2M1 codes (variant 2).
+template <int D, int VARIANT>
+constexpr int qk_row_bytes() { return VARIANT == 2 ? D / 2 : D; }
+
 template <int D, int VARIANT>
 struct Lds {
-  static constexpr int K_BYTES = kTileKV * D;                     // 64 keys x D int8
+  static constexpr int K_BYTES = kTileKV * qk_row_bytes<D, VARIANT>();  // 64 keys
   static constexpr int V_BYTES = VARIANT == 0 ? kTileKV * D * 2   // 64 keys x D fp16
                                               : D * kTileKV;      // D channels x 64 keys fp8
 };
@@ -82,13 +86,14 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_
 // one base offset per tensor, and tile t adds a uniform t * (bytes per tile).
 template <int D, int VARIANT, int NWAVES>
 struct TileCopy {
-  static constexpr int CPR = D / 16;
+  static constexpr int KD = qk_row_bytes<D, VARIANT>();  // bytes per K row
+  static constexpr int CPR = KD / 16;
   static constexpr int K_COPIES = kTileKV * CPR / 64;                                      // 1 KB each
   static constexpr int V_COPIES = (VARIANT == 0 ? kTileKV * 2 * D : D * kTileKV) / 16 / 64;
   static constexpr int K_PER_WAVE = (K_COPIES + NWAVES - 1) / NWAVES;
   static constexpr int V_PER_WAVE = (V_COPIES + NWAVES - 1) / NWAVES;
   // memory distance between copy c and copy c + NWAVES of a lane (see the layouts above)
-  static constexpr uint32_t K_STEP = (uint32_t)((NWAVES * 2) / CPR) * 32 * D;
+  static constexpr uint32_t K_STEP = (uint32_t)((NWAVES * 2) / CPR) * 32 * KD;
   static constexpr uint32_t V_STEP = VARIANT == 0 ? (uint32_t)(NWAVES * 8 / (D / 16)) * 4 * 2 * D
                                                   : (uint32_t)(NWAVES * 2 / 4) * 32;  // channels (x Np)
   uint32_t koff, voff;
@@ -98,7 +103,7 @@ struct TileCopy {
     {
       const int s = (wave % K_COPIES) * 64 + lane;
       const int x = s & 31, rest = s >> 5;
-      koff = (uint32_t)(32 * (rest / CPR) + k_perm(x)) * D + (rest % CPR) * 16;
+      koff = (uint32_t)(32 * (rest / CPR) + k_perm(x)) * KD + (rest % CPR) * 16;
     }
     {
       const int s = (wave % V_COPIES) * 64 + lane;
@@ -116,15 +121,15 @@ struct TileCopy {
     static_assert(VARIANT == 0 || (NWAVES * 2) % 4 == 0, "V^T copies must step by whole channel rows");
   }
 
-  // K tile t of the padded int8 tensor (resource over this head); the tile and copy
-  // steps go in the scalar offset.
+  // K tile t of the padded int8 / packed-E2M1 tensor (resource over this head); the
+  // tile and copy steps go in the scalar offset.
   __device__ __forceinline__ void k_tile(__amdgpu_buffer_rsrc_t krs, int t, int8_t* sK) const {
     const int wave = wave_id();
 #pragma unroll
     for (int i = 0; i < K_PER_WAVE; ++i) {
       const int c = i * NWAVES + wave;
       if (K_COPIES % NWAVES == 0 || c < K_COPIES)
-        copy16_to_lds(krs, koff, (uint32_t)(t * kTileKV * D) + i * K_STEP, sK + c * 1024);
+        copy16_to_lds(krs, koff, (uint32_t)(t * kTileKV * KD) + i * K_STEP, sK + c * 1024);
     }
   }
   // V tile t.  Variant 0 puts the whole offset in the lane offset so keys >= N fall
@@ -179,6 +184,48 @@ __device__ __forceinline__ void qk_tile(const int8_t* sK, const int8_t* sQw, int
   s[1] = acc[1];
 }
 
+// S^T tile with MXFP4 operands (variant 2).  The K and Q tiles hold two E2M1 codes
+// per byte in the int8 layout of D/2 byte columns, so the operand reads are those of
+// qk_tile; the 32 codes a lane brings to a 64-channel k-step are one MX block.  Byte ks
+// of ksw[st] is the E8M0 scale of that block of the lane's key, byte ks of qsw the one
+// of its query (v_mfma_scale_f32_32x32x64_f8f6f4, formats E2M1 x E2M1, fp32 result).
+template <int D>
+__device__ __forceinline__ void qk_tile_mx(const int8_t* sK, const int8_t* sQw, int lane, const uint32_t* ksw,
+                                           uint32_t qsw, f32x16* s) {
+  constexpr int CPR = D / 32;  // 16-byte chunks per row of D/2 bytes
+  const int8_t* kbase = sK + 16 * lane;
+  const int8_t* qbase = sQw + 16 * lane;
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  auto step = [&](auto ksc) {
+    constexpr int ks = decltype(ksc)::value;
+    const i32x4 q4 = *reinterpret_cast<const i32x4*>(qbase + ks * 1024);
+    const i32x8 qop = __builtin_shufflevector(q4, q4, 0, 1, 2, 3, -1, -1, -1, -1);  // FP4 uses 4 registers
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const i32x4 k4 = *reinterpret_cast<const i32x4*>(kbase + (st * CPR + 2 * ks) * 512);
+      const i32x8 kop = __builtin_shufflevector(k4, k4, 0, 1, 2, 3, -1, -1, -1, -1);
+      acc[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop, acc[st], 4, 4, ks, (int)ksw[st], ks,
+                                                               (int)qsw);
+    }
+  };
+  step(std::integral_constant<int, 0>{});
+  if constexpr (D == 128) step(std::integral_constant<int, 1>{});
+  s[0] = acc[0];
+  s[1] = acc[1];
+}
+
+// The MX scale bytes a lane brings to its k-steps, from a token's D/32 scale bytes
+// (byte ks = block 2*ks + h).
+template <int D>
+__device__ __forceinline__ uint32_t mx_lane_scales(const uint8_t* e8_row, int h) {
+  if constexpr (D == 128) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(e8_row);
+    return __builtin_amdgcn_perm(w, w, h ? 0x0c0c0301u : 0x0c0c0200u);
+  } else {
+    return (uint32_t)e8_row[h];
+  }
+}
+
 // 16 bytes of key `key`, chunk `chunk16`, of the K tile.
 template <int D>
 __device__ __forceinline__ const int8_t* k_lds_chunk(const int8_t* sK, int key, int chunk16) {
@@ -200,8 +247,8 @@ constexpr float kLazyLog2 = 8.0f;
 // alpha is the factor the running O must be scaled by (rescale is false for the whole
 // wave when no lane needs it).
 // MASK: keys >= N, and keys > qi when causal, get P~ = 0 and stay out of the max.
-template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK>
-__device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, const float* bias, int kl, int N,
+template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, typename SV>
+__device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const float* bias, int kl, int N,
                                              int qi, float& m, float& l, uint32_t* pk, float& alpha,
                                              bool& rescale) {
   auto keep = [&](int st, int i) {
@@ -219,6 +266,16 @@ __device__ __forceinline__ void softmax_tile(const i32x16* s, const float* c, co
         x[st][i] = fmaf((float)s[st][i], c[st], bias[32 * st + i]);
         mt = keep(st, i) ? fmaxf(mt, x[st][i]) : mt;
       }
+  } else if constexpr (VARIANT == 2) {
+    // fp32 scores (MXFP4); c > 0, so max_j fl(c * S_j) = fl(c * max_j S_j)
+    float mf[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      mf[st] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mf[st] = keep(st, i) ? fmaxf(mf[st], s[st][i]) : mf[st];
+    }
+    mt = fmaxf(c[0] * mf[0], c[1] * mf[1]);
   } else {
     // c >= 0, so max_j fl(c * S_j) = fl(c * max_j S_j): the max is taken on the integers
     int mi[2];
@@ -361,14 +418,22 @@ __device__ __forceinline__ void smooth_q_bias(const int8_t* sK, const int8_t* sQ
 // is followed by the LDS reads for the next one and a share of the softmax's VALU
 // instructions, which execute while the MFMA occupies the matrix unit.  (Written as
 // loops without conditionals: a guarded sched_group_barrier is not honoured.)
+#ifndef V2P128
+#define V2P128 12
+#endif
+#ifndef V2P64
+#define V2P64 24
+#endif
 template <int D, int VARIANT, bool SMOOTHQ>
 __device__ __forceinline__ void interleave_schedule() {
   // every MFMA takes two LDS operand reads (K and Q, two V transposes, or two V^T
   // halves); they are issued LEAD MFMAs ahead of their use, so the LDS latency (about
   // 200 cycles) overlaps the MFMAs and VALU work in between
   constexpr int LEAD = 2;
-  constexpr int MFMA = 2 * (D / 32) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
-  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13) : (D == 128 ? 8 : 14);
+  constexpr int MFMA = (VARIANT == 2 ? 2 * (D / 64) : 2 * (D / 32)) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
+  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13)
+                           : VARIANT == 1 ? (D == 128 ? 8 : 14)
+                                          : (D == 128 ? V2P128 : V2P64);
   // with Q smoothing the softmax first reads its 32 biases (8 reads of 16 bytes)
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD + (SMOOTHQ ? 8 : 0), 0);
 #pragma unroll
@@ -385,7 +450,9 @@ __device__ __forceinline__ void interleave_schedule() {
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   static_assert(!FUSEQ || (VARIANT == 0 && !SMOOTHQ), "in-kernel Q quantisation: variant 0, no Q smoothing");
+  static_assert(VARIANT != 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
+  constexpr int KD = qk_row_bytes<D, VARIANT>();  // bytes per Q / K row
   constexpr int NCT = D / 32;                       // 32-channel output tiles
   constexpr int NSUB = SMOOTHQ ? kAttnRows / 32 : 1;  // Q blocks a workgroup can span (blk_q >= 32)
   // Two slots per tile kind, as separate LDS objects: the loop body is instantiated
@@ -395,7 +462,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) int8_t sK1[L::K_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sV0[L::V_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sV1[L::V_BYTES];
-  __shared__ __attribute__((aligned(16))) int8_t sQ[kAttnRows * D];
+  __shared__ __attribute__((aligned(16))) int8_t sQ[kAttnRows * KD];
   __shared__ __attribute__((aligned(16))) int8_t sQl[SMOOTHQ ? 16 * D : 1];  // limbs of the Q block means
   __shared__ float sQs[SMOOTHQ ? NSUB : 1];                                   // their scales
   __shared__ __attribute__((aligned(16))) float sBias0[SMOOTHQ ? NSUB * kTileKV : 1];
@@ -420,16 +487,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const int qi = qw + ql;         // this lane's query row
   const bool wave_active = qw < N;
 
-  const int8_t* __restrict__ qh = FUSEQ ? nullptr : a.q_i8 + (size_t)g * a.Np * D;
-  const int8_t* __restrict__ kh = a.k_i8 + (size_t)g * a.Np * D;
-  const float* __restrict__ ksc = a.k_scale + (size_t)g * a.nkb;
+  const int8_t* __restrict__ qh = FUSEQ ? nullptr : a.q_i8 + (size_t)g * a.Np * KD;
+  const int8_t* __restrict__ kh = a.k_i8 + (size_t)g * a.Np * KD;
+  const float* __restrict__ ksc = VARIANT == 2 ? nullptr : a.k_scale + (size_t)g * a.nkb;
 
   const int ntiles_all = (N + kTileKV - 1) / kTileKV;
   const int wg_last_row = min(q0 + kAttnRows - 1, N - 1);
   const int T = CAUSAL ? min(ntiles_all, wg_last_row / kTileKV + 1) : ntiles_all;
   const int wave_last = CAUSAL ? min(ntiles_all - 1, min(qw + 31, N - 1) / kTileKV) : ntiles_all - 1;
 
-  int8_t* const sQw = sQ + wave * (D / 32) * 1024;
+  int8_t* const sQw = sQ + wave * (KD / 32) * 1024;
   // FUSEQ: lane l holds fp16 Q of row qw + l%32, channels 32*ks + 16*h .. +15 in
   // qraw[2ks], qraw[2ks+1] (the bytes its operand read takes); rows >= N are zeros
   uint4 qraw[FUSEQ ? D / 16 : 1];
@@ -443,14 +510,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
         qraw[2 * ks + j] = row_ok ? *reinterpret_cast<const uint4*>(qsrc + 32 * ks + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
   } else {
     // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
-    if (wave_active) load_q_tile<D>(make_rsrc(qh, (size_t)a.Np * D), qw, sQw);
+    if (wave_active) load_q_tile<KD>(make_rsrc(qh, (size_t)a.Np * KD), qw, sQw);
   }
   // block and group sizes are powers of two
   const int kshift = __builtin_ctz(a.blk_k), qshift = __builtin_ctz(a.blk_q);
   // Q scale of this lane's row: one per group of q_group rows, so uniform over the wave
   // for groups of 32 rows or more (FUSEQ: set once the group's |Q| max is known)
-  float dq = (!FUSEQ && wave_active) ? a.q_scale[(size_t)g * a.nqg + (min(qi, N - 1) >> __builtin_ctz(a.q_group))]
-                                     : 0.0f;
+  float dq = (!FUSEQ && VARIANT != 2 && wave_active)
+                 ? a.q_scale[(size_t)g * a.nqg + (min(qi, N - 1) >> __builtin_ctz(a.q_group))]
+                 : 0.0f;
+  // variant 2: the MX scale bytes of this lane's query (rows >= N hold zeros)
+  uint32_t qsw = 0;
+  if constexpr (VARIANT == 2) {
+    if (wave_active) qsw = mx_lane_scales<D>(a.q_e8 + ((size_t)g * a.Np + qi) * (D / 32), h);
+  }
 
   if constexpr (SMOOTHQ) {
     // wave sb splits the mean of the workgroup's Q block sb (up to 4 blocks; the others
@@ -473,7 +546,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // V(t+1) into the slot of V(t-1) right after the barrier that ends iteration t; the
   // barrier also waits for the copies started before it.
   const TileCopy<D, VARIANT, kAttnWaves> copy(a.Np);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (size_t)a.Np * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (size_t)a.Np * KD);
   const __amdgpu_buffer_rsrc_t vrs = VARIANT == 0 ? make_rsrc(a.v + (size_t)g * N * D, (size_t)N * D * 2)
                                                   : make_rsrc(a.v_f8 + (size_t)g * D * a.Np, (size_t)D * a.Np);
 
@@ -536,22 +609,48 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // scale factors c = dQ * dK * sm_scale * log2(e); the raw K scales of a tile are
   // loaded one iteration before they are needed.  S, c and packed P~ alternate
   // between two register sets by tile parity.
+  // (variant 2: S is fp32 from the scaled MFMA, c = sm_scale * log2(e), and kw holds
+  // the MX scale bytes of this lane's key in each 32-key block of tile t+1)
   constexpr int NPK = VARIANT == 0 ? 16 : 8;
-  i32x16 sA[2], sB[2];
+  using SAcc = std::conditional_t<VARIANT == 2, f32x16, i32x16>;
+  SAcc sA[2], sB[2];
   float cA[2], cB[2], kq[4];  // kq: raw K scales of tile t+1 (see tile_kscales)
+  uint32_t kw[2];
   const unsigned last_key = (unsigned)(N - 1);
   uint32_t pkA[NPK], pkB[NPK];
 #pragma unroll
   for (int i = 0; i < NPK; ++i) pkB[i] = 0u;  // P~(-1)
   const float dqs = dq * a.kscale;
-  if (wave_active) {  // tile 0 is visible to every row
-    qk_tile<D>(sK0, sQw, lane, sA);
+  // MX scale bytes of the keys this lane's A-operand rows hold in tile t (clamped into
+  // the padded tensor; the pad rows carry zeros)
+  auto mx_kscales = [&](int t, uint32_t* w) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int key = min(t * kTileKV + 32 * st + k_perm(ql), a.Np - 1);
+      w[st] = mx_lane_scales<D>(a.k_e8 + ((size_t)g * a.Np + key) * (D / 32), h);
+    }
+  };
+  // S(t) for the K tile in sKt
+  auto score_tile = [&](const int8_t* sKt, SAcc* out) {
+    if constexpr (VARIANT == 2)
+      qk_tile_mx<D>(sKt, sQw, lane, kw, qsw, out);
+    else
+      qk_tile<D>(sKt, sQw, lane, out);
+  };
+  if constexpr (VARIANT == 2) {
+    mx_kscales(0, kw);
+    if (wave_active) score_tile(sK0, sA);  // tile 0 is visible to every row
+    cA[0] = cA[1] = a.kscale;
+    mx_kscales(1, kw);
+  } else {
+    if (wave_active) score_tile(sK0, sA);  // tile 0 is visible to every row
+    tile_kscales(ksc, 0, last_key, kshift, kq);
+    cA[0] = dqs * kscale_of(kq, 0, h);
+    cA[1] = dqs * kscale_of(kq, 1, h);
+    if (SMOOTHQ)
+      smooth_q_bias<D>(sK0, sQl, sQs, a.kscale * kscale_quarter(ksc, 0, wave_id(), last_key, kshift), sBias0);
+    tile_kscales(ksc, 1, last_key, kshift, kq);
   }
-  tile_kscales(ksc, 0, last_key, kshift, kq);
-  cA[0] = dqs * kscale_of(kq, 0, h);
-  cA[1] = dqs * kscale_of(kq, 1, h);
-  if (SMOOTHQ) smooth_q_bias<D>(sK0, sQl, sQs, a.kscale * kscale_quarter(ksc, 0, wave_id(), last_key, kshift), sBias0);
-  tile_kscales(ksc, 1, last_key, kshift, kq);
   __syncthreads();
   // V(1) is copied by iteration 0, after its barrier.  Nothing is in flight when the
   // loop starts, so the compiler sees no pending copy into a slot the loop reads.
@@ -605,8 +704,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     uint8_t* const sVp = cur == 0 ? sV1 : sV0;        // V(t-1), refilled with V(t+1)
     const float* const sBc = cur == 0 ? sBias0 : sBias1;
     float* const sBn = cur == 0 ? sBias1 : sBias0;
-    i32x16* const s = cur == 0 ? sA : sB;             // S(t)
-    i32x16* const sn = cur == 0 ? sB : sA;            // S(t+1)
+    SAcc* const s = cur == 0 ? sA : sB;               // S(t)
+    SAcc* const sn = cur == 0 ? sB : sA;              // S(t+1)
     float* const c = cur == 0 ? cA : cB;
     float* const cn = cur == 0 ? cB : cA;
     uint32_t* const pk = cur == 0 ? pkA : pkB;        // P~(t)
@@ -619,8 +718,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     const bool pv_prev = wave_active && t - 1 <= wave_last;
     const bool full = (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw);
 
-    cn[0] = dqs * kscale_of(kq, 0, h);                                   // tile t+1
-    cn[1] = dqs * kscale_of(kq, 1, h);
+    if constexpr (VARIANT == 2) {
+      cn[0] = cn[1] = a.kscale;
+    } else {
+      cn[0] = dqs * kscale_of(kq, 0, h);  // tile t+1
+      cn[1] = dqs * kscale_of(kq, 1, h);
+    }
     if (t + 2 < T) copy.k_tile(krs, t + 2, sKc);
     if (SMOOTHQ && t + 1 < T)
       smooth_q_bias<D>(sKn, sQl, sQs, a.kscale * kscale_quarter(ksc, t + 1, wave_id(), last_key, kshift), sBn);
@@ -632,19 +735,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     if (compute && compute_next && pv_prev && full) {
       // Interior tile: one basic block, MFMA work (S(t+1), P~(t-1) V(t-1)) interleaved
       // with the softmax of tile t so the matrix and vector units run together.
-      if constexpr (VARIANT == 1) {
-        // the O update of the two-level accumulation follows each P~V MFMA: issuing
-        // those MFMAs first lets the updates overlap the score MFMAs
+      if constexpr (VARIANT != 0) {
         pv_tile(sVp, pkp);
-        qk_tile<D>(sKn, sQw, lane, sn);
+        score_tile(sKn, sn);
       } else {
-        qk_tile<D>(sKn, sQw, lane, sn);
+        score_tile(sKn, sn);
         pv_tile(sVp, pkp);
       }
       softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
       interleave_schedule<D, VARIANT, SMOOTHQ>();
     } else {
-      if (compute_next) qk_tile<D>(sKn, sQw, lane, sn);
+      if (compute_next) score_tile(sKn, sn);
       if (pv_prev) pv_tile(sVp, pkp);
       if (compute) {
         if (full)
@@ -660,7 +761,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
 
     // K scales of tile t+2 for the next iteration: issued here, their latency overlaps
     // the barrier
-    tile_kscales(ksc, t + 2, last_key, kshift, kq);
+    if constexpr (VARIANT == 2)
+      mx_kscales(t + 2, kw);
+    else
+      tile_kscales(ksc, t + 2, last_key, kshift, kq);
     if (t < T) {
       wait_copies();
       __syncthreads();
@@ -686,7 +790,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       float y[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) y[b] = o[ct][4 * a4 + b] * inv;
-      if (VARIANT == 1) {
+      if (VARIANT != 0) {
         const float4 dv = *reinterpret_cast<const float4*>(a.v_scale + (size_t)g * D + c0);
         y[0] *= dv.x; y[1] *= dv.y; y[2] *= dv.z; y[3] *= dv.w;
         if (a.v_mean) {  // V smoothing: every row of P~ sums to one after the division by l
@@ -755,6 +859,11 @@ hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnA
     if (variant != 0 || smooth_q) return hipErrorInvalidValue;
     if (d == 64) return causal ? launch_one<64, 0, true, false, true>(a, st) : launch_one<64, 0, false, false, true>(a, st);
     return causal ? launch_one<128, 0, true, false, true>(a, st) : launch_one<128, 0, false, false, true>(a, st);
+  }
+  if (variant == 2) {  // MXFP4 scores, never with Q smoothing
+    if (smooth_q) return hipErrorInvalidValue;
+    if (d == 64) return causal ? launch_one<64, 2, true, false>(a, st) : launch_one<64, 2, false, false>(a, st);
+    return causal ? launch_one<128, 2, true, false>(a, st) : launch_one<128, 2, false, false>(a, st);
   }
   if (d == 64)
     return variant == 0 ? launch_dv<64, 0>(causal, smooth_q, a, st) : launch_dv<64, 1>(causal, smooth_q, a, st);

@@ -31,7 +31,9 @@ struct AttnArgs {
   const uint16_t* v;      // [G][N][D] fp16 (variant 0)
   const uint8_t* v_f8;    // [G][D][Np] (variant 1)
   const float* v_scale;   // [G][D] (variant 1)
-  const float* v_mean;    // [G][D] (variant 1 with V smoothing) or null
+  const float* v_mean;    // [G][D] (variants 1, 2 with V smoothing) or null
+  const uint8_t* q_e8;    // [G][Np][D/32] MX block scales (variant 2; q_i8 / k_i8 then
+  const uint8_t* k_e8;    //  hold [G][Np][D/2] bytes of two E2M1 codes each)
   uint16_t* o;            // [G][N][D] fp16
   int G, N, Np, blk_q, blk_k, nqb, nkb;
   int q_group, nqg;       // rows per Q scale (a power of two dividing blk_q), scales per head
@@ -54,6 +56,10 @@ hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, const
 hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st);
 hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
                           uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st);
+// Variant 2: per-token MXFP4 of x (Q, or K with smooth = 1 and the statistics pass's
+// sums): codes [G][Np][D/2] (two E2M1 per byte), e8 [G][Np][D/32]; rows >= N zero.
+hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const long long* ksum_part, int smooth,
+                           uint8_t* codes, uint8_t* e8, float* k_mean, hipStream_t st);
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st);
 hipError_t launch_debug_qk(int d, const int8_t* q_i8, const int8_t* k_i8, int G, int Np, const int* tiles,
                            int n_tiles, int32_t* s_out, hipStream_t st);

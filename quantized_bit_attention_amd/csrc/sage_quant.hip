@@ -427,6 +427,86 @@ hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st) {
   return d == 64 ? launch_quant_d<64>(a, st) : launch_quant_d<128>(a, st);
 }
 
+// ---------------------------------------------------------------------------
+// Variant 2: Q and K' to MXFP4 per token (OCP microscaling: blocks of 32 channels,
+// one E8M0 scale each, E2M1 elements).  One thread per (token, block): it reads the
+// block's 32 fp16 values, subtracts K's token mean (smooth_k), and writes 16 bytes of
+// codes (two per byte, the lower channel in the low nibble) and one scale byte.
+
+// E2M1 code of a value already divided by its block scale: round to nearest with
+// ties to the even code (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4), saturating at 6; the sign bit is kept (also of zero).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_mx_kernel(const uint16_t* __restrict__ x, int N, int Np,
+                                                            int nsplit, const long long* __restrict__ ksum_part,
+                                                            int smooth, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ e8, float* __restrict__ k_mean) {
+  constexpr int BPT = D / 32;             // blocks per token
+  constexpr int TOK = kThreads / BPT;     // tokens per workgroup
+  __shared__ float s_mean[D];
+  const int g = blockIdx.y, tid = threadIdx.x;
+  if (tid < D) {
+    float m = 0.0f;
+    if (smooth) {
+      m = fixed24_mean(ksum_part[(size_t)g * nsplit * D + tid], N);  // folded into split 0
+      if (blockIdx.x == 0 && k_mean) k_mean[(size_t)g * D + tid] = m;
+    }
+    s_mean[tid] = m;
+  }
+  __syncthreads();
+  const int t = blockIdx.x * TOK + tid / BPT, b = tid % BPT;
+  if (t >= Np) return;
+  uint4 packed = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t scode = 0;
+  if (t < N) {
+    const uint16_t* src = x + ((size_t)g * N + t) * D + 32 * b;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * i);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 hv = __builtin_bit_cast(f16x2, w[j]);
+        v[8 * i + 2 * j] = (float)hv[0] - s_mean[32 * b + 8 * i + 2 * j];
+        v[8 * i + 2 * j + 1] = (float)hv[1] - s_mean[32 * b + 8 * i + 2 * j + 1];
+      }
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+    // shared exponent floor(log2 am) - 2 as an E8M0 code; frexp_exp(am) = floor(log2 am) + 1
+    scode = am > 0.0f ? (uint32_t)min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0u;
+    const int sh = 127 - (int)scode;  // elements are v * 2^sh, exact
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) word[i / 8] |= e2m1_code(__builtin_amdgcn_ldexpf(v[i], sh)) << (4 * (i % 8));
+    packed = make_uint4(word[0], word[1], word[2], word[3]);
+  }
+  *reinterpret_cast<uint4*>(codes + ((size_t)g * Np + t) * (D / 2) + 16 * b) = packed;
+  e8[((size_t)g * Np + t) * BPT + b] = (uint8_t)scode;
+}
+
+hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const long long* ksum_part, int smooth,
+                           uint8_t* codes, uint8_t* e8, float* k_mean, hipStream_t st) {
+  const int ns = stat_splits(N);
+  if (d == 64) {
+    dim3 grid(Np / (kThreads / 2), G);
+    quant_mx_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)x, N, Np, ns, ksum_part, smooth, codes, e8, k_mean);
+  } else {
+    dim3 grid(Np / (kThreads / 4), G);
+    quant_mx_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)x, N, Np, ns, ksum_part, smooth, codes, e8, k_mean);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
                           uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st) {
   dim3 grid(Np / 64, G);

@@ -135,6 +135,46 @@ def test_quant_qk_q_group_bitexact(sage, orc, cfg, shape, blk_q, blk_k, q_group,
         assert same, key
 
 
+def pack_e2m1(codes):
+    """Two codes per byte, the lower channel in the low nibble (the GPU layout)."""
+    c = codes.astype(np.uint8)
+    return c[..., 0::2] | (c[..., 1::2] << 4)
+
+
+MX_QUANT = [
+    # recipe cfg, shape overrides, smooth_k
+    (5, dict(N=1000, B=1, H=2), 1),
+    (1, dict(N=333, B=1, H=3), 1),
+    (3, dict(N=200, B=1, H=2), 1),     # outlier K channels
+    (2, dict(N=129, B=2, H=1), 0),
+]
+
+
+@pytest.mark.parametrize("cfg,shape,smooth_k", MX_QUANT)
+def test_quant_mx_bitexact(sage, orc, cfg, shape, smooth_k):
+    """Per-token MXFP4 of Q and K': E2M1 codes, E8M0 scales and k_mean bit-exact.  Q carries
+    an all-zero block, a power-of-two maximum and values that saturate at 6."""
+    c = workloads.make_inputs(cfg, **shape)
+    q = c["q"].copy()
+    q[0, 0, 3, :32] = 0
+    q[0, 0, 4, 7] = 8.0
+    q[0, 0, 5, 0] = -7.99
+    q[0, 0, 6, :] = -0.0
+    say(f"quant_mx {q.shape} smooth_k={smooth_k}")
+    g = sage.quant_qk_mx(dev(q), dev(c["k"]), smooth_k=bool(smooth_k))
+    g = {k: host(v) for k, v in g.items()}
+    r = orc.quant_mx(q, c["k"], smooth_k=smooth_k)
+    for name in ("q", "k"):
+        want_f4 = pack_e2m1(r[f"{name}_codes"])
+        for key, want in ((f"{name}_f4", want_f4), (f"{name}_e8", r[f"{name}_e8"])):
+            same = np.array_equal(g[key], want)
+            if not same:
+                bad = np.nonzero(g[key] != want)
+                say(f"  {key}: {len(bad[0])} mismatches, first at {[b[0] for b in bad]}")
+            assert same, key
+    assert np.array_equal(g["k_mean"].view(np.uint32), r["k_mean"].view(np.uint32))
+
+
 @pytest.mark.parametrize("smooth_v", [0, 1])
 @pytest.mark.parametrize("case", ["cfg5", "ragged_d64", "ties", "offset", "const_channels"])
 def test_quant_v_bitexact(sage, orc, case, smooth_v):
@@ -278,6 +318,14 @@ EDGE = [
     ("qg2_v0_smoothq", 2, dict(N=256, B=1, H=2), dict(causal=1, variant=0, smooth_q=1, q_group=2)),
     ("qg8_v1_smoothqv_d64", 1, dict(N=257, B=1, H=2), dict(causal=0, variant=1, blk_q=32, q_group=8,
                                                            smooth_v=1)),
+    # MXFP4 scores (variant 2)
+    ("mx_n1_causal", 5, dict(N=1, B=1, H=1), dict(causal=1, variant=2, smooth_q=0)),
+    ("mx_n17_d64", 1, dict(N=17, B=1, H=2), dict(causal=0, variant=2, smooth_q=0)),
+    ("mx_n129_causal_d128", 2, dict(N=129, B=2, H=1), dict(causal=1, variant=2, smooth_q=0)),
+    ("mx_n333_causal_d128", 5, dict(N=333, B=1, H=2), dict(causal=1, variant=2, smooth_q=0)),
+    ("mx_n200_d64", 3, dict(N=200, B=1, H=2), dict(causal=0, variant=2, smooth_q=0)),
+    ("mx_nosmoothk", 1, dict(N=256, B=1, H=2), dict(causal=1, variant=2, smooth_q=0, smooth_k=0)),
+    ("mx_smoothv", 5, dict(N=300, B=1, H=2), dict(causal=0, variant=2, smooth_q=0, smooth_v=1)),
 ]
 
 
@@ -303,6 +351,39 @@ def test_attn_q_offset_stress_variant1(sage, orc):
     g = run_gpu(sage, c)
     o = orc.attn(c["q"], c["k"], c["v"], **oracle_kw(c))
     check_o("q_offset_v1", g, o)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_attn_full_size_mxfp4_sampled_rows(sage, orc, cfg):
+    """The MXFP4 variant on each workload's full shape (sampled rows)."""
+    c = dict(inputs(cfg))
+    c.update(variant=2, smooth_q=0)
+    B, H, N, d = c["q"].shape
+    G = B * H
+    say(f"attn mxfp4 cfg{cfg} full size {c['q'].shape} causal={c['causal']}")
+    g = run_gpu(sage, c).reshape(G, N, d)
+    rng = np.random.default_rng(300 + cfg)
+    heads, rows = [], []
+    for hd in (0, G // 2 + 1, G - 1):
+        for r in sample_rows(N, c["causal"], rng):
+            heads.append(hd)
+            rows.append(r)
+    o = orc.attn_rows(c["q"], c["k"], c["v"], heads, rows, **oracle_kw(c))
+    check_o(f"mxfp4 cfg{cfg} sampled {len(rows)} rows", g[heads, rows], o)
+
+
+def test_prequant_mx_matches_whole_call(sage):
+    c = workloads.make_inputs(5, N=1000, B=1, H=2, v_sigma=1.0)
+    say("prequant_mx vs whole call, with V smoothing")
+    q, k, v = dev(c["q"]), dev(c["k"]), dev(c["v"])
+    N = c["q"].shape[2]
+    whole = sage.attn(q, k, v, causal=True, variant=2, smooth_q=False, smooth_v=True)
+    qk = sage.quant_qk_mx(q, k)
+    vq = sage.quant_v(v, smooth_v=True)
+    pre = sage.attn_prequant_mx(qk, vq, N, causal=True, smooth_v=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(whole.float()).all()
+    assert torch.equal(whole, pre)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])

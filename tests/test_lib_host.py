@@ -50,7 +50,8 @@ def test_pure_helpers(lib):
     assert lib.sage_pad_len(1) == 128 and lib.sage_pad_len(128) == 128 and lib.sage_pad_len(17776) == 17792
     assert lib.sage_pad_len(0) == -1
     assert lib.sage_kv_tile(0, 64) == 64 and lib.sage_kv_tile(1, 128) == 64
-    assert lib.sage_kv_tile(2, 64) < 0 and lib.sage_kv_tile(0, 96) < 0
+    assert lib.sage_kv_tile(2, 64) == 64
+    assert lib.sage_kv_tile(3, 64) < 0 and lib.sage_kv_tile(0, 96) < 0
     assert lib.sage_version() >= 100
 
 
@@ -74,6 +75,12 @@ def test_workspace_size(lib):
     assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True, q_group=1) == (
         sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) - up(G * 32 * 4) + up(G * N * 4))
     assert sage.workspace_bytes(B, H, N, d, 0, q_group=3) == 0
+    # MXFP4 variant: K and V statistics, packed E2M1 Q/K (d/2 bytes per row), their E8M0
+    # scales (d/32 per row), k_mean, FP8 V and its scales
+    ns = N // 256
+    v2 = (up(G * ns * d * 8) * 2 + up(G * ns * d * 4) * 2 + 2 * up(G * Np * d // 2) + up(G * d * 4)
+          + up(G * d * Np) + up(G * d * 4) + 2 * up(G * Np * d // 32))
+    assert sage.workspace_bytes(B, H, N, d, 2) == v2
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
     assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
 
@@ -92,7 +99,7 @@ def attn(lib, q=A, k=A, v=A, o=A, B=1, H=1, N=64, d=64, causal=0, sm=0.125, vari
     (dict(B=0), -1, "B, H, N"),
     (dict(B=1 << 12, H=1 << 8, N=1 << 10, d=128), -1, "2^31"),
     (dict(causal=2), -1, "causal"),
-    (dict(variant=2), -1, "variant"),
+    (dict(variant=3), -1, "variant"),
     (dict(sm=0.0), -1, "sm_scale"),
     (dict(sm=float("nan")), -1, "sm_scale"),
     (dict(sm=float("inf")), -1, "sm_scale"),
@@ -179,6 +186,28 @@ def test_other_entry_points_reject(lib):
     assert rc == -1 and b"k_i8 is NULL" in lib.sage_last_error()
     rc = lib.sage_attn_fwd_qf16(A, A, A, A, A, 1, 1, 64, 96, 0, 0.125, None, None)
     assert rc == -2
+
+
+def test_mxfp4_entry_points_reject(lib):
+    # Q smoothing is not part of the MXFP4 variant
+    p = sage._params(smooth_q=True)
+    assert attn(lib, params=p, variant=2) == -2 and b"smooth_q" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_prequant_mx(A, A, A, A, A, A, None, A, 1, 1, 64, 64, 0, 0.125, ctypes.byref(p), None)
+    assert rc == -2
+    rc = lib.sage_attn_fwd_prequant_mx(A, A, A, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, None, None)
+    assert rc == -1 and b"k_e8 is NULL" in lib.sage_last_error()
+    p = sage._params(smooth_v=True)
+    rc = lib.sage_attn_fwd_prequant_mx(A, A, A, A, A, A, None, A, 1, 1, 64, 64, 0, 0.125, ctypes.byref(p), None)
+    assert rc == -1 and b"v_mean" in lib.sage_last_error()
+    rc = lib.sage_quant_qk_mx(A, A, 1, 1, 64, 64, 2, A, A, A, A, None, A, 1 << 20, None)
+    assert rc == -1 and b"smooth_k" in lib.sage_last_error()
+    rc = lib.sage_quant_qk_mx(A, A, 1, 1, 64, 96, 1, A, A, A, A, None, A, 1 << 20, None)
+    assert rc == -2
+    rc = lib.sage_quant_qk_mx(A, A, 1, 1, 64, 64, 1, A, A, A, A, None, None, 0, None)
+    assert rc == -3
+    # the pre-quantised int8 entry point points MXFP4 callers to their own
+    rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, 2, None, None)
+    assert rc == -1 and b"prequant_mx" in lib.sage_last_error()
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
