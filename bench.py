@@ -123,8 +123,8 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
 
     # the attention kernel alone, as the step launches it (same stream, same launch
-    # configuration): variant 0 quantises Q inside the kernel, variant 1 reads the
-    # pre-quantised Q and FP8 V
+    # configuration): variants 0 and 2 quantise Q inside the kernel, variant 1 reads the
+    # pre-quantised Q; variants 1 and 2 read the FP8 V
     if variant == 2:
         qk = sage.quant_qk_mx(q, k)
     else:
@@ -132,7 +132,7 @@ def main():
     vq = sage.quant_v(v, smooth_v=smooth_v) if variant != 0 else None
     if variant == 2:
         def kernel():
-            sage.attn_prequant_mx(qk, vq, N, causal=bool(causal), smooth_v=smooth_v, out=out)
+            sage.attn_qf16_mx(q, qk, vq, causal=bool(causal), smooth_v=smooth_v, out=out)
     elif variant == 0:
         def kernel():
             sage.attn_qf16(q, qk, v, out=out, causal=bool(causal), blk_q=cfg["blk_q"], blk_k=cfg["blk_k"],

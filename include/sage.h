@@ -185,6 +185,16 @@ int sage_attn_fwd_prequant_mx(const uint8_t* q_f4, const uint8_t* k_f4, const ui
                               float sm_scale, const sage_params* p, void* stream);
 
 /*
+ * The attention kernel that sage_attn_fwd runs for the MXFP4 variant: Q is fp16 and
+ * each workgroup quantises its rows to MXFP4 in its prologue (the sage_quant_qk_mx rule,
+ * same codes and scales); K comes from sage_quant_qk_mx, V from sage_quant_v(_ex).
+ * Used to time the fused kernel by itself.
+ */
+int sage_attn_fwd_qf16_mx(const void* q, const uint8_t* k_f4, const uint8_t* k_e8, const uint8_t* v_f8,
+                          const float* v_scale, const float* v_mean, void* o, int B, int H, int N, int d,
+                          int causal, float sm_scale, const sage_params* p, void* stream);
+
+/*
  * The attention kernel that sage_attn_fwd runs for variant 0 without Q smoothing: Q
  * is fp16 and each workgroup quantises its own rows per block of blk_q tokens (the
  * sage_quant_qk rule above, same codes and scales); K comes pre-quantised from

@@ -18,6 +18,7 @@ import os
 import torch
 
 __all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
+           "attn_qf16_mx",
            "debug_qk_int32", "workspace_bytes",
            "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4"]
 
@@ -68,6 +69,7 @@ def _load():
         "sage_attn_fwd_qf16": ([P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_quant_qk_mx": ([P, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "sage_attn_fwd_prequant_mx": ([P, P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
+        "sage_attn_fwd_qf16_mx": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
         "sage_last_error": ([], ctypes.c_char_p),
     }
@@ -271,6 +273,22 @@ def attn_prequant_mx(qk: dict, vq: dict, N, causal=False, sm_scale=None, smooth_
         _ptr(vq["v_mean"]) if smooth_v else None, _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale),
         ctypes.byref(p), _stream(dev))
     _check(rc, "sage_attn_fwd_prequant_mx")
+    return out
+
+
+def attn_qf16_mx(q, qk: dict, vq: dict, causal=False, sm_scale=None, smooth_v=False, out=None):
+    """Variant-2 attention on fp16 q (quantised to MXFP4 inside the kernel) and the K of quant_qk_mx()."""
+    B, H, N, d = _check_qkv(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    p = _params(128, 64, True, False, smooth_v)
+    rc = _load().sage_attn_fwd_qf16_mx(
+        _ptr(q), _ptr(qk["k_f4"]), _ptr(qk["k_e8"]), _ptr(vq["v_f8"]), _ptr(vq["v_scale"]),
+        _ptr(vq["v_mean"]) if smooth_v else None, _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale),
+        ctypes.byref(p), _stream(q.device))
+    _check(rc, "sage_attn_fwd_qf16_mx")
     return out
 
 

@@ -94,8 +94,8 @@ int check_ptr(const void* p, size_t align, const char* name) {
   return SAGE_OK;
 }
 
-// Variant 0 without Q smoothing quantises Q inside the attention kernel.
-bool fuse_q(int variant, const Params& p) { return variant == 0 && !p.smooth_q; }
+// Variant 0 without Q smoothing, and variant 2, quantise Q inside the attention kernel.
+bool fuse_q(int variant, const Params& p) { return (variant == 0 && !p.smooth_q) || variant == 2; }
 
 bool valid_variant(int variant) { return variant >= 0 && variant <= 2; }
 
@@ -129,7 +129,7 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   L.v_f8 = take(fp8v ? G * d * Np : 0);
   L.v_scale = take(fp8v ? G * d * sizeof(float) : 0);
   L.v_mean = take(p.smooth_v ? G * d * sizeof(float) : 0);
-  L.q_e8 = take(mx ? G * Np * (d / 32) : 0);
+  L.q_e8 = take(mx && !fq ? G * Np * (d / 32) : 0);
   L.k_e8 = take(mx ? G * Np * (d / 32) : 0);
   L.total = off;
   return L;
@@ -233,11 +233,9 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   }
   const bool fq = fuse_q(variant, p);
   if (variant == 2) {
+    // (Q is quantised by the attention kernel itself)
     e = sage::launch_quant_mx(d, k, G, N, Np, at<long long>(ws, L.ksum), p.smooth_k, at<uint8_t>(ws, L.k_i8),
                               at<uint8_t>(ws, L.k_e8), at<float>(ws, L.k_mean), st);
-    if (e == hipSuccess)
-      e = sage::launch_quant_mx(d, q, G, N, Np, nullptr, 0, at<uint8_t>(ws, L.q_i8), at<uint8_t>(ws, L.q_e8), nullptr,
-                                st);
     if (e != hipSuccess) return hip_fail(e, "MXFP4 quantisation kernel");
   } else {
     sage::QuantArgs qa = quant_args(q, k, B, H, N, d, p, fq ? nullptr : at<int8_t>(ws, L.q_i8),
@@ -260,7 +258,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   a.q_scale = fq || variant == 2 ? nullptr : at<float>(ws, L.q_scale);
   a.k_scale = variant == 2 ? nullptr : at<float>(ws, L.k_scale);
   a.q_mean = p.smooth_q ? at<float>(ws, L.q_mean) : nullptr;
-  a.q_e8 = variant == 2 ? at<uint8_t>(ws, L.q_e8) : nullptr;
+  a.q_e8 = nullptr;  // variant 2 quantises Q in the kernel
   a.k_e8 = variant == 2 ? at<uint8_t>(ws, L.k_e8) : nullptr;
   a.v = (const uint16_t*)v;
   a.v_f8 = variant != 0 ? at<uint8_t>(ws, L.v_f8) : nullptr;
@@ -453,6 +451,33 @@ int sage_attn_fwd_prequant_mx(const uint8_t* q_f4, const uint8_t* k_f4, const ui
   a.q_i8 = (const int8_t*)q_f4;
   a.k_i8 = (const int8_t*)k_f4;
   a.q_e8 = q_e8;
+  a.k_e8 = k_e8;
+  a.v_f8 = v_f8;
+  a.v_scale = v_scale;
+  a.v_mean = p.smooth_v ? v_mean : nullptr;
+  a.o = (uint16_t*)o;
+  hipError_t e = sage::launch_attn(d, 2, causal, 0, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+int sage_attn_fwd_qf16_mx(const void* q, const uint8_t* k_f4, const uint8_t* k_e8, const uint8_t* v_f8,
+                          const float* v_scale, const float* v_mean, void* o, int B, int H, int N, int d, int causal,
+                          float sm_scale, const sage_params* pp, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, SAGE_VARIANT_MXFP4QK_FP8PV, &p))) return rc;
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k_f4, 16, "k_f4")) || (rc = check_ptr(k_e8, 4, "k_e8")) ||
+      (rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")) || (rc = check_ptr(o, 16, "o")))
+    return rc;
+  if (p.smooth_v && (rc = check_ptr(v_mean, 16, "v_mean (required with smooth_v)"))) return rc;
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
+  a.q = (const uint16_t*)q;
+  a.k_i8 = (const int8_t*)k_f4;
   a.k_e8 = k_e8;
   a.v_f8 = v_f8;
   a.v_scale = v_scale;

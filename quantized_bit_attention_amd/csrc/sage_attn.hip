@@ -418,12 +418,6 @@ __device__ __forceinline__ void smooth_q_bias(const int8_t* sK, const int8_t* sQ
 // is followed by the LDS reads for the next one and a share of the softmax's VALU
 // instructions, which execute while the MFMA occupies the matrix unit.  (Written as
 // loops without conditionals: a guarded sched_group_barrier is not honoured.)
-#ifndef V2P128
-#define V2P128 12
-#endif
-#ifndef V2P64
-#define V2P64 24
-#endif
 template <int D, int VARIANT, bool SMOOTHQ>
 __device__ __forceinline__ void interleave_schedule() {
   // every MFMA takes two LDS operand reads (K and Q, two V transposes, or two V^T
@@ -433,7 +427,7 @@ __device__ __forceinline__ void interleave_schedule() {
   constexpr int MFMA = (VARIANT == 2 ? 2 * (D / 64) : 2 * (D / 32)) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
   constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13)
                            : VARIANT == 1 ? (D == 128 ? 8 : 14)
-                                          : (D == 128 ? V2P128 : V2P64);
+                                          : (D == 128 ? 20 : 16);
   // with Q smoothing the softmax first reads its 32 biases (8 reads of 16 bytes)
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD + (SMOOTHQ ? 8 : 0), 0);
 #pragma unroll
@@ -444,12 +438,14 @@ __device__ __forceinline__ void interleave_schedule() {
   }
 }
 
-// FUSEQ (variant 0 without Q smoothing): Q arrives as fp16 and each workgroup quantises
-// its own rows into the LDS operand tile, with the per-group scale of the quantisation
-// pass (the workgroup's 128 rows are whole groups of q_group = 1 .. 128 rows).
+// FUSEQ (variant 0 without Q smoothing, and variant 2): Q arrives as fp16 and each
+// workgroup quantises its own rows into the LDS operand tile, with the rule of the
+// quantisation pass: INT8 per group of q_group = 1 .. 128 rows (the workgroup's 128
+// rows are whole groups), or MXFP4 per 32-channel block (one lane's operand per block).
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
-  static_assert(!FUSEQ || (VARIANT == 0 && !SMOOTHQ), "in-kernel Q quantisation: variant 0, no Q smoothing");
+  static_assert(!FUSEQ || ((VARIANT == 0 || VARIANT == 2) && !SMOOTHQ),
+                "in-kernel Q quantisation: variants 0 and 2, no Q smoothing");
   static_assert(VARIANT != 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
   constexpr int KD = qk_row_bytes<D, VARIANT>();  // bytes per Q / K row
@@ -497,17 +493,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const int wave_last = CAUSAL ? min(ntiles_all - 1, min(qw + 31, N - 1) / kTileKV) : ntiles_all - 1;
 
   int8_t* const sQw = sQ + wave * (KD / 32) * 1024;
-  // FUSEQ: lane l holds fp16 Q of row qw + l%32, channels 32*ks + 16*h .. +15 in
-  // qraw[2ks], qraw[2ks+1] (the bytes its operand read takes); rows >= N are zeros
+  // FUSEQ: lane l holds fp16 Q of row qw + l%32, the channels its operand reads take:
+  // variant 0: 32*ks + 16*h .. +15 in qraw[2ks], qraw[2ks+1]; variant 2: the MX block
+  // 64*ks + 32*h .. +31 in qraw[4ks .. 4ks+3].  Rows >= N are zeros.
   uint4 qraw[FUSEQ ? D / 16 : 1];
   if constexpr (FUSEQ) {
+    constexpr int PER = VARIANT == 2 ? 4 : 2;  // 16-byte loads per k-step
     const bool row_ok = wave_active && qi < N;
-    const uint16_t* qsrc = a.q + ((size_t)g * N + (row_ok ? qi : 0)) * D + 16 * h;
+    const uint16_t* qsrc = a.q + ((size_t)g * N + (row_ok ? qi : 0)) * D + 8 * PER * h;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
+    for (int ks = 0; ks < D / (16 * PER); ++ks)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        qraw[2 * ks + j] = row_ok ? *reinterpret_cast<const uint4*>(qsrc + 32 * ks + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < PER; ++j)
+        qraw[PER * ks + j] =
+            row_ok ? *reinterpret_cast<const uint4*>(qsrc + 16 * PER * ks + 8 * j) : make_uint4(0u, 0u, 0u, 0u);
   } else {
     // qw < N <= Np, and Np is a multiple of 32: an active wave's rows lie in the tensor
     if (wave_active) load_q_tile<KD>(make_rsrc(qh, (size_t)a.Np * KD), qw, sQw);
@@ -521,7 +520,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
                  : 0.0f;
   // variant 2: the MX scale bytes of this lane's query (rows >= N hold zeros)
   uint32_t qsw = 0;
-  if constexpr (VARIANT == 2) {
+  if constexpr (VARIANT == 2 && !FUSEQ) {
     if (wave_active) qsw = mx_lane_scales<D>(a.q_e8 + ((size_t)g * a.Np + qi) * (D / 32), h);
   }
 
@@ -557,7 +556,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // it; clear that slot (0 times a stale NaN pattern would not be 0)
   for (int e = tid; e < L::V_BYTES / 16; e += kAttnThreads)
     reinterpret_cast<uint4*>(sV1)[e] = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (FUSEQ) {
+  if constexpr (FUSEQ && VARIANT == 0) {
     // |Q| max: with the sign bits cleared, fp16 bit patterns order like the values, so a
     // packed 16-bit integer max finds it exactly
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -582,7 +581,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   }
   wait_copies();
   __syncthreads();
-  if constexpr (FUSEQ) {
+  if constexpr (FUSEQ && VARIANT == 2) {
+    // each k-step's 32 channels of this lane are one MX block
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w[4] = {qraw[4 * ks + j].x, qraw[4 * ks + j].y, qraw[4 * ks + j].z, qraw[4 * ks + j].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f16x2 hv = __builtin_bit_cast(f16x2, w[u]);
+          v[8 * j + 2 * u] = (float)hv[0];
+          v[8 * j + 2 * u + 1] = (float)hv[1];
+        }
+      }
+      uint4 packed;
+      qsw |= mx_block_fp4(v, packed) << (8 * ks);
+      *reinterpret_cast<uint4*>(sQw + ks * 1024 + 16 * lane) = packed;
+    }
+  }
+  if constexpr (FUSEQ && VARIANT == 0) {
     // a group of 32 rows or more spans waves w0 .. w0 + q_group/32 - 1
     float amax = dq;
     if (a.q_group >= 32) {
@@ -855,8 +874,12 @@ static hipError_t launch_dv(int causal, int smooth_q, const AttnArgs& a, hipStre
 }
 
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st) {
-  if (a.q) {  // fp16 Q, quantised in the kernel (variant 0, no Q smoothing)
-    if (variant != 0 || smooth_q) return hipErrorInvalidValue;
+  if (a.q) {  // fp16 Q, quantised in the kernel (variant 0 without Q smoothing, variant 2)
+    if (variant == 1 || smooth_q) return hipErrorInvalidValue;
+    if (variant == 2) {
+      if (d == 64) return causal ? launch_one<64, 2, true, false, true>(a, st) : launch_one<64, 2, false, false, true>(a, st);
+      return causal ? launch_one<128, 2, true, false, true>(a, st) : launch_one<128, 2, false, false, true>(a, st);
+    }
     if (d == 64) return causal ? launch_one<64, 0, true, false, true>(a, st) : launch_one<64, 0, false, false, true>(a, st);
     return causal ? launch_one<128, 0, true, false, true>(a, st) : launch_one<128, 0, false, false, true>(a, st);
   }

@@ -109,6 +109,40 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
 }
 
+// MXFP4 (OCP microscaling) of one block of 32 values: the E8M0 scale code
+// floor(log2 max|v|) - 2 + 127 clamped to [0, 254] (0 for an all-zero block) and the 32
+// E2M1 codes of v / 2^(code - 127), two per byte with the lower index in the low nibble.
+// The quantisation pass and the attention kernel's fused prologue both use this.
+// E2M1 rounding: to nearest with ties to the even code (0.25 -> 0, 0.75 -> 1,
+// 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4), saturating at 6, sign kept (also of
+// zero).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 8u);
+}
+__device__ __forceinline__ uint32_t mx_block_fp4(const float* v, uint4& packed) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+  // frexp_exp(am) = floor(log2 am) + 1
+  const uint32_t code = am > 0.0f ? (uint32_t)min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0u;
+  const int sh = 127 - (int)code;  // elements are v * 2^sh, exact
+  uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    // v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds exactly like e2m1_code (checked on
+    // MI355X over the ties, the saturation range, signed zeros and 50k random values);
+    // the first value lands in the low nibble
+    const uint32_t pair = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, __builtin_amdgcn_ldexpf(v[i], sh),
+                                                                   __builtin_amdgcn_ldexpf(v[i + 1], sh), 1.0f, 0);
+    word[i / 8] |= (pair & 0xffu) << (4 * (i % 8));
+  }
+  packed = make_uint4(word[0], word[1], word[2], word[3]);
+  return code;
+}
+
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   f32x2 v = {a, b};
   f16x2 h = __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even

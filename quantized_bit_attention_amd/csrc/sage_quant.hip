@@ -433,16 +433,6 @@ hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st) {
 // block's 32 fp16 values, subtracts K's token mean (smooth_k), and writes 16 bytes of
 // codes (two per byte, the lower channel in the low nibble) and one scale byte.
 
-// E2M1 code of a value already divided by its block scale: round to nearest with
-// ties to the even code (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
-// 3.5 -> 4, 5 -> 4), saturating at 6; the sign bit is kept (also of zero).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  return m | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const uint16_t* __restrict__ x, int N, int Np,
                                                             int nsplit, const long long* __restrict__ ksum_part,
@@ -479,16 +469,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const uint16_t* __re
         v[8 * i + 2 * j + 1] = (float)hv[1] - s_mean[32 * b + 8 * i + 2 * j + 1];
       }
     }
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
-    // shared exponent floor(log2 am) - 2 as an E8M0 code; frexp_exp(am) = floor(log2 am) + 1
-    scode = am > 0.0f ? (uint32_t)min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0u;
-    const int sh = 127 - (int)scode;  // elements are v * 2^sh, exact
-    uint32_t word[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) word[i / 8] |= e2m1_code(__builtin_amdgcn_ldexpf(v[i], sh)) << (4 * (i % 8));
-    packed = make_uint4(word[0], word[1], word[2], word[3]);
+    scode = mx_block_fp4(v, packed);
   }
   *reinterpret_cast<uint4*>(codes + ((size_t)g * Np + t) * (D / 2) + 16 * b) = packed;
   e8[((size_t)g * Np + t) * BPT + b] = (uint8_t)scode;

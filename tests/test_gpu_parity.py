@@ -381,9 +381,32 @@ def test_prequant_mx_matches_whole_call(sage):
     qk = sage.quant_qk_mx(q, k)
     vq = sage.quant_v(v, smooth_v=True)
     pre = sage.attn_prequant_mx(qk, vq, N, causal=True, smooth_v=True)
+    fused = sage.attn_qf16_mx(q, qk, vq, causal=True, smooth_v=True)
     torch.cuda.synchronize()
     assert torch.isfinite(whole.float()).all()
+    # the whole call quantises Q in the attention kernel: same codes, same bits
     assert torch.equal(whole, pre)
+    assert torch.equal(whole, fused)
+
+
+@pytest.mark.parametrize("cfg,shape,causal", [(2, dict(N=333, B=1, H=2), 1), (3, dict(N=200, B=1, H=3), 0),
+                                              (1, dict(N=65, B=1, H=1), 0)])
+def test_fused_mx_q_matches_quant_pass(sage, cfg, shape, causal):
+    """Variant 2's in-kernel MXFP4 Q equals quant_qk_mx's: fused and pre-quantised kernels give
+    the same bits.  Q carries an all-zero block, a negative zero row and saturating values."""
+    c = workloads.make_inputs(cfg, **shape)
+    q = c["q"].copy()
+    q[0, 0, 2, :32] = 0
+    q[0, 0, 3, :] = -0.0
+    q[0, 0, 4, 1] = -7.99
+    say(f"fused MX Q {q.shape} causal={causal}")
+    qd, kd, vd = dev(q), dev(c["k"]), dev(c["v"])
+    qk = sage.quant_qk_mx(qd, kd)
+    vq = sage.quant_v(vd)
+    fused = sage.attn_qf16_mx(qd, qk, vq, causal=bool(causal))
+    pre = sage.attn_prequant_mx(qk, vq, q.shape[2], causal=bool(causal))
+    torch.cuda.synchronize()
+    assert torch.equal(fused, pre)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])

@@ -75,11 +75,11 @@ def test_workspace_size(lib):
     assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True, q_group=1) == (
         sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) - up(G * 32 * 4) + up(G * N * 4))
     assert sage.workspace_bytes(B, H, N, d, 0, q_group=3) == 0
-    # MXFP4 variant: K and V statistics, packed E2M1 Q/K (d/2 bytes per row), their E8M0
-    # scales (d/32 per row), k_mean, FP8 V and its scales
+    # MXFP4 variant: K and V statistics, packed E2M1 K (d/2 bytes per row), its E8M0 scales
+    # (d/32 per row), k_mean, FP8 V and its scales; the attention kernel quantises Q itself
     ns = N // 256
-    v2 = (up(G * ns * d * 8) * 2 + up(G * ns * d * 4) * 2 + 2 * up(G * Np * d // 2) + up(G * d * 4)
-          + up(G * d * Np) + up(G * d * 4) + 2 * up(G * Np * d // 32))
+    v2 = (up(G * ns * d * 8) * 2 + up(G * ns * d * 4) * 2 + up(G * Np * d // 2) + up(G * d * 4)
+          + up(G * d * Np) + up(G * d * 4) + up(G * Np * d // 32))
     assert sage.workspace_bytes(B, H, N, d, 2) == v2
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
     assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
@@ -208,6 +208,11 @@ def test_mxfp4_entry_points_reject(lib):
     # the pre-quantised int8 entry point points MXFP4 callers to their own
     rc = lib.sage_attn_fwd_prequant(A, A, A, A, None, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, 2, None, None)
     assert rc == -1 and b"prequant_mx" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16_mx(A, A, None, A, A, None, A, 1, 1, 64, 64, 0, 0.125, None, None)
+    assert rc == -1 and b"k_e8 is NULL" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16_mx(A, A, A, A, A, None, A, 1, 1, 64, 64, 0, 0.125,
+                                   ctypes.byref(sage._params(smooth_q=True)), None)
+    assert rc == -2
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
