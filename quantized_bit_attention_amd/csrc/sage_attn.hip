@@ -383,10 +383,10 @@ __device__ __forceinline__ void split_qmean(const float* qmean, bool valid, int8
 }
 
 // The bias of keys 16*wave .. 16*wave + 15 of the K tile in sK for every Q block, one
-// 16x16x64 INT8 MFMA per 64 channels: A = those keys (row = lane%16), B = the limb
-// matrix (column = lane%16), same 16 channels per lane for both.  The result in lane l
-// is column n = l%16 (block n/4, limb n%4) for keys 4*(l/16) + 0..3; the lane holding
-// limb 0 takes limbs 1 and 2 from the next lanes of its quad and writes four biases.
+// 16x16x64 INT8 MFMA per 64 channels: A = the limb matrix (row = lane%16 = 4*block +
+// limb), B = those keys (column = lane%16), the same 16 channels per lane for both.  Lane
+// l then holds key 16*wave + l%16 in column l%16 and rows 4*(l/16) + 0..3, i.e. the four
+// limbs of Q block l/16: it combines them in its own registers and writes one bias.
 // wk = sm_scale * log2(e) * dK of those 16 keys (one K block: blk_k >= 16).
 template <int D>
 __device__ __forceinline__ void smooth_q_bias(const int8_t* sK, const int8_t* sQl, const float* sScale, float wk,
@@ -398,20 +398,11 @@ __device__ __forceinline__ void smooth_q_bias(const int8_t* sK, const int8_t* sQ
   for (int kk = 0; kk < D / 64; ++kk) {
     const i32x4 ka = *reinterpret_cast<const i32x4*>(k_lds_chunk<D>(sK, 16 * wave + n, 4 * kk + grp));
     const i32x4 qa = *reinterpret_cast<const i32x4*>(sQl + n * D + 64 * kk + 16 * grp);
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qa, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa, ka, acc, 0, 0, 0);
   }
-  const float w = wk * sScale[n >> 2];
-  float b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // |l_k . Khat| <= 64*127*D < 2^21, so 128*L0 + L1 and 128*L2 + L3 fit in int32
-    const int l1 = __builtin_amdgcn_update_dpp(0, acc[i], 0x55, 0xF, 0xF, false);  // lane 1 of the quad
-    const int l2 = __builtin_amdgcn_update_dpp(0, acc[i], 0xAA, 0xF, 0xF, false);  // lane 2
-    const int l3 = __builtin_amdgcn_update_dpp(0, acc[i], 0xFF, 0xF, 0xF, false);  // lane 3
-    b[i] = w * fmaf((float)(acc[i] * 128 + l1), 16384.0f, (float)(l2 * 128 + l3));
-  }
-  if ((n & 3) == 0)
-    *reinterpret_cast<float4*>(sBias + (n >> 2) * kTileKV + 16 * wave + 4 * grp) = make_float4(b[0], b[1], b[2], b[3]);
+  // |l_k . Khat| <= 64*127*D < 2^21, so 128*L0 + L1 and 128*L2 + L3 fit in int32
+  const float b = fmaf((float)(acc[0] * 128 + acc[1]), 16384.0f, (float)(acc[2] * 128 + acc[3]));
+  sBias[grp * kTileKV + 16 * wave + n] = wk * sScale[grp] * b;
 }
 
 // Instruction order of the interior-tile block: after a few operand reads, each MFMA
