@@ -198,7 +198,7 @@ int run_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const
                  hipStream_t st) {
   hipError_t e;
   if (p.smooth_k) {
-    e = sage::launch_stats(d, k, nullptr, B * H, N, sage::StatsOut{ksum, nullptr, nullptr, nullptr}, st);
+    e = sage::launch_stats(d, k, nullptr, false, B * H, N, sage::StatsOut{ksum, nullptr, nullptr, nullptr}, st);
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
   e = sage::launch_quant(d, quant_args(q, k, B, H, N, d, p, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, ksum), st);
@@ -228,7 +228,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   const sage::StatsOut stats{at<long long>(ws, L.ksum), at<long long>(ws, L.vsum), at<float>(ws, L.vmax),
                              at<float>(ws, L.vmin)};
   if (p.smooth_k || variant != 0) {
-    e = sage::launch_stats(d, k, variant != 0 ? v : nullptr, G, N, stats, st);
+    e = sage::launch_stats(d, k, variant != 0 ? v : nullptr, p.smooth_v, G, N, stats, st);
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
   const bool fq = fuse_q(variant, p);
@@ -325,7 +325,7 @@ int sage_quant_v_ex(const void* v, int B, int H, int N, int d, int smooth_v, uin
   const sage::StatsOut stats{at<long long>(ws, 0), at<long long>(ws, i64), at<float>(ws, 2 * i64),
                              at<float>(ws, 2 * i64 + f32)};
   // the statistics pass reads K and V together; with V as "K" too the K sums are unused
-  hipError_t e = sage::launch_stats(d, v, v, (int)G, N, stats, st);
+  hipError_t e = sage::launch_stats(d, v, v, smooth_v, (int)G, N, stats, st);
   if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   e = sage::launch_quant_v(d, v, (int)G, N, pad_len(N), stats, smooth_v, v_f8, v_scale, smooth_v ? v_mean : nullptr,
                            st);
@@ -424,7 +424,8 @@ int sage_quant_qk_mx(const void* q, const void* k, int B, int H, int N, int d, i
   hipStream_t st = (hipStream_t)stream;
   const int G = B * H, Np = pad_len(N);
   hipError_t e = hipSuccess;
-  if (smooth_k) e = sage::launch_stats(d, k, nullptr, G, N, sage::StatsOut{(long long*)ws, nullptr, nullptr, nullptr}, st);
+  if (smooth_k)
+    e = sage::launch_stats(d, k, nullptr, false, G, N, sage::StatsOut{(long long*)ws, nullptr, nullptr, nullptr}, st);
   if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   e = sage::launch_quant_mx(d, k, G, N, Np, (const long long*)ws, smooth_k, k_f4, k_e8, k_mean, st);
   if (e == hipSuccess) e = sage::launch_quant_mx(d, q, G, N, Np, nullptr, 0, q_f4, q_e8, nullptr, st);

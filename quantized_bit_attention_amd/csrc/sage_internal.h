@@ -45,14 +45,15 @@ struct AttnArgs {
 constexpr int kStatRows = 256;
 int stat_splits(int N);
 // Statistics pass outputs, [G][nsplit][D] each, folded into split 0 by the pass; the V
-// arrays are only written when V is given.
+// max and min are only written when V is given, the V sums only with v_sums.
 struct StatsOut {
   long long* ksum;  // exact sums of K in units of 2^-24
   long long* vsum;  // the same for V
   float* vmax;      // max of V per channel
   float* vmin;      // min of V per channel
 };
-hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, const StatsOut& out, hipStream_t st);
+hipError_t launch_stats(int d, const void* k, const void* v, bool v_sums, int G, int N, const StatsOut& out,
+                        hipStream_t st);
 hipError_t launch_quant(int d, const QuantArgs& a, hipStream_t st);
 hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
                           uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st);

@@ -20,14 +20,15 @@
 namespace sage {
 
 // Pass 1: per (head, split of kStatRows tokens) partial sums of K (exact, int64) and,
-// for WITH_V, of V, plus the partial max and min of V per channel.
+// for WITH_V, the partial max and min of V per channel (packed fp16, exact) and, for
+// V_SUMS (V smoothing), the sums of V.
 //   ksum_part, vsum_part [G][nsplit][D] int64; vmax_part, vmin_part [G][nsplit][D] fp32.
 // A thread accumulates its at most kStatRows / RPI values per channel in fp64, which is
 // exact: every fp16 value is an integer multiple of 2^-24 below 2^16 in magnitude, so
 // up to 2^13 of them sum exactly within fp64's 53-bit significand.  The thread totals
 // are then converted to int64 units of 2^-24 and summed exactly.  A thread issues all
 // its row loads at once (8 at a time when it also reads V).
-template <int D, bool WITH_V>
+template <int D, bool WITH_V, bool V_SUMS>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, int N,
                                                          int nsplit, long long* __restrict__ ksum_part,
@@ -44,10 +45,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   const size_t head = (size_t)g * N * D;
   const int t0 = split * kStatRows, t1 = min(N, t0 + kStatRows);
 
+  static_assert(WITH_V || !V_SUMS, "V sums need V");
   double acc[8], vacc[8];
-  float vm[8], vn[8];
+  f16x2 vmx[4], vmn[4];
+  const f16x2 ninf = __builtin_bit_cast(f16x2, 0xFC00FC00u), pinf = __builtin_bit_cast(f16x2, 0x7C007C00u);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { acc[j] = 0.0; vacc[j] = 0.0; vm[j] = -INFINITY; vn[j] = INFINITY; }
+  for (int j = 0; j < 8; ++j) { acc[j] = 0.0; vacc[j] = 0.0; }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { vmx[j] = ninf; vmn[j] = pinf; }
 
 #pragma unroll 1
   for (int base = 0; base < NIT; base += BATCH) {
@@ -69,20 +74,28 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
         acc[2 * j] += (double)(float)hk[0];
         acc[2 * j + 1] += (double)(float)hk[1];
         if (WITH_V) {
-          // rows past N hold zeros; they stay out of the max and min below
+          // rows past N hold zeros: they stay out of the max and min (and add 0 to the sums)
           const f16x2 hv = __builtin_bit_cast(f16x2, u[j]);
           const bool in = t0 + r0 + RPI * (base + b) < t1;
-          vacc[2 * j] += (double)(float)hv[0];
-          vacc[2 * j + 1] += (double)(float)hv[1];
-          vm[2 * j] = in ? fmaxf(vm[2 * j], (float)hv[0]) : vm[2 * j];
-          vm[2 * j + 1] = in ? fmaxf(vm[2 * j + 1], (float)hv[1]) : vm[2 * j + 1];
-          vn[2 * j] = in ? fminf(vn[2 * j], (float)hv[0]) : vn[2 * j];
-          vn[2 * j + 1] = in ? fminf(vn[2 * j + 1], (float)hv[1]) : vn[2 * j + 1];
+          if (V_SUMS) {
+            vacc[2 * j] += (double)(float)hv[0];
+            vacc[2 * j + 1] += (double)(float)hv[1];
+          }
+          vmx[j] = __builtin_elementwise_max(vmx[j], in ? hv : ninf);
+          vmn[j] = __builtin_elementwise_min(vmn[j], in ? hv : pinf);
         }
       }
     }
   }
 
+  float vm[8], vn[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vm[2 * j] = (float)vmx[j][0];
+    vm[2 * j + 1] = (float)vmx[j][1];
+    vn[2 * j] = (float)vmn[j][0];
+    vn[2 * j + 1] = (float)vmn[j][1];
+  }
   // two rounds through LDS: (K sums, V max), then (V sums, V min)
   __shared__ long long s_sum[kThreads][8];
   __shared__ float s_max[kThreads][8];
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
         ksum_part[o] = sm;
         if (WITH_V) vmax_part[o] = m;
       } else {
-        vsum_part[o] = sm;
+        if (V_SUMS) vsum_part[o] = sm;
         vmin_part[o] = m;
       }
     }
@@ -128,15 +141,15 @@ __global__ __launch_bounds__(4 * D) void stats_finalize_kernel(int nsplit, long 
   __shared__ float s_max[4][D], s_min[4][D];
   const int g = blockIdx.x, c = threadIdx.x % D, j = threadIdx.x / D;
   const size_t base = (size_t)g * nsplit * D + c;
-  const bool with_v = vsum_part != nullptr;
+  const bool with_v = vmax_part != nullptr, with_vsum = vsum_part != nullptr;
   long long s = 0, vs = 0;
   float mx = -INFINITY, mn = INFINITY;
 #pragma unroll 4
   for (int sp = j; sp < nsplit; sp += 4) {
     const size_t o = base + (size_t)sp * D;
     s += ksum_part[o];
+    if (with_vsum) vs += vsum_part[o];
     if (with_v) {
-      vs += vsum_part[o];
       mx = fmaxf(mx, vmax_part[o]);
       mn = fminf(mn, vmin_part[o]);
     }
@@ -148,8 +161,8 @@ __global__ __launch_bounds__(4 * D) void stats_finalize_kernel(int nsplit, long 
   __syncthreads();  // every thread has read its splits before split 0 is overwritten
   if (j == 0) {
     ksum_part[base] = s_sum[0][c] + s_sum[1][c] + s_sum[2][c] + s_sum[3][c];
+    if (with_vsum) vsum_part[base] = s_vsum[0][c] + s_vsum[1][c] + s_vsum[2][c] + s_vsum[3][c];
     if (with_v) {
-      vsum_part[base] = s_vsum[0][c] + s_vsum[1][c] + s_vsum[2][c] + s_vsum[3][c];
       vmax_part[base] = fmaxf(fmaxf(s_max[0][c], s_max[1][c]), fmaxf(s_max[2][c], s_max[3][c]));
       vmin_part[base] = fminf(fminf(s_min[0][c], s_min[1][c]), fminf(s_min[2][c], s_min[3][c]));
     }
@@ -388,24 +401,28 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __res
 int stat_splits(int N) { return (N + kStatRows - 1) / kStatRows; }
 
 template <int D>
-static void launch_stats_d(const void* k, const void* v, int G, int N, const StatsOut& out, hipStream_t st) {
+static void launch_stats_d(const void* k, const void* v, bool v_sums, int G, int N, const StatsOut& out,
+                           hipStream_t st) {
   const int ns = stat_splits(N);
   dim3 grid(ns, G);
-  if (v)
-    stats_kernel<D, true><<<grid, kThreads, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, N, ns, out.ksum,
-                                                     out.vsum, out.vmax, out.vmin);
+  const uint16_t* kk = (const uint16_t*)k;
+  const uint16_t* vv = (const uint16_t*)v;
+  if (v && v_sums)
+    stats_kernel<D, true, true><<<grid, kThreads, 0, st>>>(kk, vv, N, ns, out.ksum, out.vsum, out.vmax, out.vmin);
+  else if (v)
+    stats_kernel<D, true, false><<<grid, kThreads, 0, st>>>(kk, vv, N, ns, out.ksum, nullptr, out.vmax, out.vmin);
   else
-    stats_kernel<D, false><<<grid, kThreads, 0, st>>>((const uint16_t*)k, nullptr, N, ns, out.ksum, nullptr,
-                                                      nullptr, nullptr);
-  stats_finalize_kernel<D><<<G, 4 * D, 0, st>>>(ns, out.ksum, v ? out.vsum : nullptr, v ? out.vmax : nullptr,
-                                                v ? out.vmin : nullptr);
+    stats_kernel<D, false, false><<<grid, kThreads, 0, st>>>(kk, nullptr, N, ns, out.ksum, nullptr, nullptr, nullptr);
+  stats_finalize_kernel<D><<<G, 4 * D, 0, st>>>(ns, out.ksum, v && v_sums ? out.vsum : nullptr,
+                                                v ? out.vmax : nullptr, v ? out.vmin : nullptr);
 }
 
-hipError_t launch_stats(int d, const void* k, const void* v, int G, int N, const StatsOut& out, hipStream_t st) {
+hipError_t launch_stats(int d, const void* k, const void* v, bool v_sums, int G, int N, const StatsOut& out,
+                        hipStream_t st) {
   if (d == 64)
-    launch_stats_d<64>(k, v, G, N, out, st);
+    launch_stats_d<64>(k, v, v_sums, G, N, out, st);
   else
-    launch_stats_d<128>(k, v, G, N, out, st);
+    launch_stats_d<128>(k, v, v_sums, G, N, out, st);
   return hipGetLastError();
 }
 
