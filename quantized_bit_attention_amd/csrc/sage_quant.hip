@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const uint16_t* __restr
   constexpr int NIT = kStatRows / RPI;  // rows per thread
   constexpr int BATCH = WITH_V ? 8 : NIT;
   static_assert(NIT % BATCH == 0 && NIT <= 8192, "row batches; exact fp64 thread sums");
-  const int split = blockIdx.x, g = blockIdx.y;
+  const int split = blockIdx.x % nsplit, g = blockIdx.x / nsplit;  // 1-D grid: G may exceed 65535
   const int tid = threadIdx.x, cg = tid % TPR, r0 = tid / TPR;
   const size_t head = (size_t)g * N * D;
   const int t0 = split * kStatRows, t1 = min(N, t0 + kStatRows);
@@ -346,7 +346,8 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __res
   constexpr int TT = 64;  // tokens per tile
   __shared__ float s_r[D], s_mean[D];
   __shared__ uint8_t s_t[D][TT + 4];
-  const int tile = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int ntiles = Np / 64;  // 1-D grid over (head, 64-token tile)
+  const int tile = blockIdx.x % ntiles, g = blockIdx.x / ntiles, tid = threadIdx.x;
   if (tid < D) {
     const size_t o = (size_t)g * nsplit * D + tid;  // folded into split 0
     const float mean = smooth_v ? fixed24_mean(vsum_part[o], N) : 0.0f;
@@ -404,7 +405,7 @@ template <int D>
 static void launch_stats_d(const void* k, const void* v, bool v_sums, int G, int N, const StatsOut& out,
                            hipStream_t st) {
   const int ns = stat_splits(N);
-  dim3 grid(ns, G);
+  const int grid = ns * G;
   const uint16_t* kk = (const uint16_t*)k;
   const uint16_t* vv = (const uint16_t*)v;
   if (v && v_sums)
@@ -458,17 +459,18 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const uint16_t* __re
   constexpr int BPT = D / 32;             // blocks per token
   constexpr int TOK = kThreads / BPT;     // tokens per workgroup
   __shared__ float s_mean[D];
-  const int g = blockIdx.y, tid = threadIdx.x;
+  const int ntiles = Np / TOK;  // 1-D grid over (head, tile of TOK tokens)
+  const int tb = blockIdx.x % ntiles, g = blockIdx.x / ntiles, tid = threadIdx.x;
   if (tid < D) {
     float m = 0.0f;
     if (smooth) {
       m = fixed24_mean(ksum_part[(size_t)g * nsplit * D + tid], N);  // folded into split 0
-      if (blockIdx.x == 0 && k_mean) k_mean[(size_t)g * D + tid] = m;
+      if (tb == 0 && k_mean) k_mean[(size_t)g * D + tid] = m;
     }
     s_mean[tid] = m;
   }
   __syncthreads();
-  const int t = blockIdx.x * TOK + tid / BPT, b = tid % BPT;
+  const int t = tb * TOK + tid / BPT, b = tid % BPT;
   if (t >= Np) return;
   uint4 packed = make_uint4(0u, 0u, 0u, 0u);
   uint32_t scode = 0;
@@ -496,10 +498,10 @@ hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const lon
                            uint8_t* codes, uint8_t* e8, float* k_mean, hipStream_t st) {
   const int ns = stat_splits(N);
   if (d == 64) {
-    dim3 grid(Np / (kThreads / 2), G);
+    const int grid = Np / (kThreads / 2) * G;
     quant_mx_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)x, N, Np, ns, ksum_part, smooth, codes, e8, k_mean);
   } else {
-    dim3 grid(Np / (kThreads / 4), G);
+    const int grid = Np / (kThreads / 4) * G;
     quant_mx_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)x, N, Np, ns, ksum_part, smooth, codes, e8, k_mean);
   }
   return hipGetLastError();
@@ -507,7 +509,7 @@ hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const lon
 
 hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
                           uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st) {
-  dim3 grid(Np / 64, G);
+  const int grid = Np / 64 * G;
   const int ns = stat_splits(N);
   if (d == 64)
     quant_v_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, ns, stats.vsum, stats.vmax, stats.vmin,

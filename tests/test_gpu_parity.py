@@ -570,6 +570,31 @@ def test_fused_q_quantisation_matches_quant_pass(sage, cfg, shape, blk_q, blk_k,
     assert torch.equal(whole, pre)
 
 
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_attn_maximum_size_sampled_heads(sage, orc, variant):
+    """B*H*pad_len(N)*d one tile short of 2^31 (131071 heads of N = 100, d = 128): offsets
+    near the limit of the contract.  Inputs come from torch's seeded generator on the
+    GPU; the sampled heads are copied back for the oracle."""
+    H, N, d = 131071, 100, 128
+    assert H * 128 * d < 2 ** 31 <= (H + 1) * 128 * d
+    gen = torch.Generator(device="cuda").manual_seed(77 + variant)
+    shape = (1, H, N, d)
+    q = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).half()
+    k = (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+         + 3.0 * torch.randn((1, H, 1, d), generator=gen, device="cuda", dtype=torch.float32)).half()
+    v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).half()
+    say(f"attn maximum size {shape} variant={variant}")
+    o = sage.attn(q, k, v, causal=True, variant=variant)
+    heads = [0, 1, H // 2, H - 2, H - 1]
+    sel = torch.tensor(heads, device="cuda")
+    qs, ks, vs = (host(t.index_select(1, sel)) for t in (q, k, v))
+    g = host(o.index_select(1, sel)).astype(np.float64)
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    ref = orc.attn(qs, ks, vs, causal=1, variant=variant)
+    check_o(f"max size v{variant}", g, ref)
+
+
 def test_api_rejects_bad_arguments_on_gpu(sage):
     q = torch.zeros((1, 1, 64, 96), dtype=torch.float16, device="cuda")
     with pytest.raises(sage.SageError, match="head dim"):
