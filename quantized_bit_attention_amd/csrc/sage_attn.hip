@@ -5,6 +5,8 @@
 // FlashAttention-style tiling with an online softmax, P~ V in FP16.
 // "SageAttention2 ..." (abstract): FP8 P~ and V with two-level accumulation, and the
 // Q-smoothing term added back to the scores.
+// "SageAttention3 ..." (abstract): FP4 attention on matrix units; variant 2 reads it as
+// OCP MXFP4 scores (E2M1 with an E8M0 scale per 32 channels) before the FP8 P~ V.
 // Online softmax: "Online normalizer calculation for softmax" and FlashAttention(-2),
 // entries of the summary page's reference list.
 //
@@ -16,10 +18,12 @@
 //    row max or sum needs only its own registers plus one v_permlane32_swap.
 //    The K rows are loaded into the A operand in the order perm(r) so that
 //    accumulator register i of lane half h is key 16h + i.
+//  - Variant 2 forms the same S^T with v_mfma_scale_f32_32x32x64_f8f6f4 on packed E2M1
+//    codes (the INT8 tile layouts with D/2 byte columns) and per-lane E8M0 scales.
 //  - O is kept transposed, O^T = V^T P^T: P~ (converted in registers) is the B
 //    operand as it stands; V^T comes from row-major LDS through ds_read_b64_tr_b16
 //    (variant 0, fp16, v_mfma_f32_32x32x16_f16) or from the key-contiguous FP8 V^T
-//    (variant 1, v_mfma_f32_32x32x64_f8f6f4).
+//    (variants 1 and 2, v_mfma_f32_32x32x64_f8f6f4), accumulated in fp32 in O.
 //  - Causal: tiles past a wave's last row are skipped; workgroups run
 //    longest-first and consecutive workgroups of one head stay on one XCD.
 #include <type_traits>

@@ -3,11 +3,13 @@
 // Method: "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
 // Acceleration" (summary page, "Summary" and "Interesting ideas" I1): K loses its
 // token mean, then Q and K become INT8 with one fp32 scale per block of tokens.
-// "SageAttention2 ..." (abstract): Q loses its block mean; V becomes FP8 with one
-// scale per channel.
+// "SageAttention2 ..." (abstracts): Q loses its block mean; V becomes FP8 with one
+// scale per channel, optionally after losing its token mean ("smooth Q and V").
+// "SageAttention3 ..." (abstract): FP4 attention, read as per-token OCP MXFP4 of Q and
+// K' (variant 2).
 //
-// All three passes are bound by HBM bandwidth: they read fp16 rows with 16-byte
-// loads (8 channels per thread, d/8 threads per row) and write int8 / fp8 codes.
+// All passes are bound by HBM bandwidth: they read fp16 rows with 16-byte loads and
+// write int8 / fp8 / packed fp4 codes.
 //
 // Exactness: token sums are exact int64 sums of the fp16 values in units of 2^-24,
 // so means do not depend on summation order; every fp32 step (subtract, multiply by
