@@ -321,6 +321,10 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
       if constexpr (VARIANT == 0) {
         pk[st * 8 + i / 2] = pack_f16x2(pv[0], pv[1]);
         pk[st * 8 + i / 2 + 1] = pack_f16x2(pv[2], pv[3]);
+        // an empty use keeps each pack next to its exps: left alone, the compiler sinks
+        // the packs past the end of the interleaved block, so all 32 fp32 P~ of the lane
+        // stay live across it (about 30 VGPRs, the third wave per SIMD at d = 64)
+        asm volatile("" ::"v"(pk[st * 8 + i / 2]), "v"(pk[st * 8 + i / 2 + 1]));
       } else {
         pk[st * 4 + i / 4] = cvt_pk_fp8(pv[2], pv[3], cvt_pk_fp8(pv[0], pv[1], 0u, false), true);
       }
