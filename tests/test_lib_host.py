@@ -222,3 +222,14 @@ def test_binding_fails_loudly_without_gpu_tensors():
         sage.attn(x, x, x)
     with pytest.raises(TypeError):
         sage.attn(x.float(), x, x)
+
+
+def test_bench_refuses_several_gpus():
+    # one GPU only: the multi-GPU request ends before anything touches a device
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 2
+    assert "one GPU" in res.stdout + res.stderr
+    assert not res.stdout.lstrip().startswith("{")
