@@ -255,10 +255,10 @@ template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, typename SV>
 __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const float* bias, int kl, int N,
                                              int qi, float& m, float& l, uint32_t* pk, float& alpha,
                                              bool& rescale) {
-  auto keep = [&](int st, int i) {
-    const int key = kl + 32 * st + i;
-    return !MASK || (key < N && (!CAUSAL || key <= qi));
-  };
+  // key kl + j is visible iff j <= jmax (keys < N, and <= qi when causal): one compare
+  // against a constant per score
+  const int jmax = (CAUSAL ? min(qi, N - 1) : N - 1) - kl;
+  auto keep = [&](int st, int i) { return !MASK || 32 * st + i <= jmax; };
   float x[2][16];
   float mt;
   if (SMOOTHQ) {
@@ -287,7 +287,7 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
     for (int st = 0; st < 2; ++st) {
       mi[st] = INT_MIN;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mi[st] = keep(st, i) ? max(mi[st], s[st][i]) : mi[st];
+      for (int i = 0; i < 16; ++i) mi[st] = max(mi[st], keep(st, i) ? s[st][i] : INT_MIN);
     }
     const float m0 = (MASK && mi[0] == INT_MIN) ? -INFINITY : c[0] * (float)mi[0];
     const float m1 = (MASK && mi[1] == INT_MIN) ? -INFINITY : c[1] * (float)mi[1];
