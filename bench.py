@@ -69,7 +69,7 @@ def main():
                     help="0: INT8 QK + FP16 P~V, 1: INT8 QK + Q smoothing + FP8 P~V, 2: MXFP4 QK + FP8 P~V "
                          "(default: the workload's)")
     ap.add_argument("--smooth-v", action="store_true",
-                    help="variant 1 only: subtract V's token mean before FP8 and add it back")
+                    help="variants 1 and 2 (FP8 P~V): subtract V's token mean before FP8 and add it back")
     ap.add_argument("--q-group", type=int, default=0,
                     help="rows per Q scale (0: one per Q block; 1: per token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

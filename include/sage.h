@@ -62,7 +62,7 @@ typedef struct {
   int blk_k;    /* tokens per K scale block: 16, 32, 64 or 128 (default 64) */
   int smooth_k; /* subtract the token mean of K (default 1) */
   int smooth_q; /* subtract the block mean of Q and add its term back (default: variant == 1) */
-  int smooth_v; /* variant 1 only: subtract the token mean of V before FP8, add it to O
+  int smooth_v; /* FP8 P~V variants (1, 2): subtract the token mean of V before FP8, add it to O
                    (SageAttention2 abstract, "smooth Q and V"; default 0) */
   int q_group;  /* rows per Q scale: 0 (= blk_q, default) or a power of two <= blk_q.
                    The SageAttention2 abstracts quantise Q and K at thread- / warp-level

@@ -142,7 +142,7 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
          smooth_k=True, smooth_q=None, smooth_v=False, q_group=0, out=None, workspace=None):
     """o = SageAttention(q, k, v) for [B, H, N, d] fp16 tensors on the GPU.
 
-    smooth_v (variant 1 only) subtracts V's token mean before FP8 and adds it to O.
+    smooth_v (FP8 P~V variants 1 and 2) subtracts V's token mean before FP8 and adds it to O.
     q_group: rows per Q scale (0 = blk_q; 1 = per token)."""
     B, H, N, d = _check_qkv(q, k, v)
     if sm_scale is None:
