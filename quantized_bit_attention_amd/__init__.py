@@ -142,6 +142,8 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
          smooth_k=True, smooth_q=None, smooth_v=False, q_group=0, out=None, workspace=None):
     """o = SageAttention(q, k, v) for [B, H, N, d] fp16 tensors on the GPU.
 
+    An empty input (B, H or N zero) returns the empty output without a launch.
+
     smooth_v (FP8 P~V variants 1 and 2) subtracts V's token mean before FP8 and adds it to O.
     q_group: rows per Q scale (0 = blk_q; 1 = per token)."""
     B, H, N, d = _check_qkv(q, k, v)
@@ -151,6 +153,8 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
         smooth_q = variant == VARIANT_FP8PV
     if out is None:
         out = torch.empty_like(q)
+    if q.numel() == 0:  # no heads or no tokens: nothing to compute (the C ABI wants B, H, N >= 1)
+        return out
     p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v, q_group)
     lib = _load()
     nbytes = lib.sage_workspace_bytes(B, H, N, d, variant, ctypes.byref(p))

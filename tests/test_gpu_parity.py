@@ -520,6 +520,17 @@ def test_attn_degenerate_inputs(sage, orc, variant):
             check_o(f"{name} v{variant} c{causal}", g, o)
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 0, 64), (0, 2, 16, 128), (2, 0, 8, 64)])
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_attn_empty_inputs(sage, shape, variant):
+    """No heads or no tokens: the output is empty, nothing is launched."""
+    say(f"attn empty shape={shape} variant={variant}")
+    import torch
+    x = torch.zeros(shape, dtype=torch.float16, device="cuda")
+    o = sage.attn(x, x, x, causal=True, variant=variant)
+    assert o.shape == x.shape and o.numel() == 0
+
+
 def test_prequant_matches_whole_call_and_is_deterministic(sage):
     c = inputs(2)
     say("prequant vs whole call, determinism (cfg2)")
