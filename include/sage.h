@@ -10,7 +10,11 @@
  *   "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and
  *    Per-thread INT4 Quantization" (abstract): Q is smoothed as well, P~ and V
  *    are quantised to FP8, and P~ V uses two-level accumulation.  Here Q/K stay
- *    INT8 (one fp32 scale per block of tokens) in both variants.
+ *    INT8 in variants 0 and 1 (one fp32 scale per block of tokens, or per group
+ *    of rows);
+ *   "SageAttention3: Microscaling FP4 Attention for Inference and An Exploration
+ *    of 8-Bit Training" (abstract): FP4 attention on matrix units, taken here as
+ *    variant 2 (MXFP4 Q K^T on the scaled FP4 MFMA, P~ V as variant 1).
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, allocated and owned by the caller.
@@ -80,9 +84,10 @@ int sage_version(void);
 /* Rows of the padded int8 / fp8 tensors: N rounded up to a multiple of 128. */
 int sage_pad_len(int N);
 
-/* Keys per online-softmax tile (the tile over which the running max advances and,
- * in variant 1, the span of one fresh FP8 accumulator).  Ascending tiles of this
- * size define the exact schedule of the softmax.  Returns < 0 for bad arguments. */
+/* Keys per online-softmax tile (the tile over which the running max advances; the
+ * FP8 codes of P~ in variants 1 and 2 depend on the max at each tile).  Ascending
+ * tiles of this size define the exact schedule of the softmax.  Returns < 0 for bad
+ * arguments. */
 int sage_kv_tile(int variant, int d);
 
 /* Bytes of device workspace sage_attn_fwd / sage_attn_fwd_ex / sage_quant_qk /
@@ -130,8 +135,9 @@ int sage_quant_v_ex(const void* v, int B, int H, int N, int d, int smooth_v, uin
 
 /*
  * o = SageAttention(q, k, v): the whole plug-and-play forward (quantisation kernels
- * plus the attention kernel; for variant 0 without Q smoothing the attention kernel
- * quantises Q itself, see sage_attn_fwd_qf16).  causal: key j is visible to query i iff j <= i.
+ * plus the attention kernel; for variant 0 without Q smoothing, and for variant 2,
+ * the attention kernel quantises Q itself, see sage_attn_fwd_qf16 and
+ * sage_attn_fwd_qf16_mx).  causal: key j is visible to query i iff j <= i.
  * sm_scale: softmax scale (finite, > 0; normally 1/sqrt(d)), applied when the int32
  * scores are dequantised.  variant: SAGE_VARIANT_*.  ws: device workspace of at
  * least sage_workspace_bytes(...) bytes.
@@ -196,8 +202,8 @@ int sage_attn_fwd_qf16_mx(const void* q, const uint8_t* k_f4, const uint8_t* k_e
 
 /*
  * The attention kernel that sage_attn_fwd runs for variant 0 without Q smoothing: Q
- * is fp16 and each workgroup quantises its own rows per block of blk_q tokens (the
- * sage_quant_qk rule above, same codes and scales); K comes pre-quantised from
+ * is fp16 and each workgroup quantises its own rows per group of q_group rows
+ * (default blk_q; the sage_quant_qk rule above, same codes and scales); K comes pre-quantised from
  * sage_quant_qk (k_i8, k_scale, same p); v is fp16.  Variant 0 only: p->smooth_q = 1
  * returns SAGE_ERR_UNSUPPORTED.  Used to time the fused kernel by itself, and for
  * callers that keep K quantised across calls.
@@ -211,7 +217,7 @@ int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, 
  * for chosen 128 x 64 tiles.  tiles[3*i + 0..2] = (flat head b*H+h, query tile, key
  * tile) with query rows [128*qt, 128*qt+128) and keys [64*kt, 64*kt+64) of the padded
  * tensors; tiles is a device array.  s_out: device [n_tiles][128][64] int32.
- * blk_q is only used for validation and may be 0.
+ * A tile outside the tensors yields zeros.
  */
 int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int N, int d,
                         const int* tiles, int n_tiles, int32_t* s_out, void* stream);
