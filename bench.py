@@ -27,10 +27,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention TOPS at 1 MI355X (d=128,N=4096); % of INT8 MFMA peak"
-INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 MFMA, published
+# MI355X published dense matrix peaks, in tera-operations per second
+INT8_PEAK_TOPS = 5000.0
+FP16_PEAK_TOPS = 2500.0
+FP8_PEAK_TOPS = 5000.0
+FP4_PEAK_TOPS = 10100.0
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["quantized_bit_attention_amd/csrc/sage_attn.hip", "quantized_bit_attention_amd/csrc/sage_device.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_hbm_traffic_llm_prefill_causal.txt")
+VARIANT_TAG = {0: "", 1: "_fp8pv", 2: "_fp8pv_mxfp4"}
+
+
+def mfma_ceiling_tops(variant: int) -> float:
+    """The attention kernel's matrix-unit ceiling for its own operand types: half of the
+    counted operations are Q K^T (INT8, or FP4 in variant 2), half P~ V (FP16 in variant 0,
+    FP8 otherwise), so the ceiling is the harmonic combination of the two peaks."""
+    qk = FP4_PEAK_TOPS if variant == 2 else INT8_PEAK_TOPS
+    pv = FP16_PEAK_TOPS if variant == 0 else FP8_PEAK_TOPS
+    return 1.0 / (0.5 / qk + 0.5 / pv)
+
+
+def traffic_file(cfg_name: str, variant: int) -> str:
+    return os.path.join(ROOT, "profiles", f"attn_kernel_hbm_traffic_{cfg_name.replace('-', '_')}"
+                                          f"{VARIANT_TAG[variant]}.txt")
 
 
 def kernel_source_hash() -> str:
@@ -41,13 +59,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(cfg_id):
-    """HBM bytes per attention-kernel launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken from another version of the kernel."""
-    if cfg_id != 2 or not os.path.exists(TRAFFIC_FILE):
+def read_traffic(cfg_name, variant):
+    """HBM bytes per attention-kernel launch from the committed rocprofv3 counter summary of
+    this workload and variant, or None when it is missing or was taken from another version
+    of the kernel."""
+    path = traffic_file(cfg_name, variant)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -161,8 +181,9 @@ def main():
 
     value = ops / (ms * 1e-3) / 1e12
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
-    # the counter summary covers the default workload's kernel only
-    traffic = read_traffic(args.config) if variant == 0 and q_group == 0 else None
+    # counter summaries exist per workload and variant, for the default options
+    traffic = read_traffic(cfg["name"], variant) if q_group == 0 and not smooth_v else None
+    ceiling = mfma_ceiling_tops(variant)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -182,8 +203,11 @@ def main():
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_tops": round(attn_tops, 2),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tops / INT8_PEAK_TOPS, 4),
+        # the attention kernel against the matrix-unit ceiling of its own operand types
+        # (variant 0: INT8 + FP16 = 3333 TOPS; 1: INT8 + FP8 = 5000; 2: FP4 + FP8 = 6689)
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(ceiling, 1),
+                     "unit": "TOPS", "frac": round(attn_tops / ceiling, 4),
+                     "frac_of_int8_peak": round(attn_tops / INT8_PEAK_TOPS, 4),
                      "traffic": traffic},
     }
 

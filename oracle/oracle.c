@@ -16,7 +16,7 @@
  *  [SA2-g]   the same abstracts on the granularity of the Q/K scales: "thread-level"
  *            (ICML 2025, arXiv 2411.10958) and "warp-level" (arXiv 2502.01776); the
  *            [SA-sum] "Key points" speak of per-token quantisation.
- *  [SA3]     the SageAttention3 abstract (ICLR 2025 page): FP4 attention on matrix
+ *  [SA3]     the SageAttention3 abstract (author page, "NeurIPS Conference 2025"): FP4 attention on matrix
  *            units with microscaling.  The pages give no block format; variant 2 reads
  *            it as OCP MXFP4 (Microscaling Formats v1.0): E2M1 elements, one E8M0
  *            scale per 32 consecutive values.

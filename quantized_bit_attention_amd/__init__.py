@@ -114,6 +114,45 @@ def _check_qkv(*ts):
     return ref.shape
 
 
+def _check_out(out, shape, device):
+    """A caller-supplied output must be a contiguous fp16 [B, H, N, d] tensor on the inputs' GPU;
+    None allocates one."""
+    if out is None:
+        return torch.empty(shape, dtype=torch.float16, device=device)
+    if not isinstance(out, torch.Tensor) or out.dtype != torch.float16:
+        raise TypeError("out must be a float16 tensor")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.device != device:
+        raise ValueError("out must be on the same device as the inputs")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    return out
+
+
+def _check_tensor(t, name, shape, dtype, device):
+    """A pre-quantised operand: a contiguous tensor of exactly this shape and dtype on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _check_n(N, Np):
+    """N of a pre-quantised call must be the length the padded tensors were made for."""
+    N = int(N)
+    if N < 1 or pad_len(N) != Np:
+        raise ValueError(f"N = {N} does not match the padded length {Np} of the quantised tensors")
+    return N
+
+
 def pad_len(N: int) -> int:
     return _load().sage_pad_len(N)
 
@@ -132,6 +171,8 @@ def workspace_bytes(B, H, N, d, variant=0, blk_q=128, blk_k=64, smooth_k=True, s
 
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
@@ -151,8 +192,7 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
         sm_scale = 1.0 / math.sqrt(d)
     if smooth_q is None:
         smooth_q = variant == VARIANT_FP8PV
-    if out is None:
-        out = torch.empty_like(q)
+    out = _check_out(out, q.shape, q.device)
     if q.numel() == 0:  # no heads or no tokens: nothing to compute (the C ABI wants B, H, N >= 1)
         return out
     p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v, q_group)
@@ -211,14 +251,32 @@ def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_F
                   blk_q=128, blk_k=64, smooth_q=None, smooth_v=False, q_group=0, out=None):
     """The attention kernel alone, on quant_qk() / quant_v() outputs (quant_v(smooth_v=True) with
     smooth_v)."""
+    if variant not in (VARIANT_FP16PV, VARIANT_FP8PV):
+        raise ValueError("attn_prequant takes variant 0 or 1 (the MXFP4 variant: attn_prequant_mx)")
     B, H, Np, d = qk["q_i8"].shape
+    dev = qk["q_i8"].device
+    N = _check_n(N, Np)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if smooth_q is None:
         smooth_q = variant == VARIANT_FP8PV
-    dev = qk["q_i8"].device
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
+    nqb, nkb, nqg = -(-N // blk_q), -(-N // blk_k), -(-N // (q_group or blk_q))
+    _check_tensor(qk["q_i8"], "q_i8", (B, H, Np, d), torch.int8, dev)
+    _check_tensor(qk["k_i8"], "k_i8", (B, H, Np, d), torch.int8, dev)
+    _check_tensor(qk["q_scale"], "q_scale", (B, H, nqg), torch.float32, dev)
+    _check_tensor(qk["k_scale"], "k_scale", (B, H, nkb), torch.float32, dev)
+    if smooth_q:
+        _check_tensor(qk["q_mean"], "q_mean", (B, H, nqb, d), torch.float32, dev)
+    if variant == VARIANT_FP16PV:
+        _check_tensor(v, "v", (B, H, N, d), torch.float16, dev)
+    else:
+        if vq is None:
+            raise ValueError("variant 1 needs the FP8 V of quant_v()")
+        _check_tensor(vq["v_f8"], "v_f8", (B, H, d, Np), torch.uint8, dev)
+        _check_tensor(vq["v_scale"], "v_scale", (B, H, d), torch.float32, dev)
+        if smooth_v:
+            _check_tensor(vq["v_mean"], "v_mean", (B, H, d), torch.float32, dev)
+    out = _check_out(out, (B, H, N, d), dev)
     p = _params(blk_q, blk_k, True, smooth_q, smooth_v, q_group)
     rc = _load().sage_attn_fwd_prequant(
         _ptr(qk["q_i8"]), _ptr(qk["k_i8"]), _ptr(qk["q_scale"]), _ptr(qk["k_scale"]),
@@ -234,8 +292,10 @@ def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, 
     B, H, N, d = _check_qkv(q, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    Np = pad_len(N)
+    _check_tensor(qk["k_i8"], "k_i8", (B, H, Np, d), torch.int8, q.device)
+    _check_tensor(qk["k_scale"], "k_scale", (B, H, -(-N // blk_k)), torch.float32, q.device)
+    out = _check_out(out, q.shape, q.device)
     p = _params(blk_q, blk_k, True, False, False, q_group)
     rc = _load().sage_attn_fwd_qf16(_ptr(q), _ptr(qk["k_i8"]), _ptr(qk["k_scale"]), _ptr(v), _ptr(out), B, H, N, d,
                                     int(bool(causal)), float(sm_scale), ctypes.byref(p), _stream(q.device))
@@ -266,11 +326,12 @@ def attn_prequant_mx(qk: dict, vq: dict, N, causal=False, sm_scale=None, smooth_
     """The variant-2 attention kernel alone, on quant_qk_mx() and quant_v() outputs."""
     B, H, Np, dh = qk["q_f4"].shape
     d = 2 * dh
+    dev = qk["q_f4"].device
+    N = _check_n(N, Np)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    dev = qk["q_f4"].device
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float16, device=dev)
+    _check_mx_operands(qk, vq, B, H, N, d, dev, smooth_v, with_q=True)
+    out = _check_out(out, (B, H, N, d), dev)
     p = _params(128, 64, True, False, smooth_v)
     rc = _load().sage_attn_fwd_prequant_mx(
         _ptr(qk["q_f4"]), _ptr(qk["k_f4"]), _ptr(qk["q_e8"]), _ptr(qk["k_e8"]), _ptr(vq["v_f8"]), _ptr(vq["v_scale"]),
@@ -285,8 +346,8 @@ def attn_qf16_mx(q, qk: dict, vq: dict, causal=False, sm_scale=None, smooth_v=Fa
     B, H, N, d = _check_qkv(q)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    _check_mx_operands(qk, vq, B, H, N, d, q.device, smooth_v, with_q=False)
+    out = _check_out(out, q.shape, q.device)
     p = _params(128, 64, True, False, smooth_v)
     rc = _load().sage_attn_fwd_qf16_mx(
         _ptr(q), _ptr(qk["k_f4"]), _ptr(qk["k_e8"]), _ptr(vq["v_f8"]), _ptr(vq["v_scale"]),
@@ -296,11 +357,26 @@ def attn_qf16_mx(q, qk: dict, vq: dict, causal=False, sm_scale=None, smooth_v=Fa
     return out
 
 
+def _check_mx_operands(qk, vq, B, H, N, d, dev, smooth_v, with_q):
+    Np = pad_len(N)
+    names = (("q", "k") if with_q else ("k",))
+    for n in names:
+        _check_tensor(qk[f"{n}_f4"], f"{n}_f4", (B, H, Np, d // 2), torch.uint8, dev)
+        _check_tensor(qk[f"{n}_e8"], f"{n}_e8", (B, H, Np, d // 32), torch.uint8, dev)
+    _check_tensor(vq["v_f8"], "v_f8", (B, H, d, Np), torch.uint8, dev)
+    _check_tensor(vq["v_scale"], "v_scale", (B, H, d), torch.float32, dev)
+    if smooth_v:
+        _check_tensor(vq["v_mean"], "v_mean", (B, H, d), torch.float32, dev)
+
+
 def debug_qk_int32(q_i8, k_i8, N, tiles) -> torch.Tensor:
     """int32 S = Qhat Khat^T tiles (128 queries x 64 keys) as the attention kernel forms them.
     tiles: list of (flat head, query tile, key tile)."""
     B, H, Np, d = q_i8.shape
     dev = q_i8.device
+    N = _check_n(N, Np)
+    _check_tensor(q_i8, "q_i8", (B, H, Np, d), torch.int8, dev)
+    _check_tensor(k_i8, "k_i8", (B, H, Np, d), torch.int8, dev)
     t = torch.tensor(list(tiles), dtype=torch.int32, device=dev).reshape(-1, 3).contiguous()
     out = torch.empty((t.shape[0], 128, 64), dtype=torch.int32, device=dev)
     rc = _load().sage_debug_qk_int32(_ptr(q_i8), _ptr(k_i8), B, H, N, d, _ptr(t), t.shape[0], _ptr(out),

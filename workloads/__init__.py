@@ -155,6 +155,33 @@ def make_inputs(cfg, seed: int | None = None, N: int | None = None, B: int | Non
     return c
 
 
+def make_accum_stress(N: int = 16384, d: int = 128, big: float = 640.0, seed: int = 11) -> dict:
+    """Input that separates an fp32 P~V accumulator from narrower ones (FP8 P~V variant).
+
+    Q = 0, so every score is 0 and every P~ * 448 is exactly 448.  K follows workload 5's
+    recipe (it does not matter).  In each V channel the first half of the tokens is +big
+    and the second half -big (the sign chosen per channel), except exactly N/16 random
+    tokens of each half, which hold U(0, 2): the running sum of P~ V climbs to about
+    N/2 * 448^2 and cancels back to a small result (|O| about 0.125), so the rounding of
+    every tile's addition at the peak magnitude shows in O.  Token 0 keeps +-big, so
+    every channel's absmax is big.  Drawn with numpy's PCG64 (seed).
+    """
+    rng = np.random.default_rng(seed)
+    sign = np.where(rng.random(d) < 0.5, 1.0, -1.0)
+    v = np.empty((N, d), np.float64)
+    v[: N // 2] = big * sign
+    v[N // 2:] = -big * sign
+    k_small = N // 16
+    for c in range(d):
+        for lo in (1, N // 2):
+            idx = lo + rng.choice(N // 2 - 1, k_small, replace=False)
+            v[idx, c] = rng.uniform(0.0, 2.0, k_small)
+    kin = make_inputs(5, B=1, H=1, N=N)
+    return dict(name="accum-stress", B=1, H=1, N=N, d=d, causal=0, variant=1, blk_q=128, blk_k=64,
+                smooth_q=0, q=np.zeros((1, 1, N, d), np.float16), k=kin["k"][..., :d].copy(),
+                v=v.astype(np.float16).reshape(1, 1, N, d))
+
+
 def attention_ops(B: int, H: int, N: int, d: int, causal: int) -> float:
     """Operation count the throughput metric uses: 4*B*H*N^2*d, halved for causal."""
     ops = 4.0 * B * H * N * N * d
