@@ -45,6 +45,8 @@ def load(path: str | None = None):
     lib.oracle_quant_mx.restype = i
     lib.oracle_qk_int32.argtypes = [p, p, i, i, i, i, i, i, p]
     lib.oracle_qk_int32.restype = i
+    lib.oracle_qsmooth_terms.argtypes = [p, i, p, i, ctypes.c_float, p, p]
+    lib.oracle_qsmooth_terms.restype = None
     lib.oracle_pad_len.argtypes = [i]
     lib.oracle_pad_len.restype = i
     for name in ("oracle_f16_decode_n", "oracle_f16_encode_n", "oracle_e4m3_decode_n",
@@ -95,6 +97,18 @@ class Oracle:
         a = np.ascontiguousarray(x, dtype=np.float64)
         out = np.empty(a.shape, dtype=np.uint8)
         self.lib.oracle_e4m3_encode_n(a.ctypes.data, a.size, out.ctypes.data)
+        return out
+
+    def qsmooth_terms(self, qmean, khat, kscale, dk) -> np.ndarray:
+        """FP8 path: the Q-smoothing terms (fp32) of the keys khat [n, d] (int8) with scales
+        dk [n] for one Q-block mean qmean [d] (fp32), kscale = sm_scale * log2(e) (fp32)."""
+        qm = np.ascontiguousarray(qmean, dtype=np.float32)
+        kh = np.ascontiguousarray(khat, dtype=np.int8)
+        dkv = np.ascontiguousarray(dk, dtype=np.float32)
+        n, d = kh.shape
+        out = np.empty(n, np.float32)
+        self.lib.oracle_qsmooth_terms(qm.ctypes.data, d, kh.ctypes.data, n, float(kscale), dkv.ctypes.data,
+                                      out.ctypes.data)
         return out
 
     def pad_len(self, N: int) -> int:

@@ -379,14 +379,145 @@ static int32_t dot_i8(const int8_t* a, const int8_t* b, int d) {
   return s;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Variants 1 and 2: P~ in FP8, decided in fp32                              */
+/* ------------------------------------------------------------------------ */
+
+/* log2(448) rounded to fp32: P~ * 448 = 2^(x - m + log2 448). */
+static const float kLog2_448f = 8.807354922057604f;
+
+/* The Q-smoothing term of key j for a Q block with mean qm[d] ([SA2]: the term q_mean . K_j
+ * added back to the scores).  It enters the fp32 decision of P~'s FP8 code, so it is
+ * formed as a reproducible fp32 number:
+ *   qm in fixed point with 28 bits under the block's largest |qm| < 2^e (e >= -100):
+ *   Qbar_c = rint(qm_c * 2^(27 - e));
+ *   B_j = sum_c Qbar_c * Khat_jc, an exact integer; b = B_j rounded once to fp32;
+ *   term = ((kscale * dK_j) * 2^(e - 27)) * b in fp32.
+ * Qbar is the mean itself up to 2^-28 of the block's largest |qm|. */
+typedef struct {
+  int64_t qbar[256];
+  float s3; /* 2^(e - 27) */
+} qmfix_t;
+
+static void qmean_fixed(const float* qm, int d, qmfix_t* f) {
+  float am = 0.0f;
+  for (int c = 0; c < d; ++c) am = fmaxf(am, fabsf(qm[c]));
+  int e = 0;
+  frexpf(am, &e); /* am in [2^(e-1), 2^e); e = 0 for am = 0 */
+  if (e < -100) e = -100;
+  for (int c = 0; c < d; ++c) f->qbar[c] = (int64_t)rintf(ldexpf(qm[c], 27 - e));
+  f->s3 = ldexpf(1.0f, e - 27);
+}
+
+static float qsmooth_term(const qmfix_t* f, const int8_t* khat, int d, float kscale, float dk) {
+  int64_t B = 0;
+  for (int c = 0; c < d; ++c) B += f->qbar[c] * (int64_t)khat[c];
+  const float b = (float)(double)B;
+  const float w = kscale * dk;
+  const float w3 = w * f->s3;
+  return w3 * b;
+}
+
+/* O row i of one head for variants 1 and 2 (fp64, before the final fp16 rounding).
+ *
+ * The FP8 code of P~ * 448 is an integer that floating point decides, so it is decided
+ * in the precision the GPU kernels use, fp32, by this sequence of correctly rounded fp32
+ * operations (fmaf: one rounding):
+ *   kscale = sm_scale * log2(e)              (sm_scale as the fp32 number the C ABI takes)
+ *   variant 1: c_j = (dQ_i * kscale) * dK_j, S_ij the exact int32 product;
+ *              with Q smoothing t_j = fmaf(S_ij, c_j, term_j), else t_j = c_j * S_ij
+ *   variant 2: c_j = kscale, S_ij the exact MX score rounded to fp32, t_j = c_j * S_ij
+ *   m = running max of t over the visible keys of the tiles so far (base-2 units)
+ *   shift = log2(448) - m
+ *   z_j = t_j + shift with Q smoothing, else fmaf(S_ij, c_j, shift)
+ *   P~_j * 448 = 2^(z_j) rounded to fp32;  code_j = E4M3(P~_j * 448), nearest even.
+ * The rest is fp64: alpha = 2^(m_old - m_new), l sums P~ (the unrounded fp32 value, R-11),
+ * O = alpha * O + sum_j code_j * Vhat_j per tile (two-level: a fresh sum per tile), and
+ * the epilogue O * dV / (448 l) (+ v_mean). */
+static void attn_row_fp8(const params_t* P, const prep_t* h, int i, double* o, double* work) {
+  const int N = P->N, d = P->d, bkv = P->bkv, Np = oracle_pad_len(N);
+  float* t = (float*)work;          /* t_j of the tile (fp32) */
+  double* p = work + bkv;           /* P~ * 448 of the tile, then its FP8 value */
+  double* inner = work + 2 * bkv;   /* the per-tile accumulator, d entries */
+  const float kscale = (float)P->sm_scale * 1.4426950408889634f;
+  const int qb = i / P->blk_q;
+  const int with_term = P->variant == 1 && P->smooth_q;
+  static __thread qmfix_t qf;
+  if (with_term) qmean_fixed(h->qmean + (size_t)qb * d, d, &qf);
+  float m = -INFINITY;
+  double l = 0.0;
+  for (int c = 0; c < d; ++c) o[c] = 0.0;
+
+  for (int j0 = 0; j0 < N; j0 += bkv) {
+    if (P->causal && j0 > i) break; /* every key of this and later tiles is masked */
+    int j1 = j0 + bkv < N ? j0 + bkv : N;
+    if (P->causal && j1 > i + 1) j1 = i + 1; /* keys > i are masked: left out of the tile */
+    float tmax = -INFINITY;
+    float Sf[256], cj[256];
+    for (int j = j0; j < j1; ++j) {
+      float S, c;
+      if (P->variant == 2) {
+        /* per 32-channel block: exact E2M1 dot product times both block scales */
+        const int nb = d / 32;
+        double acc = 0.0;
+        for (int b = 0; b < nb; ++b) {
+          double blk = 0.0;
+          for (int cc = 32 * b; cc < 32 * b + 32; ++cc)
+            blk += oracle_e2m1_decode(h->qc[(size_t)i * d + cc]) * oracle_e2m1_decode(h->kc[(size_t)j * d + cc]);
+          acc += ldexp(blk, (int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb + b] - 254);
+        }
+        S = (float)acc;
+        c = kscale;
+      } else {
+        S = (float)dot_i8(h->qi + (size_t)i * d, h->ki + (size_t)j * d, d);
+        const float dk = h->ks[j / P->blk_k];
+        c = (h->qs[i / P->q_group] * kscale) * dk;
+      }
+      Sf[j - j0] = S;
+      cj[j - j0] = c;
+      if (with_term) {
+        const float term = qsmooth_term(&qf, h->ki + (size_t)j * d, d, kscale, h->ks[j / P->blk_k]);
+        t[j - j0] = fmaf(S, c, term);
+      } else {
+        t[j - j0] = c * S;
+      }
+      if (t[j - j0] > tmax) tmax = t[j - j0];
+    }
+    /* key 0 is visible to every row, so tmax is finite and m is finite after tile 0 */
+    const float mnew = tmax > m ? tmax : m;
+    const double alpha = exp2((double)m - (double)mnew); /* m = -inf gives 0 */
+    const float shift = kLog2_448f - mnew;
+    double psum = 0.0;
+    for (int j = j0; j < j1; ++j) {
+      const float z = with_term ? t[j - j0] + shift : fmaf(Sf[j - j0], cj[j - j0], shift);
+      const float p448 = (float)exp2((double)z);
+      psum += (double)p448 / 448.0;
+      p[j - j0] = oracle_e4m3_decode(oracle_e4m3_encode((double)p448));
+    }
+    l = alpha * l + psum;
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      const uint8_t* vrow = h->vt + (size_t)c * Np;
+      for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_e4m3_decode(vrow[j]);
+      inner[c] = acc;
+    }
+    for (int c = 0; c < d; ++c) o[c] = alpha * o[c] + inner[c];
+    m = mnew;
+  }
+  for (int c = 0; c < d; ++c) o[c] = o[c] * (double)h->vs[c] / (448.0 * l) + (double)h->vm[c];
+}
+
 /* O row i of one head (fp64, before the final fp16 rounding).
- * work: 3 * bkv doubles of scratch. */
+ * work: 2 * bkv + d doubles of scratch. */
 static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, const uint16_t* k,
                      const uint16_t* v, int i, double* o, double* work) {
-  const int N = P->N, d = P->d, bkv = P->bkv, Np = oracle_pad_len(N);
+  if (P->variant >= 1 && !P->exact) {
+    attn_row_fp8(P, h, i, o, work);
+    return;
+  }
+  const int N = P->N, d = P->d, bkv = P->bkv;
   double* s = work;            /* scores of the tile */
   double* p = work + bkv;      /* P~ of the tile */
-  double* inner = work + 2 * bkv; /* variant 1: the per-tile accumulator, d entries */
   const int qb = i / P->blk_q;
   double m = -INFINITY, l = 0.0;
   for (int c = 0; c < d; ++c) o[c] = 0.0;
@@ -406,17 +537,6 @@ static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, cons
         double acc = 0.0;
         for (int c = 0; c < d; ++c)
           acc += oracle_f16_decode(q[(size_t)i * d + c]) * oracle_f16_decode(k[(size_t)j * d + c]);
-        sj = P->sm_scale * acc;
-      } else if (P->variant == 2) {
-        /* per 32-channel block: exact E2M1 dot product times both block scales */
-        const int nb = d / 32;
-        double acc = 0.0;
-        for (int b = 0; b < nb; ++b) {
-          double blk = 0.0;
-          for (int c = 32 * b; c < 32 * b + 32; ++c)
-            blk += oracle_e2m1_decode(h->qc[(size_t)i * d + c]) * oracle_e2m1_decode(h->kc[(size_t)j * d + c]);
-          acc += ldexp(blk, (int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb + b] - 254);
-        }
         sj = P->sm_scale * acc;
       } else {
         int32_t S = dot_i8(h->qi + (size_t)i * d, h->ki + (size_t)j * d, d);
@@ -450,7 +570,7 @@ static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, cons
         for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_f16_decode(v[(size_t)j * d + c]);
         o[c] = alpha * o[c] + acc;
       }
-    } else if (P->variant == 0) {
+    } else {
       /* P~ rounded to fp16, V in fp16, wide accumulation */
       for (int j = j0; j < j1; ++j) p[j - j0] = oracle_f16_decode(oracle_f16_encode(p[j - j0]));
       for (int c = 0; c < d; ++c) {
@@ -458,25 +578,10 @@ static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, cons
         for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_f16_decode(v[(size_t)j * d + c]);
         o[c] = alpha * o[c] + acc;
       }
-    } else {
-      /* P~ * 448 in FP8, V in FP8; fresh accumulator for the tile, then the
-       * outer buffer is rescaled and the tile's sum added (two-level). */
-      for (int j = j0; j < j1; ++j) p[j - j0] = oracle_e4m3_decode(oracle_e4m3_encode(p[j - j0] * 448.0));
-      for (int c = 0; c < d; ++c) {
-        double acc = 0.0;
-        const uint8_t* vrow = h->vt + (size_t)c * Np;
-        for (int j = j0; j < j1; ++j) acc += p[j - j0] * oracle_e4m3_decode(vrow[j]);
-        inner[c] = acc;
-      }
-      for (int c = 0; c < d; ++c) o[c] = alpha * o[c] + inner[c];
     }
     m = mnew;
   }
-  if (P->exact || P->variant == 0) {
-    for (int c = 0; c < d; ++c) o[c] = o[c] / l;
-  } else {
-    for (int c = 0; c < d; ++c) o[c] = o[c] * (double)h->vs[c] / (448.0 * l) + (double)h->vm[c];
-  }
+  for (int c = 0; c < d; ++c) o[c] = o[c] / l;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -551,6 +656,7 @@ static int pick_threads(int want) {
 static int check_params(const params_t* P) {
   if (P->B < 1 || P->H < 1 || P->N < 1 || P->d < 1) return -1;
   if (P->blk_q < 1 || P->blk_k < 1 || P->bkv < 1) return -1;
+  if (P->bkv > 256 || P->d > 256) return -1; /* the row functions keep one tile and one row on the stack */
   if (P->q_group < 1 || P->blk_q % P->q_group) return -1;
   if (P->causal != 0 && P->causal != 1) return -1;
   if (P->variant < 0 || P->variant > 2) return -1;
@@ -696,6 +802,16 @@ int oracle_quant_mx(const uint16_t* q, const uint16_t* k, int B, int H, int N, i
 }
 
 /* Array forms of the codecs (for tests). */
+/* The Q-smoothing terms of n keys (khat [n][d]) for one Q-block mean qm[d], as the FP8
+ * path forms them (qsmooth_term): out[j] in fp32. */
+void oracle_qsmooth_terms(const float* qm, int d, const int8_t* khat, int n, float kscale, const float* dk,
+                          float* out) {
+  qmfix_t f;
+  if (d < 1 || d > 256) return;
+  qmean_fixed(qm, d, &f);
+  for (int j = 0; j < n; ++j) out[j] = qsmooth_term(&f, khat + (size_t)j * d, d, kscale, dk[j]);
+}
+
 void oracle_e2m1_decode_n(const uint8_t* c, size_t n, double* out) {
   for (size_t i = 0; i < n; ++i) out[i] = oracle_e2m1_decode(c[i]);
 }

@@ -363,7 +363,10 @@ __device__ __forceinline__ float kscale_quarter(const float* ksc, int t, int w, 
 // units 128 times smaller: l_k = rint(r_k / (s0 * 2^-7k)), r_(k+1) = r_k - l_k*s0*2^-7k.
 // Each residual is exact in fp32 and every limb lies in [-64, 64]:
 // qmean = s3 * (2^21*l0 + 2^14*l1 + 2^7*l2 + l3) up to s3/2 per channel, s3 = s0 * 2^-21
-// (2^-27 of the block's largest mean), below the fp32 rounding of the bias itself.
+// (2^-27 of the block's largest mean), below the fp32 rounding of the bias itself.  Only
+// the last limb rounds a non-integer residual, and 128 * (higher limbs) is even, so the
+// limbs compose exactly rint(qmean * 2^(27-e)), ties to even: the fixed-point mean that
+// defines the term.
 template <int D>
 __device__ __forceinline__ void split_qmean(const float* qmean, bool valid, int8_t* sQl, float* sScale, int sb) {
   const int lane = threadIdx.x & 63;
@@ -408,8 +411,11 @@ __device__ __forceinline__ void smooth_q_bias(const int8_t* sK, const int8_t* sQ
     const i32x4 qa = *reinterpret_cast<const i32x4*>(sQl + n * D + 64 * kk + 16 * grp);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa, ka, acc, 0, 0, 0);
   }
-  // |l_k . Khat| <= 64*127*D < 2^21, so 128*L0 + L1 and 128*L2 + L3 fit in int32
-  const float b = fmaf((float)(acc[0] * 128 + acc[1]), 16384.0f, (float)(acc[2] * 128 + acc[3]));
+  // The dot product of the fixed-point mean with the key, B = 2^21 L0 + 2^14 L1 + 2^7 L2 + L3,
+  // is formed exactly and rounded once to fp32, so the term is a reproducible fp32 number
+  // (it decides FP8 codes of P~): |l_k . Khat| <= 64*127*D < 2^21, so 128*L0 + L1 and
+  // 128*L2 + L3 fit in int32, and the fp64 fma is exact (|B| < 2^43).
+  const float b = (float)__builtin_fma((double)(acc[0] * 128 + acc[1]), 16384.0, (double)(acc[2] * 128 + acc[3]));
   sBias[grp * kTileKV + 16 * wave + n] = wk * sScale[grp] * b;
 }
 

@@ -40,7 +40,12 @@ MUTANTS = {
     "q scale indexed by smoothing block": ("h->qs[i / P->q_group]", "h->qs[i / P->blk_q]"),
     "q groups span the smoothing block": ("int r0 = gi * grp, r1 = r0 + grp < N ? r0 + grp : N;",
                                           "int r0 = gi * grp, r1 = (r0 / blk + 1) * blk < N ? (r0 / blk + 1) * blk : N;"),
-    "p~ fp8 scale dropped": ("oracle_e4m3_encode(p[j - j0] * 448.0)", "oracle_e4m3_encode(p[j - j0])"),
+    "p~ fp8 scale dropped": ("const float shift = kLog2_448f - mnew;", "const float shift = 0.0f - mnew;"),
+    "fp8 q-smoothing term sign": ("t[j - j0] = fmaf(S, c, term);", "t[j - j0] = fmaf(S, c, -term);"),
+    "fp8 shift from the tile max": ("const float shift = kLog2_448f - mnew;", "const float shift = kLog2_448f - tmax;"),
+    "fp8 mean fixed point truncates": ("(int64_t)rintf(ldexpf(qm[c], 27 - e))", "(int64_t)truncf(ldexpf(qm[c], 27 - e))"),
+    "fp8 term scale exponent": ("f->s3 = ldexpf(1.0f, e - 27);", "f->s3 = ldexpf(1.0f, e - 26);"),
+    "fp8 l sums the fp8 value": ("psum += (double)p448 / 448.0;", "psum += oracle_e4m3_decode(oracle_e4m3_encode((double)p448)) / 448.0;"),
     "v mean not added back": ("/ (448.0 * l) + (double)h->vm[c];", "/ (448.0 * l);"),
     "v mean subtracted twice": ("      if (smooth_v) x = x - mean;\n      float y = x * r;",
                                 "      if (smooth_v) x = x - mean - mean;\n      float y = x * r;"),
@@ -75,7 +80,12 @@ def _battery(orc):
             yield f"lossless v{var} c{causal}", (
                 lambda var=var, causal=causal: pins.test_lossless_inputs_match_exact_attention(orc, var, causal))
     yield "single token", lambda: pins.test_closed_form_single_token_and_causal_row0(orc)
-    yield "q smoothing term", lambda: pins.test_q_smoothing_term_restores_scores(orc)
+    for var in (0, 1):
+        yield f"q smoothing term v{var}", lambda var=var: pins.test_q_smoothing_term_restores_scores(orc, var)
+    for causal in (0, 1):
+        yield f"fp8 l unrounded c{causal}", lambda causal=causal: pins.test_fp8_l_sums_the_unrounded_p(orc, causal)
+    for seed in (0, 1, 2):
+        yield f"fp8 q smoothing term {seed}", lambda seed=seed: pins.test_fp8_q_smoothing_term_bruteforce(orc, seed)
     yield "vs fp64 cfg1", lambda: pins.test_oracle_vs_fp64_attention_config1(orc)
     yield "v smoothing quant", lambda: pins.test_v_smoothing_quant_matches_fraction_bruteforce(orc)
     for causal in (0, 1):

@@ -519,15 +519,18 @@ def test_lossless_inputs_match_exact_attention(orc, variant, causal):
     assert np.max(np.abs(o[0, 0] - ref)) < 1e-12
 
 
-def test_q_smoothing_term_restores_scores(orc):
+@pytest.mark.parametrize("variant", [0, 1])
+def test_q_smoothing_term_restores_scores(orc, variant):
     """Q block = lossless residual w + shared offset u.  With Q smoothing the
-    added-back term makes s = ln2 * (w_i + u) . K_j exactly ([SA2] Q smoothing)."""
+    added-back term makes s = ln2 * (w_i + u) . K_j exactly ([SA2] Q smoothing), in the
+    fp64 path of variant 0 and in the fp32 FP8 path of variant 1 (V integers in [-7, 7]
+    with a 7 per column, so V is exact in FP8, and P~ * 448 is exact in E4M3)."""
     u = np.zeros(16)
     u[3:7] = [1.0, -1.0, 1.0, -1.0]
     q, k, v = _lossless_case(increasing=False, seed=22, u=u, kexp=(0,))
     r = orc.quant(q, k, blk_q=64, blk_k=16, smooth_q=1)
     assert np.array_equal(r["q_mean"][0, 0, 0], u.astype(np.float32))
-    o = orc.attn(q, k, v, variant=0, blk_q=64, blk_k=16, bkv=16, sm_scale=math.log(2.0), smooth_q=1)
+    o = orc.attn(q, k, v, variant=variant, blk_q=64, blk_k=16, bkv=16, sm_scale=math.log(2.0), smooth_q=1)
     qf, kf, vf = (a[0, 0].astype(np.float64) for a in (q, k, v))
     S = qf @ kf.T
     w = np.exp2(S - S.max(1, keepdims=True))
@@ -537,6 +540,88 @@ def test_q_smoothing_term_restores_scores(orc):
     S0 = (qf - u) @ kf.T
     w0 = np.exp2(S0 - S0.max(1, keepdims=True))
     assert np.max(np.abs((w0 @ vf) / w0.sum(1, keepdims=True) - ref)) > 0.1
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_fp8_l_sums_the_unrounded_p(orc, causal):
+    """R-11 in the FP8 path: l sums P~ before its FP8 rounding.  With V constant per channel
+    (7, so V is exact in FP8) and exact integer scores, O_i = 7 * sum_j E4M3(448 P~_ij) /
+    (448 * sum_j P~_ij); P~ = 2^(0.3 (S_ij - max_j S_ij)) is mostly not an E4M3 value, so O
+    differs from 7 (what a sum of the rounded P~ would give) by up to a few percent."""
+    q, k, _ = _lossless_case(increasing=False, seed=23, kexp=(0,))
+    N, d = q.shape[2], q.shape[3]
+    v = np.full((1, 1, N, d), 7.0, np.float16)
+    sm = 0.3 * math.log(2.0)
+    o = orc.attn(q, k, v, causal=causal, variant=1, blk_q=64, blk_k=16, bkv=16, sm_scale=sm, smooth_q=1)
+    S = q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T
+    if causal:
+        S = np.where(np.tril(np.ones((N, N), bool)), S, -np.inf)
+    # the running max of the 16-key tiles; P~ relative to the final max, rescaled exactly in
+    # fp64, so the closed form uses the row max directly except for the FP8 rounding, which
+    # happens against the running max of each tile
+    num = np.zeros(N)
+    den = np.zeros(N)
+    for i in range(N):
+        m = -np.inf
+        for j0 in range(0, N, 16):
+            s_t = S[i, j0:j0 + 16]
+            if not np.isfinite(s_t).any():
+                break
+            mnew = max(m, s_t[np.isfinite(s_t)].max())
+            a = 2.0 ** (0.3 * (m - mnew)) if np.isfinite(m) else 0.0
+            p448 = 448.0 * 2.0 ** (0.3 * (s_t[np.isfinite(s_t)] - mnew))
+            codes = orc.e4m3_decode(orc.e4m3_encode(p448))
+            # keep away from E4M3 midpoints, where fp32 and fp64 could round differently
+            mids = np.abs(orc.e4m3_decode(orc.e4m3_encode(p448 * (1 + 1e-6))) - codes) + \
+                np.abs(orc.e4m3_decode(orc.e4m3_encode(p448 * (1 - 1e-6))) - codes)
+            assert not mids.any()
+            num[i] = a * num[i] + codes.sum()
+            den[i] = a * den[i] + p448.sum()
+            m = mnew
+    ref = 7.0 * num / den
+    assert np.max(np.abs(o[0, 0] - ref[:, None])) < 1e-5
+    assert np.max(np.abs(ref - 7.0)) > 1e-2
+
+
+def _rne_int(x: Fraction) -> int:
+    lo = x.numerator // x.denominator
+    rem = x - lo
+    return lo + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2) else 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fp8_q_smoothing_term_bruteforce(orc, seed):
+    """The FP8 path's Q-smoothing term, against exact rational arithmetic: the block mean in
+    28-bit fixed point under its largest |q_mean| (nearest, ties to even), the exact integer
+    dot product with the codes, one rounding to fp32, then the fp32 products
+    (kscale * dK) * 2^(e-27) * b.  Bit-equal; and within fp32 rounding of the exact term
+    kscale * dK * (q_mean . Khat)."""
+    rng = np.random.default_rng(40 + seed)
+    d, n = 64, 40
+    mags = [1.0, 3e-3, 40.0][seed]
+    qm = (rng.standard_normal(d) * mags * rng.choice([1.0, 1e-3, 10.0], d)).astype(np.float32)
+    qm[5] = 0.0
+    kh = rng.integers(-127, 128, (n, d)).astype(np.int8)
+    dk = (rng.random(n) * 0.05 + 1e-3).astype(np.float32)
+    kscale = np.float32(1.0 / math.sqrt(d)) * np.float32(1.4426950408889634)
+    got = orc.qsmooth_terms(qm, kh, kscale, dk)
+    am = float(np.abs(qm).max())
+    e = math.frexp(am)[1]  # am in [2^(e-1), 2^e)
+    e = max(e, -100)
+    qbar = [_rne_int(Fraction(float(x)) * Fraction(2) ** (27 - e)) for x in qm]
+    for j in range(n):
+        B = sum(qbar[c] * int(kh[j, c]) for c in range(d))
+        b = rn32(Fraction(B))
+        w = rn32(Fraction(float(kscale)) * Fraction(float(dk[j])))
+        w3 = rn32(Fraction(float(w)) * Fraction(2) ** (e - 27))
+        want = rn32(Fraction(float(w3)) * Fraction(float(b)))
+        assert got[j].view(np.uint32) == np.float32(want).view(np.uint32), j
+        exact = float(kscale) * float(dk[j]) * float(np.dot(qm.astype(np.float64), kh[j].astype(np.float64)))
+        # four fp32 roundings (2^-24 each), and the fixed point: at most 2^-27 * 2 * am per channel
+        w_exact = float(kscale) * float(dk[j])
+        bound = w_exact * (2.0 ** -21 * float(np.abs(qm).astype(np.float64) @ np.abs(kh[j]))
+                           + 2.0 ** -26 * am * float(np.abs(kh[j]).sum()))
+        assert abs(float(got[j]) - exact) <= bound, j
 
 
 # --------------------------------------------------------------------------
