@@ -11,7 +11,12 @@
  *    Per-thread INT4 Quantization" (abstract): Q is smoothed as well, P~ and V
  *    are quantised to FP8, and P~ V uses two-level accumulation.  Here Q/K stay
  *    INT8 in variants 0 and 1 (one fp32 scale per block of tokens, or per group
- *    of rows);
+ *    of rows).  The FP8 matrix instruction accumulates in fp32; the kernel lets it
+ *    add each key tile's products straight into O, which is the fp32 outer buffer of
+ *    the two-level scheme (a stress input on which a 22-bit truncating or a 20-bit
+ *    accumulator would miss the O tolerance pins this).  The FP8 code of P~ * 448 is
+ *    decided in fp32 by a fixed sequence of operations (scores, running max, exp2),
+ *    so the codes are reproducible;
  *   "SageAttention3: Microscaling FP4 Attention for Inference and An Exploration
  *    of 8-Bit Training" (abstract): FP4 attention on matrix units, taken here as
  *    variant 2 (MXFP4 Q K^T on the scaled FP4 MFMA, P~ V as variant 1).
@@ -53,7 +58,8 @@ enum {
 
 enum {
   SAGE_VARIANT_INT8QK_FP16PV = 0, /* SageAttention: INT8 Q K^T, FP16 P~ V (fp32 accumulation) */
-  SAGE_VARIANT_INT8QK_FP8PV = 1,  /* SageAttention2-style: + Q smoothing, FP8 P~ and V, two-level accumulation */
+  SAGE_VARIANT_INT8QK_FP8PV = 1,  /* SageAttention2-style: + Q smoothing, FP8 P~ and V; each key tile's
+                                     P~ V products summed by the matrix unit into the fp32 O */
   SAGE_VARIANT_MXFP4QK_FP8PV = 2  /* SageAttention3-style FP4 scores: per-token MXFP4 Q and K' (OCP
                                      microscaling, blocks of 32 channels), P~ V as variant 1; no Q
                                      smoothing */
