@@ -157,6 +157,25 @@ int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B
                      size_t ws_bytes, void* stream);
 
 /*
+ * sage_attn_fwd_ex for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, same
+ * kernels and the same result as sage_attn_fwd_ex with a workspace, but the workspace is
+ * the library's own array of SAGE_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, which each GPU
+ * the library runs on holds until the process ends.  Nothing is allocated or freed per
+ * call.  Shapes whose workspace (sage_workspace_bytes) exceeds the array return
+ * SAGE_ERR_WORKSPACE before any launch (e.g. B*H = 128 heads of N = 4096, d = 128, variant
+ * 0 fit; B*H = 64 heads of N = 32768, d = 128, variant 1 do not).  All calls on one GPU
+ * share its array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give wrong results; calls in order on one stream are safe.  The
+ * array keeps the last call's contents; no pass reads workspace it has not written in
+ * the same call.  The first call on a device looks the array's address up (no
+ * allocation).
+ */
+#define SAGE_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                          int causal, float sm_scale, int variant, const sage_params* p, void* stream);
+
+/*
  * The attention kernel alone, on tensors sage_quant_qk / sage_quant_v(_ex) produced
  * (same p).  Variant 0 reads v (fp16); variant 1 reads v_f8 / v_scale, with
  * smooth_q q_mean, and with smooth_v v_mean (16-byte aligned, [B,H,d]).  Pointers a

@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["attn", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
+__all__ = ["attn", "attn_noalloc", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
            "attn_qf16_mx",
            "debug_qk_int32", "workspace_bytes",
            "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4"]
@@ -71,6 +71,7 @@ def _load():
         "sage_attn_fwd_prequant_mx": ([P, P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_attn_fwd_qf16_mx": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
+        "sage_attn_fwd_noalloc": ([P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
         "sage_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -205,6 +206,33 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
                               float(sm_scale), int(variant), ctypes.byref(p), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(q.device))
     _check(rc, "sage_attn_fwd_ex")
+    return out
+
+
+# Workspace of attn_noalloc: the library's own array per GPU (SAGE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
+
+
+def attn_noalloc(q, k, v, out, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128, blk_k=64,
+                 smooth_k=True, smooth_q=None, smooth_v=False, q_group=0):
+    """attn() without any device allocation: the caller passes `out` (a contiguous fp16
+    [B, H, N, d] tensor), and the library uses its own per-GPU workspace array
+    (sage_attn_fwd_noalloc).  Shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES raise
+    SageError.  Calls that overlap in time on one GPU share that array and race."""
+    B, H, N, d = _check_qkv(q, k, v)
+    if out is None:
+        raise ValueError("attn_noalloc needs a caller-allocated out")
+    out = _check_out(out, q.shape, q.device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if smooth_q is None:
+        smooth_q = variant == VARIANT_FP8PV
+    if q.numel() == 0:
+        return out
+    p = _params(blk_q, blk_k, smooth_k, smooth_q, smooth_v, q_group)
+    rc = _load().sage_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, int(bool(causal)),
+                                       float(sm_scale), int(variant), ctypes.byref(p), _stream(q.device))
+    _check(rc, "sage_attn_fwd_noalloc")
     return out
 
 

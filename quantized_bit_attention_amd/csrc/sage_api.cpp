@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sage.h"
 #include "sage_internal.h"
@@ -270,6 +271,34 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   return ok();
 }
 
+// Workspace of sage_attn_fwd_noalloc: one array per GPU, held for the life of the process.
+// Host code never uses the array's name as an address: on the host it is only a handle,
+// and its device address comes from hipGetSymbolAddress (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[SAGE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per device with
+// that device current.  Returns SAGE_OK and sets *out, or an error status.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SAGE_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(SAGE_ERR_HIP, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +375,30 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, i
 int sage_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
                      float sm_scale, int variant, const sage_params* p, void* ws, size_t ws_bytes, void* stream) {
   return attn_common(q, k, v, o, B, H, N, d, causal, sm_scale, variant, p, ws, ws_bytes, stream);
+}
+
+int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                          int causal, float sm_scale, int variant, const sage_params* pp, void* stream) {
+  int rc;
+  // the argument checks of sage_attn_fwd_ex, then the size check, before any HIP call
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (!valid_variant(variant)) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0, 1 or 2");
+  Params p;
+  if ((rc = read_params(pp, variant, &p))) return rc;
+  const size_t need = layout(B, H, N, d, variant, p).total;
+  if (need > (size_t)SAGE_NOALLOC_SCRATCH_BYTES)
+    return fail(SAGE_ERR_WORKSPACE, "this shape needs %zu bytes of workspace; sage_attn_fwd_noalloc has %zu",
+                need, (size_t)SAGE_NOALLOC_SCRATCH_BYTES);
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k, 16, "k")) || (rc = check_ptr(v, 16, "v")) ||
+      (rc = check_ptr(o, 16, "o")))
+    return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  return attn_common(q, k, v, o, B, H, N, d, causal, sm_scale, variant, pp, ws, (size_t)SAGE_NOALLOC_SCRATCH_BYTES,
+                     stream);
 }
 
 int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* q_scale, const float* k_scale,
