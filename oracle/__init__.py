@@ -45,6 +45,8 @@ def load(path: str | None = None):
     lib.oracle_quant_mx.restype = i
     lib.oracle_qk_int32.argtypes = [p, p, i, i, i, i, i, i, p]
     lib.oracle_qk_int32.restype = i
+    lib.oracle_attn_bwd.argtypes = [p, p, p, p, p, i, i, i, i, i, d, i, i, i, i, i, p, p, p, i]
+    lib.oracle_attn_bwd.restype = i
     lib.oracle_qsmooth_terms.argtypes = [p, i, p, i, ctypes.c_float, p, p]
     lib.oracle_qsmooth_terms.restype = None
     lib.oracle_pad_len.argtypes = [i]
@@ -197,6 +199,26 @@ class Oracle:
             raise ValueError("oracle_attn_rows: bad arguments")
         self.threads_used = used.value
         return out
+
+    def attn_bwd(self, q, k, v, o, dout, causal=0, sm_scale=None, blk_q=128, blk_k=64, smooth_k=1, smooth_v=1,
+                 exact=0, nthreads=0) -> dict:
+        """dq, dk, dv ([B, H, N, d] fp64) of the 8-bit forward (variant-0 scores) given its output
+        o and the output gradient dout (fp16 arrays).  exact=1: no quantisation or rounding."""
+        q, k, v, o, dout = _f16(q), _f16(k), _f16(v), _f16(o), _f16(dout)
+        B, H, N, d = q.shape
+        for t in (k, v, o, dout):
+            if t.shape != q.shape:
+                raise ValueError("q, k, v, o, dout must share one shape")
+        if sm_scale is None:
+            sm_scale = 1.0 / np.sqrt(d)
+        r = {n: np.empty((B, H, N, d), np.float64) for n in ("dq", "dk", "dv")}
+        rc = self.lib.oracle_attn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data, dout.ctypes.data,
+                                      B, H, N, d, int(causal), float(sm_scale), blk_q, blk_k, int(smooth_k),
+                                      int(smooth_v), int(exact), r["dq"].ctypes.data, r["dk"].ctypes.data,
+                                      r["dv"].ctypes.data, nthreads)
+        if rc:
+            raise ValueError("oracle_attn_bwd: bad arguments")
+        return r
 
     def attn(self, q, k, v, **kw) -> np.ndarray:
         """O for every row, [B, H, N, d] fp64."""

@@ -40,6 +40,10 @@
  *      V' = V - v_mean (token mean per channel)
  *   9. O / l (variant 1 also * dV / 448, plus v_mean with V smoothing: the rows
  *      of P~ / l sum to one, so the mean comes back out unchanged)
+ * The backward (oracle_attn_bwd, [SA3]: 8-bit attention for the backward too) returns
+ * dQ, dK, dV of the variant-0 forward in FlashAttention-2's order, with dP = dO V^T in
+ * INT8 (per-token scales, V smoothed) and the products with P and dS on fp16 operands;
+ * its readings are listed where it is defined.
  * Variant 2 ([SA3]) replaces steps 3-5: Q and K' are quantised per token to MXFP4
  * (blocks of 32 channels), S = sum over blocks of 2^(eq + ek) * (E2M1 dot product),
  * s = sm_scale * S (no Q smoothing); steps 6-9 are those of variant 1.
@@ -802,6 +806,231 @@ int oracle_quant_mx(const uint16_t* q, const uint16_t* k, int B, int H, int N, i
 }
 
 /* Array forms of the codecs (for tests). */
+/* ------------------------------------------------------------------------ */
+/* Backward: dQ, dK, dV of the 8-bit forward ([SA3]: 8-bit attention for      */
+/* both forward and backward propagation)                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages say only that the backward is 8-bit as well.  Readings (each also in the
+ * design notes):
+ *  - The backward differentiates O = softmax(s) V at the forward's scores s: the variant-0
+ *    scores (smoothed K, per-block INT8 Q and K, exact int32 S, dequantised); the
+ *    quantisers pass gradients straight through (dS/dQ uses Q itself, dS/dK uses K).
+ *  - FlashAttention-2's backward order ([FA]): P = exp(s - L) with L the row log-sum-exp,
+ *    D_i = sum_c dO_ic O_ic with O the forward output, dS = P * (dP - D).
+ *  - 8-bit where SageAttention puts 8 bits, on the score-shaped product: dP = dO V^T
+ *    (a dot product over the head dimension, like Q K^T) takes dO and V in INT8 with one
+ *    scale per token (absmax / 127, nearest even, the forward's rule) and exact int32
+ *    sums.  V is smoothed first (its exact token mean per channel is subtracted, the K
+ *    rule): that shifts every dP_ij of row i by dO_i . vmean, and D_i is shifted by the
+ *    same amount, so dS does not change in exact arithmetic.
+ *  - dQ uses the smoothed K' = K - kmean (the forward's K smoothing, fp32, rounded to fp16
+ *    as the operand): in exact arithmetic every row of dS sums to zero, so dS K' = dS K,
+ *    and K' keeps a channel offset of K from multiplying the rounding of dS.
+ *  - The products with P or dS (dV = P^T dO, dK = dS^T Q, dQ = dS K') keep FP16 operands
+ *    and fp32 accumulation, as SageAttention keeps P~ V in FP16: P is rounded to fp16 as
+ *    2^8 P, and dS as sigma dS with sigma = 2^(14 - e), where 2^e is the first power of
+ *    two above B = 2 max_i |dO_i| max_j |V'_j| (Euclidean norms of the rows), which bounds
+ *    |dS| (|dS_ij| <= |dP_ij - D_i| <= max_j dP_ij - min_j dP_ij): the scaled operands stay
+ *    in fp16's normal range; both scales are undone after the sums.
+ *  - Gradients are returned unrounded (fp64 here, fp32 on the GPU).
+ * exact = 1 turns every quantisation and rounding off (fp64 throughout): the textbook
+ * attention backward, which the pins compare with autograd.
+ */
+typedef struct {
+  int B, H, N, d, causal, blk_q, blk_k, smooth_k, smooth_v, exact;
+  double sm_scale;
+} bwdparams_t;
+
+static void bwd_head(const bwdparams_t* P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const uint16_t* o, const uint16_t* dout, double* dq, double* dk, double* dv) {
+  const int N = P->N, d = P->d, Np = oracle_pad_len(N);
+  const int nqb = (N + P->blk_q - 1) / P->blk_q, nkb = (N + P->blk_k - 1) / P->blk_k;
+  int8_t *qi = NULL, *ki = NULL, *vi = NULL, *gi = NULL;
+  float *qs = NULL, *ks = NULL, *vs = NULL, *gs = NULL, *vmean = NULL, *vsm = NULL, *kmean = NULL;
+  double* ksm = NULL; /* K' rounded to fp16 */
+  double* s = (double*)malloc(sizeof(double) * (size_t)N);
+  double* pr = (double*)malloc(sizeof(double) * (size_t)N);
+  double* ds = (double*)malloc(sizeof(double) * (size_t)N);
+  for (size_t e = 0; e < (size_t)N * d; ++e) dq[e] = dk[e] = dv[e] = 0.0;
+
+  if (!P->exact) {
+    /* forward's Q and K codes (variant 0: K smoothed over all tokens, Q not smoothed) */
+    qi = (int8_t*)malloc((size_t)Np * d);
+    ki = (int8_t*)malloc((size_t)Np * d);
+    qs = (float*)malloc(sizeof(float) * (size_t)nqb);
+    ks = (float*)malloc(sizeof(float) * (size_t)nkb);
+    kmean = (float*)calloc((size_t)d, sizeof(float));
+    quant_head(k, N, Np, d, P->blk_k, P->blk_k, P->smooth_k ? 1 : 0, ki, ks, P->smooth_k ? kmean : NULL, NULL);
+    /* K' in fp16, the operand of dQ */
+    ksm = (double*)malloc(sizeof(double) * (size_t)N * d);
+    for (int t = 0; t < N; ++t)
+      for (int c = 0; c < d; ++c) {
+        const float x = (float)oracle_f16_decode(k[(size_t)t * d + c]) - kmean[c];
+        ksm[(size_t)t * d + c] = oracle_f16_decode(oracle_f16_encode((double)x));
+      }
+    quant_head(q, N, Np, d, P->blk_q, P->blk_q, 0, qi, qs, NULL, NULL);
+    /* V' = V - vmean (fp32), then V' and dO in INT8 per token */
+    vmean = (float*)calloc((size_t)d, sizeof(float));
+    vsm = (float*)malloc(sizeof(float) * (size_t)N * d);
+    if (P->smooth_v)
+      for (int c = 0; c < d; ++c) vmean[c] = exact_mean(v, d, 0, N, c);
+    for (int t = 0; t < N; ++t)
+      for (int c = 0; c < d; ++c) {
+        const float x = (float)oracle_f16_decode(v[(size_t)t * d + c]);
+        vsm[(size_t)t * d + c] = P->smooth_v ? x - vmean[c] : x;
+      }
+    vi = (int8_t*)malloc((size_t)N * d);
+    gi = (int8_t*)malloc((size_t)N * d);
+    vs = (float*)malloc(sizeof(float) * (size_t)N);
+    gs = (float*)malloc(sizeof(float) * (size_t)N);
+    float* row = (float*)malloc(sizeof(float) * (size_t)d);
+    for (int t = 0; t < N; ++t) {
+      vs[t] = quant_block_i8(vsm + (size_t)t * d, (size_t)d, vi + (size_t)t * d);
+      for (int c = 0; c < d; ++c) row[c] = (float)oracle_f16_decode(dout[(size_t)t * d + c]);
+      gs[t] = quant_block_i8(row, (size_t)d, gi + (size_t)t * d);
+    }
+    free(row);
+  }
+
+  /* the fp16 operand scales: 2^8 for P; sigma = 2^(14 - e) for dS */
+  double sigma = 1.0;
+  const double pscale = 256.0;
+  if (!P->exact) {
+    double gmax = 0.0, vmax = 0.0;
+    for (int t = 0; t < N; ++t) {
+      double a = 0.0, b = 0.0;
+      for (int c = 0; c < d; ++c) {
+        const double g = oracle_f16_decode(dout[(size_t)t * d + c]);
+        const double w = (double)vsm[(size_t)t * d + c];
+        a += g * g;
+        b += w * w;
+      }
+      if (sqrt(a) > gmax) gmax = sqrt(a);
+      if (sqrt(b) > vmax) vmax = sqrt(b);
+    }
+    const double bound = 2.0 * gmax * vmax;
+    if (bound > 0.0) {
+      int e;
+      frexp(bound, &e); /* bound in [2^(e-1), 2^e) */
+      sigma = ldexp(1.0, 14 - e);
+    }
+  }
+
+  for (int i = 0; i < N; ++i) {
+    const int jend = P->causal ? i + 1 : N;
+    /* scores, their log-sum-exp, P */
+    double m = -INFINITY;
+    for (int j = 0; j < jend; ++j) {
+      double sj;
+      if (P->exact) {
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c)
+          acc += oracle_f16_decode(q[(size_t)i * d + c]) * oracle_f16_decode(k[(size_t)j * d + c]);
+        sj = P->sm_scale * acc;
+      } else {
+        const int32_t S = dot_i8(qi + (size_t)i * d, ki + (size_t)j * d, d);
+        sj = P->sm_scale * (double)qs[i / P->blk_q] * (double)ks[j / P->blk_k] * (double)S;
+      }
+      s[j] = sj;
+      if (sj > m) m = sj;
+    }
+    double lsum = 0.0;
+    for (int j = 0; j < jend; ++j) lsum += exp(s[j] - m);
+    const double L = m + log(lsum);
+    /* D_i (with V smoothed, the same shift dO_i . vmean as every dP_ij of the row) */
+    double D = 0.0;
+    for (int c = 0; c < d; ++c) {
+      const double g = oracle_f16_decode(dout[(size_t)i * d + c]);
+      D += g * oracle_f16_decode(o[(size_t)i * d + c]);
+      if (!P->exact && P->smooth_v) D -= g * (double)vmean[c];
+    }
+    for (int j = 0; j < jend; ++j) {
+      const double p = exp(s[j] - L);
+      double dp;
+      if (P->exact) {
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c)
+          acc += oracle_f16_decode(dout[(size_t)i * d + c]) * oracle_f16_decode(v[(size_t)j * d + c]);
+        dp = acc;
+      } else {
+        const int32_t S = dot_i8(gi + (size_t)i * d, vi + (size_t)j * d, d);
+        dp = (double)gs[i] * (double)vs[j] * (double)S;
+      }
+      const double dsv = p * (dp - D);
+      if (P->exact) {
+        pr[j] = p;
+        ds[j] = dsv;
+      } else {
+        pr[j] = oracle_f16_decode(oracle_f16_encode(pscale * p)) / pscale;
+        ds[j] = oracle_f16_decode(oracle_f16_encode(sigma * dsv)) / sigma;
+      }
+    }
+    /* dQ_i = sm_scale sum_j dS_ij K'_j;  dK_j += sm_scale dS_ij Q_i;  dV_j += P_ij dO_i */
+    for (int j = 0; j < jend; ++j)
+      for (int c = 0; c < d; ++c) {
+        const double kv = P->exact ? oracle_f16_decode(k[(size_t)j * d + c]) : ksm[(size_t)j * d + c];
+        const double qv = oracle_f16_decode(q[(size_t)i * d + c]);
+        const double gv = oracle_f16_decode(dout[(size_t)i * d + c]);
+        dq[(size_t)i * d + c] += P->sm_scale * ds[j] * kv;
+        dk[(size_t)j * d + c] += P->sm_scale * ds[j] * qv;
+        dv[(size_t)j * d + c] += pr[j] * gv;
+      }
+  }
+  free(s); free(pr); free(ds);
+  free(qi); free(ki); free(vi); free(gi); free(qs); free(ks); free(vs); free(gs); free(vmean); free(vsm);
+  free(kmean); free(ksm);
+}
+
+typedef struct {
+  const bwdparams_t* P;
+  const uint16_t *q, *k, *v, *o, *dout;
+  double *dq, *dk, *dv;
+  int G, next;
+  pthread_mutex_t mu;
+} bwdjob_t;
+
+static void* bwd_worker(void* arg) {
+  bwdjob_t* J = (bwdjob_t*)arg;
+  const size_t hs = (size_t)J->P->N * J->P->d;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int g = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (g >= J->G) break;
+    bwd_head(J->P, J->q + g * hs, J->k + g * hs, J->v + g * hs, J->o + g * hs, J->dout + g * hs, J->dq + g * hs,
+             J->dk + g * hs, J->dv + g * hs);
+  }
+  return NULL;
+}
+
+/*
+ * dQ, dK, dV ([B][H][N][d] fp64 each) of the forward at q, k, v given its output o and
+ * the output gradient dout (all [B][H][N][d] fp16 bits).  Heads run on a thread pool;
+ * each head is computed sequentially, so the result does not depend on threading.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                    const uint16_t* dout, int B, int H, int N, int d, int causal, double sm_scale, int blk_q,
+                    int blk_k, int smooth_k, int smooth_v, int exact, double* dq, double* dk, double* dv,
+                    int nthreads) {
+  if (B < 1 || H < 1 || N < 1 || d < 1 || d > 256 || blk_q < 1 || blk_k < 1) return -1;
+  if ((causal != 0 && causal != 1) || (smooth_k != 0 && smooth_k != 1) || (smooth_v != 0 && smooth_v != 1) ||
+      (exact != 0 && exact != 1))
+    return -1;
+  if (!(sm_scale > 0.0) || !isfinite(sm_scale)) return -1;
+  bwdparams_t P = {B, H, N, d, causal, blk_q, blk_k, smooth_k, smooth_v, exact, sm_scale};
+  bwdjob_t J = {&P, q, k, v, o, dout, dq, dk, dv, B * H, 0, PTHREAD_MUTEX_INITIALIZER};
+  int nt = pick_threads(nthreads);
+  if (nt > J.G) nt = J.G;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+  for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, bwd_worker, &J);
+  for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+  free(th);
+  return 0;
+}
+
 /* The Q-smoothing terms of n keys (khat [n][d]) for one Q-block mean qm[d], as the FP8
  * path forms them (qsmooth_term): out[j] in fp32. */
 void oracle_qsmooth_terms(const float* qm, int d, const int8_t* khat, int n, float kscale, const float* dk,

@@ -13,6 +13,7 @@ import pytest
 
 import oracle as oracle_pkg
 from oracle import Oracle
+from tests import test_oracle_bwd_pins as bw
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
@@ -56,6 +57,23 @@ MUTANTS = {
     "mx k not smoothed": ("quant_head_mx(k, N, Np, d, P->smooth_k ? 1 : 0,", "quant_head_mx(k, N, Np, d, 0,"),
     "v absmax before smoothing": ("      if (smooth_v) x = x - mean;\n      a = fmaxf(a, fabsf(x));",
                                   "      a = fmaxf(a, fabsf(x));"),
+    # backward
+    "bwd D without the V-mean shift": ("if (!P->exact && P->smooth_v) D -= g * (double)vmean[c];", ""),
+    "bwd dS sign": ("const double dsv = p * (dp - D);", "const double dsv = p * (D - dp);"),
+    "bwd dK uses K": ("dk[(size_t)j * d + c] += P->sm_scale * ds[j] * qv;",
+                      "dk[(size_t)j * d + c] += P->sm_scale * ds[j] * kv;"),
+    "bwd dQ without sm_scale": ("dq[(size_t)i * d + c] += P->sm_scale * ds[j] * kv;",
+                                "dq[(size_t)i * d + c] += ds[j] * kv;"),
+    "bwd P not normalised": ("const double L = m + log(lsum);", "const double L = m;"),
+    "bwd dP scale of V dropped": ("dp = (double)gs[i] * (double)vs[j] * (double)S;", "dp = (double)gs[i] * (double)S;"),
+    "bwd sigma not undone": ("ds[j] = oracle_f16_decode(oracle_f16_encode(sigma * dsv)) / sigma;",
+                             "ds[j] = oracle_f16_decode(oracle_f16_encode(sigma * dsv));"),
+    "bwd sigma from V only": ("const double bound = 2.0 * gmax * vmax;", "const double bound = 2.0 * vmax;"),
+    "bwd dV uses the row of dO of the key": ("dv[(size_t)j * d + c] += pr[j] * gv;",
+                                             "dv[(size_t)j * d + c] += pr[j] * oracle_f16_decode(dout[(size_t)j * d + c]);"),
+    "bwd causal mask dropped": ("const int jend = P->causal ? i + 1 : N;", "const int jend = N;"),
+    "bwd dQ uses unsmoothed K": ("const float x = (float)oracle_f16_decode(k[(size_t)t * d + c]) - kmean[c];",
+                                 "const float x = (float)oracle_f16_decode(k[(size_t)t * d + c]);"),
 }
 
 
@@ -98,6 +116,14 @@ def _battery(orc):
     for causal in (0, 1):
         yield f"mx lossless c{causal}", lambda causal=causal: pins.test_mx_lossless_inputs_match_exact_attention(orc, causal)
     yield "mx k smoothing", lambda: pins.test_mx_k_smoothing_removes_the_channel_offset_error(orc)
+    for a in [(37, 32, 0), (37, 32, 1)]:
+        yield f"bwd exact {a}", lambda a=a: bw.test_exact_mode_equals_autograd(orc, *a)
+    for causal in (0, 1):
+        yield f"bwd quality c{causal}", lambda causal=causal: bw.test_quantised_gradients_track_exact_ones(orc, causal)
+        yield f"bwd const v c{causal}", lambda causal=causal: bw.test_constant_v_gives_zero_score_gradients(orc, causal)
+    yield "bwd single token", lambda: bw.test_single_token(orc)
+    yield "bwd v offset", lambda: bw.test_v_offset_does_not_change_the_8bit_gradients(orc)
+    yield "bwd dout scaling", lambda: bw.test_power_of_two_scaling_of_dout(orc)
 
 
 @pytest.fixture(scope="module")
