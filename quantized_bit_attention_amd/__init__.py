@@ -17,7 +17,7 @@ import os
 
 import torch
 
-__all__ = ["attn", "attn_noalloc", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
+__all__ = ["attn", "attn_noalloc", "attn_fwd_train", "attn_bwd", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
            "attn_qf16_mx",
            "debug_qk_int32", "workspace_bytes",
            "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4"]
@@ -72,6 +72,9 @@ def _load():
         "sage_attn_fwd_qf16_mx": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
         "sage_attn_fwd_noalloc": ([P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
+        "sage_attn_fwd_train": ([P, P, P, P, P, I, I, I, I, I, F, PP, P, S, P], I),
+        "sage_attn_bwd_workspace_bytes": ([I, I, I, I, PP], S),
+        "sage_attn_bwd": ([P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P, S, P], I),
         "sage_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -234,6 +237,56 @@ def attn_noalloc(q, k, v, out, causal=False, sm_scale=None, variant=VARIANT_FP16
                                        float(sm_scale), int(variant), ctypes.byref(p), _stream(q.device))
     _check(rc, "sage_attn_fwd_noalloc")
     return out
+
+
+def attn_fwd_train(q, k, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, smooth_k=True, out=None, lse=None,
+                   workspace=None):
+    """The variant-0 forward for training: returns (o, lse), lse [B, H, N] fp32 the natural-log
+    row log-sum-exp of the dequantised scores, which attn_bwd takes.  blk_q must be 64 or 128."""
+    B, H, N, d = _check_qkv(q, k, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    out = _check_out(out, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32, q.device)
+    if q.numel() == 0:
+        return out, lse
+    p = _params(blk_q, blk_k, smooth_k, False, False, 0)
+    lib = _load()
+    nbytes = lib.sage_workspace_bytes(B, H, N, d, VARIANT_FP16PV, ctypes.byref(p))
+    if nbytes == 0:
+        _check(-1, "sage_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.sage_attn_fwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, int(bool(causal)),
+                                 float(sm_scale), ctypes.byref(p), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(q.device))
+    _check(rc, "sage_attn_fwd_train")
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, causal=False, sm_scale=None, blk_q=128, blk_k=64, smooth_k=True,
+             workspace=None) -> dict:
+    """dq, dk, dv ([B, H, N, d] fp32) of the 8-bit forward at q, k, v given its output o, the
+    output gradient dout (fp16 like q) and the lse of attn_fwd_train (same options)."""
+    B, H, N, d = _check_qkv(q, k, v, o, dout)
+    _check_tensor(lse, "lse", (B, H, N), torch.float32, q.device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    r = {n: torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) for n in ("dq", "dk", "dv")}
+    if q.numel() == 0:
+        return r
+    p = _params(blk_q, blk_k, smooth_k, False, False, 0)
+    lib = _load()
+    nbytes = lib.sage_attn_bwd_workspace_bytes(B, H, N, d, ctypes.byref(p))
+    if nbytes == 0:
+        _check(-1, "sage_attn_bwd_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.sage_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(r["dq"]), _ptr(r["dk"]),
+                           _ptr(r["dv"]), B, H, N, d, int(bool(causal)), float(sm_scale), ctypes.byref(p), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(q.device))
+    _check(rc, "sage_attn_bwd")
+    return r
 
 
 def quant_qk(q, k, blk_q=128, blk_k=64, smooth_k=True, smooth_q=False, q_group=0) -> dict:

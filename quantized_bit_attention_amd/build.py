@@ -7,8 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage.so")
-SOURCES = ["sage_api.cpp", "sage_quant.hip", "sage_attn.hip"]
-HEADERS = ["sage_device.h", "sage_internal.h"]
+SOURCES = ["sage_api.cpp", "sage_quant.hip", "sage_attn.hip", "sage_bwd.hip"]
+HEADERS = ["sage_device.h", "sage_internal.h", "sage_tiles.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

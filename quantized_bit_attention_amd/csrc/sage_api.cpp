@@ -208,7 +208,8 @@ int run_quant_qk(const void* q, const void* k, int B, int H, int N, int d, const
 }
 
 int attn_common(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int causal,
-                float sm_scale, int variant, const sage_params* pp, void* ws, size_t ws_bytes, void* stream) {
+                float sm_scale, int variant, const sage_params* pp, void* ws, size_t ws_bytes, void* stream,
+                float* lse = nullptr) {
   int rc;
   if ((rc = check_shape(B, H, N, d))) return rc;
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -266,9 +267,53 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   a.v_scale = variant != 0 ? at<float>(ws, L.v_scale) : nullptr;
   a.v_mean = p.smooth_v ? at<float>(ws, L.v_mean) : nullptr;
   a.o = (uint16_t*)o;
+  a.lse = lse;
   e = sage::launch_attn(d, variant, causal, p.smooth_q, a, st);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
+}
+
+// Backward workspace (each piece 256-byte aligned).
+struct BwdLayout {
+  size_t ksum, vsum, vmax, vmin, q_i8, k_i8, q_scale, k_scale, k_mean, v_i8, do_i8, v_scale, do_scale, dvec, lse2,
+      nrm, kp, total;
+};
+
+BwdLayout bwd_layout(int B, int H, int N, int d, const Params& p) {
+  const size_t G = (size_t)B * H, Np = pad_len(N), ns = ceil_div(N, sage::kStatRows);
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  L.ksum = take(G * ns * d * sizeof(long long));
+  L.vsum = take(G * ns * d * sizeof(long long));
+  L.vmax = take(G * ns * d * sizeof(float));
+  L.vmin = take(G * ns * d * sizeof(float));
+  L.q_i8 = take(G * Np * d);
+  L.k_i8 = take(G * Np * d);
+  L.q_scale = take(G * ceil_div(N, p.blk_q) * sizeof(float));
+  L.k_scale = take(G * ceil_div(N, p.blk_k) * sizeof(float));
+  L.k_mean = take(G * d * sizeof(float));
+  L.v_i8 = take(G * Np * d);
+  L.do_i8 = take(G * Np * d);
+  L.v_scale = take(G * Np * sizeof(float));
+  L.do_scale = take(G * Np * sizeof(float));
+  L.dvec = take(G * Np * sizeof(float));
+  L.lse2 = take(G * Np * sizeof(float));
+  L.nrm = take(G * (Np / 64) * 2 * sizeof(float));
+  L.kp = take(G * Np * d * sizeof(uint16_t));
+  L.total = off;
+  return L;
+}
+
+// The backward differentiates the variant-0 forward: per-block Q scales of 64 or 128 rows
+// (a 64-row query tile lies in one block), no Q smoothing, one Q scale per block.
+int read_bwd_params(const sage_params* pp, Params* p) {
+  int rc;
+  if ((rc = read_params(pp, SAGE_VARIANT_INT8QK_FP16PV, p))) return rc;
+  if (p->blk_q < 64) return fail(SAGE_ERR_UNSUPPORTED, "the backward needs blk_q = 64 or 128 (got %d)", p->blk_q);
+  if (p->smooth_q) return fail(SAGE_ERR_UNSUPPORTED, "the backward differentiates the forward without Q smoothing");
+  if (p->q_group != p->blk_q) return fail(SAGE_ERR_UNSUPPORTED, "the backward takes one Q scale per block (q_group = 0)");
+  return SAGE_OK;
 }
 
 // Workspace of sage_attn_fwd_noalloc: one array per GPU, held for the life of the process.
@@ -399,6 +444,94 @@ int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, 
   if ((rc = scratch_ptr(&ws))) return rc;
   return attn_common(q, k, v, o, B, H, N, d, causal, sm_scale, variant, pp, ws, (size_t)SAGE_NOALLOC_SCRATCH_BYTES,
                      stream);
+}
+
+int sage_attn_fwd_train(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                        int d, int causal, float sm_scale, const sage_params* pp, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc;
+  Params p;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if ((rc = read_bwd_params(pp, &p))) return rc;
+  if ((rc = check_ptr(lse, 16, "lse"))) return rc;
+  return attn_common(q, k, v, o, B, H, N, d, causal, sm_scale, SAGE_VARIANT_INT8QK_FP16PV, pp, ws, ws_bytes, stream,
+                     lse);
+}
+
+size_t sage_attn_bwd_workspace_bytes(int B, int H, int N, int d, const sage_params* pp) {
+  if (check_shape(B, H, N, d)) return 0;
+  Params p;
+  if (read_bwd_params(pp, &p)) return 0;
+  return bwd_layout(B, H, N, d, p).total;
+}
+
+int sage_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  float* dq, float* dk, float* dv, int B, int H, int N, int d, int causal, float sm_scale,
+                  const sage_params* pp, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_bwd_params(pp, &p))) return rc;
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k, 16, "k")) || (rc = check_ptr(v, 16, "v")) ||
+      (rc = check_ptr(o, 16, "o")) || (rc = check_ptr(dout, 16, "dout")) || (rc = check_ptr(lse, 16, "lse")) ||
+      (rc = check_ptr(dq, 16, "dq")) || (rc = check_ptr(dk, 16, "dk")) || (rc = check_ptr(dv, 16, "dv")))
+    return rc;
+  const BwdLayout L = bwd_layout(B, H, N, d, p);
+  if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int G = B * H;
+  // exact token sums of K and V (the V sums give V's mean for the smoothed dP)
+  const sage::StatsOut stats{at<long long>(ws, L.ksum), at<long long>(ws, L.vsum), at<float>(ws, L.vmax),
+                             at<float>(ws, L.vmin)};
+  hipError_t e = sage::launch_stats(d, k, v, true, G, N, stats, st);
+  if (e != hipSuccess) return hip_fail(e, "statistics kernel");
+  // the forward's codes: variant 0, K smoothed, per-block Q and K scales
+  sage::QuantArgs qa = quant_args(q, k, B, H, N, d, p, at<int8_t>(ws, L.q_i8), at<int8_t>(ws, L.k_i8),
+                                  at<float>(ws, L.q_scale), at<float>(ws, L.k_scale), at<float>(ws, L.k_mean), nullptr,
+                                  at<long long>(ws, L.ksum));
+  e = sage::launch_quant(d, qa, st);
+  if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
+  sage::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.q_i8 = at<int8_t>(ws, L.q_i8);
+  a.k_i8 = at<int8_t>(ws, L.k_i8);
+  a.q_scale = at<float>(ws, L.q_scale);
+  a.k_scale = at<float>(ws, L.k_scale);
+  a.ksum = at<long long>(ws, L.ksum);
+  a.vsum = at<long long>(ws, L.vsum);
+  a.v_i8 = at<int8_t>(ws, L.v_i8);
+  a.do_i8 = at<int8_t>(ws, L.do_i8);
+  a.v_scale = at<float>(ws, L.v_scale);
+  a.do_scale = at<float>(ws, L.do_scale);
+  a.dvec = at<float>(ws, L.dvec);
+  a.lse2 = at<float>(ws, L.lse2);
+  a.nrm = at<float>(ws, L.nrm);
+  a.kp = at<uint16_t>(ws, L.kp);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.G = G;
+  a.N = N;
+  a.Np = pad_len(N);
+  a.blk_q = p.blk_q;
+  a.blk_k = p.blk_k;
+  a.nqb = ceil_div(N, p.blk_q);
+  a.nkb = ceil_div(N, p.blk_k);
+  a.nsplit = ceil_div(N, sage::kStatRows);
+  a.smooth_k = p.smooth_k;
+  a.kscale = sm_scale * 1.4426950408889634f;
+  a.sm_scale = sm_scale;
+  e = sage::launch_bwd(d, causal, a, st);
+  if (e != hipSuccess) return hip_fail(e, "backward kernels");
+  return ok();
 }
 
 int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* q_scale, const float* k_scale,

@@ -1,0 +1,458 @@
+// sage_bwd.hip -- 8-bit attention backward for gfx950 (CDNA4): dQ, dK, dV.
+//
+// Method: "SageAttention3: Microscaling FP4 Attention for Inference and An Exploration of
+// 8-Bit Training" (abstract on the author page, "NeurIPS Conference 2025"): an 8-bit
+// attention for the backward pass as well as the forward.  The backward follows
+// FlashAttention-2 (an entry of the SageAttention summary page's reference list): it
+// recomputes P = exp(s - L) from the forward's scores and the row log-sum-exp L, forms
+// D_i = sum_c dO_ic O_ic, dP = dO V^T, dS = P (dP - D), and accumulates dV = P^T dO,
+// dK = dS^T Q, dQ = dS K.
+//
+// 8-bit products: the recomputed scores use the forward's INT8 codes (K smoothed, per-block
+// Q and K scales, exact int32); dP = dO V^T runs on per-token INT8 dO and V' (V minus its
+// token mean, which shifts dP_ij and D_i by the same dO_i . vmean, so dS does not move),
+// also with exact int32 sums.  The products with P and dS keep fp16 operands and fp32
+// accumulation, as SageAttention keeps P~ V in FP16: P enters as fp16(2^8 P) and dS as
+// fp16(sigma dS), sigma = 2^(14 - e) with 2^e the first power of two above
+// 2 max|dO_i| max|V'_j| (a bound of |dS|), and dQ uses the smoothed K' in fp16.
+//
+// Kernels (all on [G = B*H heads][N][D] tensors):
+//  - bwd_prep_kernel: per token, INT8 V' and dO with their scales, D', the log-sum-exp in
+//    base 2, K' in fp16, and per 64-row block the largest |dO_i| and |V'_j| (for sigma);
+//  - bwd_dkdv_kernel: a workgroup owns 128 keys (32 per wave) and walks 64-row query
+//    tiles.  S = Qhat Khat^T and dP = dOhat V'hat^T come out of v_mfma_i32_32x32x32_i8
+//    with the query tile as the A operand (rows in the k_perm order of the forward's K
+//    tile), so each lane holds one key and 16 consecutive rows of each 32-row block; P
+//    and dS are then packed as fp16 pairs in exactly the layout of the forward's P~, and
+//    dV^T = dO^T P and dK^T = Q^T dS run as the forward's P~ V product with the dO and Q
+//    fp16 tiles in place of V;
+//  - bwd_dq_kernel: the forward's layout (a workgroup owns 128 query rows): S^T and dP^T
+//    per 64-key tile, dS packed as the forward's P~, and dQ^T = K'^T dS^T as its P~ V
+//    product with the K' fp16 tile in place of V.
+// No atomics: dK and dV are written by the key blocks' owners, dQ by the query blocks'
+// owners, so the results are deterministic.
+#include "sage_device.h"
+#include "sage_internal.h"
+#include "sage_tiles.h"
+
+namespace sage {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or query rows (dQ) per workgroup
+constexpr float kPScale = 256.0f;         // P enters the fp16 products as 2^8 P
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// sigma = 2^(14 - e), 2^e the first power of two above 2 max|dO_i| max|V'_j| (1 when the bound is 0),
+// from the per-block maxima the preparation pass wrote ([nblk][2]).  Every thread of the
+// workgroup gets the same value.
+__device__ __forceinline__ float bwd_sigma(const float* nrm, int nblk, float* sRed) {
+  const int tid = threadIdx.x;
+  float gm = 0.0f, vm = 0.0f;
+  for (int b = tid; b < nblk; b += blockDim.x) {
+    gm = fmaxf(gm, nrm[2 * b]);
+    vm = fmaxf(vm, nrm[2 * b + 1]);
+  }
+  gm = wave_max(gm);
+  vm = wave_max(vm);
+  if ((tid & 63) == 0) {
+    sRed[2 * (tid >> 6)] = gm;
+    sRed[2 * (tid >> 6) + 1] = vm;
+  }
+  __syncthreads();
+  gm = 0.0f;
+  vm = 0.0f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    gm = fmaxf(gm, sRed[2 * w]);
+    vm = fmaxf(vm, sRed[2 * w + 1]);
+  }
+  __syncthreads();
+  const float bound = 2.0f * gm * vm;
+  return bound > 0.0f ? __builtin_amdgcn_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(bound)) : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// preparation: one workgroup per (head, 64 tokens); wave w takes tokens 16w .. 16w+15,
+// lane l channels l and l + 64 (D = 128) or l (D = 64).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int CPL = D / 64;  // channels per lane
+  const int nblk = a.Np / 64;
+  const int g = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float sRed[8];
+  // exact token means of K and V (split 0 of the statistics pass holds the head's sums)
+  float kmean[CPL], vmean[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    kmean[j] = a.smooth_k ? fixed24_mean(a.ksum[(size_t)g * a.nsplit * D + c], a.N) : 0.0f;
+    vmean[j] = fixed24_mean(a.vsum[(size_t)g * a.nsplit * D + c], a.N);
+  }
+  float gmax = 0.0f, vmax = 0.0f;
+  for (int r = 0; r < 16; ++r) {
+    const int t = blk * 64 + 16 * wave + r;
+    const size_t row = (size_t)g * a.Np + t;
+    if (t >= a.N) {  // pad rows: zero codes and scales, no weight in dK / dV (log-sum-exp +inf)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        a.v_i8[row * D + c] = 0;
+        a.do_i8[row * D + c] = 0;
+        a.kp[row * D + c] = 0;
+      }
+      if (lane == 0) {
+        a.v_scale[row] = 0.0f;
+        a.do_scale[row] = 0.0f;
+        a.dvec[row] = 0.0f;
+        a.lse2[row] = INFINITY;
+      }
+      continue;
+    }
+    const size_t src = ((size_t)g * a.N + t) * D;
+    float vv[CPL], gg[CPL];
+    float va = 0.0f, ga = 0.0f, vn = 0.0f, gn = 0.0f;
+    double dsum = 0.0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      const float vx = (float)__builtin_bit_cast(_Float16, a.v[src + c]) - vmean[j];
+      const float gx = (float)__builtin_bit_cast(_Float16, a.dout[src + c]);
+      const float ox = (float)__builtin_bit_cast(_Float16, a.o[src + c]);
+      const float kx = (float)__builtin_bit_cast(_Float16, a.k[src + c]) - kmean[j];
+      a.kp[row * D + c] = __builtin_bit_cast(uint16_t, (_Float16)kx);
+      vv[j] = vx;
+      gg[j] = gx;
+      va = fmaxf(va, fabsf(vx));
+      ga = fmaxf(ga, fabsf(gx));
+      vn = fmaf(vx, vx, vn);
+      gn = fmaf(gx, gx, gn);
+      // exact products of fp16 values; the fp64 sum of the row is exact for ordinary data
+      dsum += (double)gx * (double)ox - (double)gx * (double)vmean[j];
+    }
+    va = wave_max(va);
+    ga = wave_max(ga);
+    vn = wave_sum(vn);
+    gn = wave_sum(gn);
+    dsum = wave_sum_f64(dsum);
+    const float vr = i8_factor(va), gr = i8_factor(ga);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      a.v_i8[row * D + c] = (int8_t)i8_code_int(vv[j], vr);
+      a.do_i8[row * D + c] = (int8_t)i8_code_int(gg[j], gr);
+    }
+    if (lane == 0) {
+      a.v_scale[row] = i8_scale(va);
+      a.do_scale[row] = i8_scale(ga);
+      a.dvec[row] = (float)dsum;
+      a.lse2[row] = a.lse[(size_t)g * a.N + t] * 1.4426950408889634f;
+    }
+    gmax = fmaxf(gmax, __builtin_sqrtf(gn));
+    vmax = fmaxf(vmax, __builtin_sqrtf(vn));
+  }
+  if (lane == 0) {
+    sRed[2 * wave] = gmax;
+    sRed[2 * wave + 1] = vmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float gm = 0.0f, vm = 0.0f;
+    for (int w = 0; w < 4; ++w) {
+      gm = fmaxf(gm, sRed[2 * w]);
+      vm = fmaxf(vm, sRed[2 * w + 1]);
+    }
+    a.nrm[((size_t)g * nblk + blk) * 2] = gm;
+    a.nrm[((size_t)g * nblk + blk) * 2 + 1] = vm;
+  }
+}
+
+// The INT8 product of one 32-row block st of an A tile in the k_tile layout with a B
+// operand held in registers (b[ks]: the lane's 16 bytes of k-step ks): acc[i] = row
+// 32*st + 16*h + i of the tile . column l%32.
+template <int D>
+__device__ __forceinline__ i32x16 i8_block_regb(const int8_t* sA, int st, const i32x4* b, int lane) {
+  constexpr int CPR = D / 16;
+  const int8_t* abase = sA + 16 * lane;
+  i32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    acc = mfma_i8(*reinterpret_cast<const i32x4*>(abase + (st * CPR + 2 * ks) * 512), b[ks], acc);
+  return acc;
+}
+
+// The fp16 product of one 32-row block st of a [64 rows][D] fp16 tile (v_tile layout,
+// vbase = tile + pv_lane_offset) with 8 packed weights of the lane's 16 rows of block st.
+template <int D>
+__device__ __forceinline__ void f16_block(const uint8_t* vbase, const uint32_t* pk, int st, f32x16* o) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t pq[4] = {pk[u * 4], pk[u * 4 + 1], pk[u * 4 + 2], pk[u * 4 + 3]};
+    const f16x8 pb = __builtin_bit_cast(f16x8, pq);
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct) {
+      const i16x4 a0 = lds_read_tr16(vbase + 128 * ((8 * st + 2 * u) * (D / 16) + 2 * ct));
+      const i16x4 a1 = lds_read_tr16(vbase + 128 * ((8 * st + 2 * u + 1) * (D / 16) + 2 * ct));
+      const i16x4 a01[2] = {a0, a1};
+      o[ct] = mfma_f16(__builtin_bit_cast(f16x8, a01), pb, o[ct]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: workgroup = 128 keys of one head (wave w: keys 32w .. 32w+31), 64-row query tiles.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NCT = D / 32;
+  __shared__ __attribute__((aligned(16))) int8_t sQ[kTileKV * D];      // Qhat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sG[kTileKV * D];      // dOhat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) uint8_t sQf[kTileKV * D * 2];  // Q fp16 tile (v_tile layout)
+  __shared__ __attribute__((aligned(16))) uint8_t sGf[kTileKV * D * 2];  // dO fp16 tile (v_tile layout)
+  __shared__ __attribute__((aligned(16))) float sL[kTileKV];  // log2-sum-exp of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sD[kTileKV];  // D' of the rows
+  __shared__ __attribute__((aligned(16))) float sGs[kTileKV];  // INT8 scales of the dO rows
+  __shared__ float sRed[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int nkb = a.Np / kBwdRows;
+  const int g = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int k0 = kb * kBwdRows, kw = k0 + 32 * wave, key = kw + (lane & 31);
+  const int N = a.N, Np = a.Np;
+
+  const float sigma = bwd_sigma(a.nrm + (size_t)g * (Np / 64) * 2, Np / 64, sRed);
+
+  // B operands of this wave: Khat and V'hat rows of its 32 keys (pad rows are zero)
+  i32x4 kb_op[D / 32], vb_op[D / 32];
+  {
+    const int8_t* kr = a.k_i8 + ((size_t)g * Np + key) * D + 16 * h;
+    const int8_t* vr = a.v_i8 + ((size_t)g * Np + key) * D + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      kb_op[ks] = *reinterpret_cast<const i32x4*>(kr + 32 * ks);
+      vb_op[ks] = *reinterpret_cast<const i32x4*>(vr + 32 * ks);
+    }
+  }
+  // the key's K scale times sm_scale * log2(e), and its V' scale
+  const float ck = a.kscale * a.k_scale[(size_t)g * a.nkb + min(key, N - 1) / a.blk_k];
+  const float dvk = a.v_scale[(size_t)g * Np + key];
+
+  f32x16 dv[NCT], dk[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dv[ct] = dk[ct] = f32x16{};
+
+  const TileCopy<D, 0, kBwdWaves> copy(Np);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q_i8 + (size_t)g * Np * D, (size_t)Np * D);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.do_i8 + (size_t)g * Np * D, (size_t)Np * D);
+  const __amdgpu_buffer_rsrc_t qfrs = make_rsrc(a.q + (size_t)g * N * D, (size_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t gfrs = make_rsrc(a.dout + (size_t)g * N * D, (size_t)N * D * 2);
+  const int vb = pv_lane_offset<D>(lane);
+
+  // causal: rows below the workgroup's first key see none of its keys
+  const int t0 = CAUSAL ? k0 / kTileKV : 0;
+  const int T = (N + kTileKV - 1) / kTileKV;
+  for (int t = t0; t < T; ++t) {
+    copy.k_tile(qrs, t, sQ);
+    copy.k_tile(grs, t, sG);
+    copy.v_tile(qfrs, t, Np, sQf);
+    copy.v_tile(gfrs, t, Np, sGf);
+    if (tid < kTileKV) {
+      const size_t r = (size_t)g * Np + t * kTileKV + tid;
+      sL[tid] = a.lse2[r];
+      sD[tid] = a.dvec[r];
+      sGs[tid] = a.do_scale[r];
+    }
+    wait_copies();
+    __syncthreads();
+    const int r0 = t * kTileKV;
+    // this wave's keys are all beyond the tile's last row: nothing to add
+    const bool active = !CAUSAL || r0 + kTileKV - 1 >= kw;
+    if (active) {
+      const float c = a.q_scale[(size_t)g * a.nqb + min(r0, N - 1) / a.blk_q] * ck;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const i32x16 s = i8_block_regb<D>(sQ, st, kb_op, lane);
+        const i32x16 dp = i8_block_regb<D>(sG, st, vb_op, lane);
+        // rows 32*st + 16*h + i of the tile
+        const float4* pl = reinterpret_cast<const float4*>(sL + 32 * st + 16 * h);
+        const float4* pd = reinterpret_cast<const float4*>(sD + 32 * st + 16 * h);
+        const float4* pg = reinterpret_cast<const float4*>(sGs + 32 * st + 16 * h);
+        uint32_t pkp[8], pks[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 L4 = pl[q4], D4 = pd[q4], G4 = pg[q4];
+          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+          const float Gr[4] = {G4.x, G4.y, G4.z, G4.w};
+          float p[4], ds[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int i = 4 * q4 + b;
+            const int row = r0 + 32 * st + 16 * h + i;
+            float pv = __builtin_amdgcn_exp2f(fmaf((float)s[i], c, -Lr[b]));
+            if (CAUSAL) pv = row >= key ? pv : 0.0f;
+            const float dpv = (float)dp[i] * (Gr[b] * dvk);
+            p[b] = pv;
+            ds[b] = pv * (dpv - Dr[b]);
+          }
+          pkp[2 * q4] = pack_f16x2(kPScale * p[0], kPScale * p[1]);
+          pkp[2 * q4 + 1] = pack_f16x2(kPScale * p[2], kPScale * p[3]);
+          pks[2 * q4] = pack_f16x2(sigma * ds[0], sigma * ds[1]);
+          pks[2 * q4 + 1] = pack_f16x2(sigma * ds[2], sigma * ds[3]);
+        }
+        f16_block<D>(sGf + vb, pkp, st, dv);
+        f16_block<D>(sQf + vb, pks, st, dk);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (key >= N) return;
+  const float sv = 1.0f / kPScale, sk = a.sm_scale / sigma;
+  float* dvr = a.dv + ((size_t)g * N + key) * D;
+  float* dkr = a.dk + ((size_t)g * N + key) * D;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int c0 = ct * 32 + 8 * a4 + 4 * h;
+      *reinterpret_cast<float4*>(dvr + c0) = make_float4(dv[ct][4 * a4] * sv, dv[ct][4 * a4 + 1] * sv,
+                                                         dv[ct][4 * a4 + 2] * sv, dv[ct][4 * a4 + 3] * sv);
+      *reinterpret_cast<float4*>(dkr + c0) = make_float4(dk[ct][4 * a4] * sk, dk[ct][4 * a4 + 1] * sk,
+                                                         dk[ct][4 * a4 + 2] * sk, dk[ct][4 * a4 + 3] * sk);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: workgroup = 128 query rows of one head (wave w: rows 32w .. 32w+31), 64-key tiles.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NCT = D / 32;
+  __shared__ __attribute__((aligned(16))) int8_t sK[kTileKV * D];       // Khat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sV[kTileKV * D];       // V'hat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) uint8_t sKf[kTileKV * D * 2];  // K' fp16 tile (v_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sQo[kBwdRows * D];     // per wave: Qhat rows (B operand)
+  __shared__ __attribute__((aligned(16))) int8_t sGo[kBwdRows * D];     // per wave: dOhat rows (B operand)
+  __shared__ __attribute__((aligned(16))) float sVs[kTileKV];  // INT8 scales of the tile's V' rows
+  __shared__ float sRed[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
+  const int nqt = a.Np / kBwdRows;
+  const int g = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  const int q0 = qt * kBwdRows, qw = q0 + 32 * wave, qi = qw + ql;
+  const int N = a.N, Np = a.Np;
+
+  const float sigma = bwd_sigma(a.nrm + (size_t)g * (Np / 64) * 2, Np / 64, sRed);
+
+  int8_t* const sQw = sQo + wave * D * 32;
+  int8_t* const sGw = sGo + wave * D * 32;
+  // qw < Np: every wave's 32 rows lie in the padded tensors
+  load_q_tile<D>(make_rsrc(a.q_i8 + (size_t)g * Np * D, (size_t)Np * D), qw, sQw);
+  load_q_tile<D>(make_rsrc(a.do_i8 + (size_t)g * Np * D, (size_t)Np * D), qw, sGw);
+  const size_t rq = (size_t)g * Np + qi;
+  const float l2 = a.lse2[rq], drow = a.dvec[rq], gsc = a.do_scale[rq];
+  const float cq = a.kscale * a.q_scale[(size_t)g * a.nqb + min(qi, N - 1) / a.blk_q];
+
+  f32x16 dq[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dq[ct] = f32x16{};
+
+  const TileCopy<D, 0, kBwdWaves> copy(Np);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k_i8 + (size_t)g * Np * D, (size_t)Np * D);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v_i8 + (size_t)g * Np * D, (size_t)Np * D);
+  // K' is padded to Np rows of zeros: the copy of the last tile stays inside
+  const __amdgpu_buffer_rsrc_t kfrs = make_rsrc(a.kp + (size_t)g * Np * D, (size_t)Np * D * 2);
+  const int vb = pv_lane_offset<D>(lane);
+  const int ntiles = (N + kTileKV - 1) / kTileKV;
+  const int T = CAUSAL ? min(ntiles, (min(q0 + kBwdRows, N) - 1) / kTileKV + 1) : ntiles;
+  const int wave_last = CAUSAL ? min(ntiles - 1, min(qw + 31, N - 1) / kTileKV) : ntiles - 1;
+  const unsigned last_key = (unsigned)(N - 1);
+  const int kshift = __builtin_ctz(a.blk_k);
+
+  for (int t = 0; t < T; ++t) {
+    copy.k_tile(krs, t, sK);
+    copy.k_tile(vrs, t, sV);
+    copy.v_tile(kfrs, t, Np, sKf);
+    if (tid < kTileKV) sVs[tid] = a.v_scale[(size_t)g * Np + t * kTileKV + tid];
+    float kq[4];
+    tile_kscales(a.k_scale + (size_t)g * a.nkb, t, last_key, kshift, kq);
+    wait_copies();
+    __syncthreads();
+    if (qw < N && t <= wave_last) {
+      i32x16 s[2], dp[2];
+      qk_tile<D>(sK, sQw, lane, s);
+      qk_tile<D>(sV, sGw, lane, dp);
+      uint32_t pk[16];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const float c = cq * kscale_of(kq, st, h);
+        const float4* pv4 = reinterpret_cast<const float4*>(sVs + 32 * st + 16 * h);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 V4 = pv4[q4];
+          const float Vr[4] = {V4.x, V4.y, V4.z, V4.w};
+          float ds[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int i = 4 * q4 + b;
+            const int kj = t * kTileKV + 32 * st + 16 * h + i;
+            float pv = __builtin_amdgcn_exp2f(fmaf((float)s[st][i], c, -l2));
+            // keys past N, and past the row when causal, carry no weight
+            pv = (kj < N && (!CAUSAL || kj <= qi)) ? pv : 0.0f;
+            const float dpv = (float)dp[st][i] * (gsc * Vr[b]);
+            ds[b] = pv * (dpv - drow);
+          }
+          pk[st * 8 + 2 * q4] = pack_f16x2(sigma * ds[0], sigma * ds[1]);
+          pk[st * 8 + 2 * q4 + 1] = pack_f16x2(sigma * ds[2], sigma * ds[3]);
+        }
+      }
+      pv_tile_f16<D>(sKf + vb, pk, dq);
+    }
+    __syncthreads();
+  }
+
+  if (qi >= N) return;
+  const float sq = a.sm_scale / sigma;
+  float* dqr = a.dq + ((size_t)g * N + qi) * D;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int c0 = ct * 32 + 8 * a4 + 4 * h;
+      *reinterpret_cast<float4*>(dqr + c0) = make_float4(dq[ct][4 * a4] * sq, dq[ct][4 * a4 + 1] * sq,
+                                                         dq[ct][4 * a4 + 2] * sq, dq[ct][4 * a4 + 3] * sq);
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+template <int D>
+static hipError_t launch_bwd_d(int causal, const BwdArgs& a, hipStream_t st) {
+  const int G = a.G;
+  bwd_prep_kernel<D><<<G * (a.Np / 64), 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = G * (a.Np / kBwdRows);
+  if (causal) {
+    bwd_dkdv_kernel<D, true><<<grid, kBwdThreads, 0, st>>>(a);
+    bwd_dq_kernel<D, true><<<grid, kBwdThreads, 0, st>>>(a);
+  } else {
+    bwd_dkdv_kernel<D, false><<<grid, kBwdThreads, 0, st>>>(a);
+    bwd_dq_kernel<D, false><<<grid, kBwdThreads, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(int d, int causal, const BwdArgs& a, hipStream_t st) {
+  return d == 64 ? launch_bwd_d<64>(causal, a, st) : launch_bwd_d<128>(causal, a, st);
+}
+
+}  // namespace sage

@@ -35,6 +35,7 @@ struct AttnArgs {
   const uint8_t* q_e8;    // [G][Np][D/32] MX block scales (variant 2; q_i8 / k_i8 then
   const uint8_t* k_e8;    //  hold [G][Np][D/2] bytes of two E2M1 codes each)
   uint16_t* o;            // [G][N][D] fp16
+  float* lse;             // [G][N] row log-sum-exp of the dequantised scores (natural log), or null
   int G, N, Np, blk_q, blk_k, nqb, nkb;
   int q_group, nqg;       // rows per Q scale (a power of two dividing blk_q), scales per head
   float kscale;           // sm_scale * log2(e)
@@ -62,6 +63,26 @@ hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const Stat
 hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const long long* ksum_part, int smooth,
                            uint8_t* codes, uint8_t* e8, float* k_mean, hipStream_t st);
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st);
+// Backward (sage_bwd.hip).  Inputs [G][N][D] fp16 unless noted; the workspace pieces are
+// filled by the statistics pass (ksum, vsum), the quantisation pass (q_i8, k_i8 and their
+// scales, variant-0 rules) and the preparation kernel (the rest).
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *o, *dout;
+  const float* lse;            // [G][N] natural-log row log-sum-exp of the forward
+  const int8_t *q_i8, *k_i8;   // [G][Np][D] forward codes
+  const float *q_scale, *k_scale;
+  const long long *ksum, *vsum;  // [G][nsplit][D], split 0 = the head's exact sums
+  int8_t *v_i8, *do_i8;        // [G][Np][D] per-token INT8 of V' and dO
+  float *v_scale, *do_scale;   // [G][Np]
+  float *dvec, *lse2;          // [G][Np]: D' per row; log2-sum-exp (+inf on pad rows)
+  float* nrm;                  // [G][Np/64][2]: max |dO_i|, max |V'_j| per 64 rows
+  uint16_t* kp;                // [G][Np][D] K' = K - kmean in fp16, pad rows zero
+  float *dq, *dk, *dv;         // [G][N][D] fp32 outputs
+  int G, N, Np, blk_q, blk_k, nqb, nkb, nsplit, smooth_k;
+  float kscale, sm_scale;      // sm_scale * log2(e), sm_scale
+};
+hipError_t launch_bwd(int d, int causal, const BwdArgs& a, hipStream_t st);
+
 hipError_t launch_debug_qk(int d, const int8_t* q_i8, const int8_t* k_i8, int G, int Np, const int* tiles,
                            int n_tiles, int32_t* s_out, hipStream_t st);
 
