@@ -94,6 +94,8 @@ def main():
                     help="rows per Q scale (0: one per Q block; 1: per token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads of the workload the oracle runs")
+    ap.add_argument("--bwd", action="store_true",
+                    help="measure the 8-bit backward (dQ, dK, dV) of the workload instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -108,6 +110,9 @@ def main():
 
     import quantized_bit_attention_amd as sage
     import workloads
+
+    if args.bwd:
+        return bench_bwd(args)
 
     cfg = workloads.config(args.config)
     x = workloads.make_inputs(args.config)
@@ -228,6 +233,64 @@ def main():
                                   "cores": orc.threads_used, "kind": "oracle",
                                   "sample": f"{nh} of {B * H} heads, all {N} rows, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
+
+
+def bench_bwd(args):
+    """The 8-bit backward of the workload: one step = stats + quantisation + preparation +
+    dK/dV + dQ kernels on inputs resident in HBM.  Operations counted: the five products
+    of the backward, 2*N^2*d each per head (10*B*H*N^2*d, halved for causal); the dQ kernel's
+    recomputation of S and dP is not counted.  Ceiling: two INT8 products (5.0 POP/s) and
+    three FP16 products (2.5 PFLOP/s) -> 3125 TOPS."""
+    import numpy as np
+    import torch
+
+    import quantized_bit_attention_amd as sage
+    import workloads
+
+    cfg = workloads.config(args.config)
+    x = workloads.make_inputs(args.config)
+    B, H, N, d = x["q"].shape
+    causal = bool(cfg["causal"])
+    blk_q = max(cfg["blk_q"], 64)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v"))
+    rng = np.random.default_rng(12)
+    dout = torch.from_numpy(rng.standard_normal(x["q"].shape).astype(np.float16)).to(dev)
+    o, lse = sage.attn_fwd_train(q, k, v, causal=causal, blk_q=blk_q, blk_k=cfg["blk_k"])
+    ws = torch.empty(sage._load().sage_attn_bwd_workspace_bytes(
+        B, H, N, d, ctypes_params(sage, blk_q, cfg["blk_k"])), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(causal=causal, blk_q=blk_q, blk_k=cfg["blk_k"], workspace=ws)
+    for _ in range(args.warmup):
+        sage.attn_bwd(q, k, v, o, dout, lse, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        sage.attn_bwd(q, k, v, o, dout, lse, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ops = 2.5 * workloads.attention_ops(B, H, N, d, causal)  # 5 products of 2*N^2*d
+    tops = ops / (ms * 1e-3) / 1e12
+    ceiling = 1.0 / (0.4 / INT8_PEAK_TOPS + 0.6 / FP16_PEAK_TOPS)
+    result = {
+        "metric": "8-bit attention backward TOPS (10*B*H*N^2*d per step, halved for causal)",
+        "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+fp16", "data": "synthetic (seeded SplitMix64/Box-Muller; dO from numpy PCG64 seed 12)",
+        "config": {"workload": f"{cfg['name']} backward B={B} H={H} N={N} d={d}", "B": B, "H": H, "N": N, "d": d,
+                   "causal": int(causal), "blk_q": blk_q, "blk_k": cfg["blk_k"]},
+        "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": round(ceiling, 1), "unit": "TOPS",
+                     "frac": round(tops / ceiling, 4), "traffic": None,
+                     "scope": "whole backward call (per-kernel split in the rocprofv3 summary)"},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def ctypes_params(sage, blk_q, blk_k):
+    import ctypes
+    return ctypes.byref(sage._params(blk_q, blk_k, True, False, False, 0))
 
 
 if __name__ == "__main__":

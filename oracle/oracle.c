@@ -853,7 +853,16 @@ static void bwd_head(const bwdparams_t* P, const uint16_t* q, const uint16_t* k,
   double* s = (double*)malloc(sizeof(double) * (size_t)N);
   double* pr = (double*)malloc(sizeof(double) * (size_t)N);
   double* ds = (double*)malloc(sizeof(double) * (size_t)N);
-  for (size_t e = 0; e < (size_t)N * d; ++e) dq[e] = dk[e] = dv[e] = 0.0;
+  /* the fp16 inputs as doubles (exact) */
+  double* qf = (double*)malloc(sizeof(double) * (size_t)N * d);
+  double* kf = (double*)malloc(sizeof(double) * (size_t)N * d);
+  double* gf = (double*)malloc(sizeof(double) * (size_t)N * d);
+  for (size_t e = 0; e < (size_t)N * d; ++e) {
+    qf[e] = oracle_f16_decode(q[e]);
+    kf[e] = oracle_f16_decode(k[e]);
+    gf[e] = oracle_f16_decode(dout[e]);
+    dq[e] = dk[e] = dv[e] = 0.0;
+  }
 
   if (!P->exact) {
     /* forward's Q and K codes (variant 0: K smoothed over all tokens, Q not smoothed) */
@@ -970,15 +979,15 @@ static void bwd_head(const bwdparams_t* P, const uint16_t* q, const uint16_t* k,
     /* dQ_i = sm_scale sum_j dS_ij K'_j;  dK_j += sm_scale dS_ij Q_i;  dV_j += P_ij dO_i */
     for (int j = 0; j < jend; ++j)
       for (int c = 0; c < d; ++c) {
-        const double kv = P->exact ? oracle_f16_decode(k[(size_t)j * d + c]) : ksm[(size_t)j * d + c];
-        const double qv = oracle_f16_decode(q[(size_t)i * d + c]);
-        const double gv = oracle_f16_decode(dout[(size_t)i * d + c]);
+        const double kv = P->exact ? kf[(size_t)j * d + c] : ksm[(size_t)j * d + c];
+        const double qv = qf[(size_t)i * d + c];
+        const double gv = gf[(size_t)i * d + c];
         dq[(size_t)i * d + c] += P->sm_scale * ds[j] * kv;
         dk[(size_t)j * d + c] += P->sm_scale * ds[j] * qv;
         dv[(size_t)j * d + c] += pr[j] * gv;
       }
   }
-  free(s); free(pr); free(ds);
+  free(s); free(pr); free(ds); free(qf); free(kf); free(gf);
   free(qi); free(ki); free(vi); free(gi); free(qs); free(ks); free(vs); free(gs); free(vmean); free(vsm);
   free(kmean); free(ksm);
 }

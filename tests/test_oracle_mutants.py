@@ -70,7 +70,7 @@ MUTANTS = {
                              "ds[j] = oracle_f16_decode(oracle_f16_encode(sigma * dsv));"),
     "bwd sigma from V only": ("const double bound = 2.0 * gmax * vmax;", "const double bound = 2.0 * vmax;"),
     "bwd dV uses the row of dO of the key": ("dv[(size_t)j * d + c] += pr[j] * gv;",
-                                             "dv[(size_t)j * d + c] += pr[j] * oracle_f16_decode(dout[(size_t)j * d + c]);"),
+                                             "dv[(size_t)j * d + c] += pr[j] * gf[(size_t)j * d + c];"),
     "bwd causal mask dropped": ("const int jend = P->causal ? i + 1 : N;", "const int jend = N;"),
     "bwd dQ uses unsmoothed K": ("const float x = (float)oracle_f16_decode(k[(size_t)t * d + c]) - kmean[c];",
                                  "const float x = (float)oracle_f16_decode(k[(size_t)t * d + c]);"),
