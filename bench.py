@@ -33,8 +33,9 @@ FP16_PEAK_TOPS = 2500.0
 FP8_PEAK_TOPS = 5000.0
 FP4_PEAK_TOPS = 10100.0
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["quantized_bit_attention_amd/csrc/sage_attn.hip", "quantized_bit_attention_amd/csrc/sage_device.h"]
-VARIANT_TAG = {0: "", 1: "_fp8pv", 2: "_fp8pv_mxfp4"}
+KERNEL_SOURCES = ["quantized_bit_attention_amd/csrc/sage_attn.hip", "quantized_bit_attention_amd/csrc/sage_device.h",
+                  "quantized_bit_attention_amd/csrc/sage_tiles.h"]
+VARIANT_TAG = {0: "_int8qk_fp16pv", 1: "_int8qk_fp8pv", 2: "_mxfp4qk_fp8pv"}
 
 
 def mfma_ceiling_tops(variant: int) -> float:
@@ -46,9 +47,15 @@ def mfma_ceiling_tops(variant: int) -> float:
     return 1.0 / (0.5 / qk + 0.5 / pv)
 
 
-def traffic_file(cfg_name: str, variant: int) -> str:
-    return os.path.join(ROOT, "profiles", f"attn_kernel_hbm_traffic_{cfg_name.replace('-', '_')}"
-                                          f"{VARIANT_TAG[variant]}.txt")
+def profile_name(cfg: dict, variant: int) -> str:
+    """File-name stem of a workload's profile summaries; a variant other than the workload's
+    own is appended as a suffix."""
+    tag = "" if variant == cfg["variant"] else VARIANT_TAG[variant]
+    return cfg["name"].replace("-", "_") + tag
+
+
+def traffic_file(cfg: dict, variant: int) -> str:
+    return os.path.join(ROOT, "profiles", f"attn_kernel_hbm_traffic_{profile_name(cfg, variant)}.txt")
 
 
 def kernel_source_hash() -> str:
@@ -59,11 +66,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(cfg_name, variant):
+def read_traffic(cfg, variant):
     """HBM bytes per attention-kernel launch from the committed rocprofv3 counter summary of
     this workload and variant, or None when it is missing or was taken from another version
     of the kernel."""
-    path = traffic_file(cfg_name, variant)
+    path = traffic_file(cfg, variant)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -187,7 +194,7 @@ def main():
     value = ops / (ms * 1e-3) / 1e12
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     # counter summaries exist per workload and variant, for the default options
-    traffic = read_traffic(cfg["name"], variant) if q_group == 0 and not smooth_v else None
+    traffic = read_traffic(cfg, variant) if q_group == 0 and not smooth_v else None
     ceiling = mfma_ceiling_tops(variant)
     result = {
         "metric": METRIC,

@@ -238,6 +238,47 @@ int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, 
                        const sage_params* p, void* stream);
 
 /*
+ * Training forward of the 8-bit backward (SageAttention3 abstract: 8-bit attention for
+ * training; FlashAttention-2 "Backward pass": the backward recomputes P from the row
+ * log-sum-exp).  Exactly sage_attn_fwd_ex with variant SAGE_VARIANT_INT8QK_FP16PV
+ * (same kernels, same o), and additionally
+ *   lse[B,H,N] fp32 (16-byte aligned, device) = ln of the row sum of exp(sm_scale * S)
+ *   over the visible keys, S the dequantised INT8 scores of the smoothed K (the shift by
+ *   K's mean drops out of the softmax), i.e. ln(l) + the running maximum, per row.
+ * p must satisfy the backward's rules: blk_q 64 or 128, smooth_q 0, q_group 0 (one Q
+ * scale per block); otherwise SAGE_ERR_UNSUPPORTED.  ws: sage_workspace_bytes(..., 0, p).
+ */
+int sage_attn_fwd_train(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                        int d, int causal, float sm_scale, const sage_params* p, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Device workspace bytes sage_attn_bwd needs for this shape (0 for bad arguments or a p
+ * the backward does not support). */
+size_t sage_attn_bwd_workspace_bytes(int B, int H, int N, int d, const sage_params* p);
+
+/*
+ * 8-bit attention backward (SageAttention3 abstract: 8-bit attention for training; the
+ * gradient order of FlashAttention-2 "Backward pass"), differentiating the variant-0
+ * forward of the same q, k, v, causal, sm_scale and p:
+ *   q, k, v, o, dout: fp16 [B,H,N,d]; lse: sage_attn_fwd_train's output for o;
+ *   dq, dk, dv: fp32 [B,H,N,d] (device, 16-byte aligned), fully overwritten.
+ * The quantisers are straight-through: dQ, dK, dV are the gradients of attention with
+ * the forward's dequantised Q and K (K smoothed when p->smooth_k).  Inside:
+ *   P recomputed from the INT8 scores and lse; dV = P^T dO with P as fp16(2^8 P);
+ *   dP = dO V^T with dO and V - mean_t(V) in per-token INT8 (the mean's term drops out
+ *   of dS, as it shifts every row's dP and D by the same amount);
+ *   D = rowsum(dO * O) - dO . mean_t(V); dS = P * (dP - D);
+ *   dQ = sm_scale dS K' (K' = K - mean_t(K) in fp16), dK = sm_scale dS^T Qdeq, both
+ *   with dS as fp16 of a power-of-two multiple of dS chosen per call from bounds of
+ *   |dO| and |V| so that it cannot overflow.
+ * p: blk_q 64 or 128, smooth_q 0, q_group 0; otherwise SAGE_ERR_UNSUPPORTED.
+ * ws: at least sage_attn_bwd_workspace_bytes(...) bytes.  d 64 or 128.
+ */
+int sage_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  float* dq, float* dk, float* dv, int B, int H, int N, int d, int causal, float sm_scale,
+                  const sage_params* p, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Test surface: the int32 products S = Qhat Khat^T that the attention kernel forms,
  * for chosen 128 x 64 tiles.  tiles[3*i + 0..2] = (flat head b*H+h, query tile, key
  * tile) with query rows [128*qt, 128*qt+128) and keys [64*kt, 64*kt+64) of the padded
