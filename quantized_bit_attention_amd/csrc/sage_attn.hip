@@ -108,7 +108,7 @@ constexpr float kLazyLog2 = 8.0f;
 template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, typename SV>
 __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const float* bias, int kl, int N,
                                              int qi, float& m, float& l, uint32_t* pk, float& alpha,
-                                             bool& rescale) {
+                                             bool& rescale, float lazy = kLazyLog2) {
   // key kl + j is visible iff j <= jmax (keys < N, and <= qi when causal): one compare
   // against a constant per score
   const int jmax = (CAUSAL ? min(qi, N - 1) : N - 1) - kl;
@@ -152,7 +152,7 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
   // variant 1: P~ * 448 must stay <= 448 for FP8, so the max moves as soon as a row's
   // does (a wave whose rows all keep their max has alpha = 1 exactly and skips the
   // rescale)
-  rescale = __builtin_amdgcn_ballot_w64(mt > m + (VARIANT == 0 ? kLazyLog2 : 0.0f)) != 0;
+  rescale = __builtin_amdgcn_ballot_w64(mt > m + (VARIANT == 0 ? lazy : 0.0f)) != 0;
   // branch-free so the caller's fast path stays one basic block
   const float mnew = rescale ? fmaxf(m, mt) : m;
   alpha = rescale ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;  // exp2(-inf) = 0 on the first tile
@@ -171,7 +171,6 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
         pv[j] = __builtin_amdgcn_exp2f(e);
         if (MASK) pv[j] = keep(st, i + j) ? pv[j] : 0.0f;
       }
-      psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
       if constexpr (VARIANT == 0) {
         pk[st * 8 + i / 2] = pack_f16x2(pv[0], pv[1]);
         pk[st * 8 + i / 2 + 1] = pack_f16x2(pv[2], pv[3]);
@@ -179,13 +178,47 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
         // the packs past the end of the interleaved block, so all 32 fp32 P~ of the lane
         // stay live across it (about 30 VGPRs, the third wave per SIMD at d = 64)
         asm volatile("" ::"v"(pk[st * 8 + i / 2]), "v"(pk[st * 8 + i / 2 + 1]));
+        // l sums the fp16 P~ that enter the product, two per dot instruction
+        psum[st] = sum_f16x2(pk[st * 8 + i / 2 + 1], sum_f16x2(pk[st * 8 + i / 2], psum[st]));
       } else {
+        psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pk[st * 4 + i / 4] = cvt_pk_fp8(pv[2], pv[3], cvt_pk_fp8(pv[0], pv[1], 0u, false), true);
       }
     }
   l += psum[0] + psum[1];
 }
 
+
+// Variant 0, unmasked tile: P~ against the row's current reference m, without the
+// tile's maximum.  The reference only has to keep P~ within fp16 and the sums
+// finite, so a tile whose P~ stay small keeps it: when every lane's 32 P~ (fp16) sum
+// to at most 2^kFastLog2, l gains that sum and pk holds the tile, and the function
+// returns false.  Otherwise (a key far above m, or m = -inf on a row's first tile) it
+// returns true for the whole wave, leaves m and l untouched, and the caller recomputes
+// the tile with softmax_tile, which moves m to the running maximum.
+constexpr float kFastSum = 1024.0f;  // 2^10
+__device__ __forceinline__ bool softmax_tile_fast(const i32x16* s, const float* c, float m, float& l,
+                                                  uint32_t* pk) {
+  const float shift = -m;
+  float psum[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf((float)s[st][i + j], c[st], shift));
+      pk[st * 8 + i / 2] = pack_f16x2(p[0], p[1]);
+      pk[st * 8 + i / 2 + 1] = pack_f16x2(p[2], p[3]);
+      asm volatile("" ::"v"(pk[st * 8 + i / 2]), "v"(pk[st * 8 + i / 2 + 1]));  // as in softmax_tile
+      psum[st] = sum_f16x2(pk[st * 8 + i / 2 + 1], sum_f16x2(pk[st * 8 + i / 2], psum[st]));
+    }
+  const float t = psum[0] + psum[1];
+  // also true for inf and NaN sums
+  const bool slow = __builtin_amdgcn_ballot_w64(!(t <= kFastSum)) != 0;
+  l = slow ? l : l + t;
+  return slow;
+}
 
 // Q smoothing: the term sm_scale*log2(e) * dK_j * (qmean_sb . Khat_j) of every key j of a
 // tile, for each Q block sb of the workgroup (up to 4), runs on the matrix unit.  The
@@ -265,7 +298,7 @@ __device__ __forceinline__ void interleave_schedule() {
   // 200 cycles) overlaps the MFMAs and VALU work in between
   constexpr int LEAD = 2;
   constexpr int MFMA = (VARIANT == 2 ? 2 * (D / 64) : 2 * (D / 32)) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
-  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 7 : 13)
+  constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 5 : 12)
                            : VARIANT == 1 ? (D == 128 ? 8 : 14)
                                           : (D == 128 ? 20 : 16);
   // with Q smoothing the softmax first reads its 32 biases (8 reads of 16 bytes)
@@ -585,13 +618,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       if constexpr (VARIANT != 0) {
         pv_tile(sVp, pkp);
         score_tile(sKn, sn);
+        softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+        interleave_schedule<D, VARIANT, SMOOTHQ>();
+      } else if constexpr (D == 128 && !SMOOTHQ) {
+        score_tile(sKn, sn);
+        pv_tile(sVp, pkp);
+        const bool slow = softmax_tile_fast(s, c, m, l, pk);
+        interleave_schedule<D, VARIANT, SMOOTHQ>();
+        __builtin_amdgcn_s_setprio(0);
+        // the reference moves to the row maximum (rare after a row's first tiles)
+        if (slow) softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, 0.0f);
       } else {
         score_tile(sKn, sn);
         pv_tile(sVp, pkp);
+        softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+        interleave_schedule<D, VARIANT, SMOOTHQ>();
+        __builtin_amdgcn_s_setprio(0);
       }
-      softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
-      interleave_schedule<D, VARIANT, SMOOTHQ>();
-      if constexpr (VARIANT == 0) __builtin_amdgcn_s_setprio(0);
     } else {
       if (compute_next) score_tile(sKn, sn);
       if (pv_prev) pv_tile(sVp, pkp);
