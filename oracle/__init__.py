@@ -43,6 +43,10 @@ def load(path: str | None = None):
     lib.oracle_quant.restype = i
     lib.oracle_quant_mx.argtypes = [p, p, i, i, i, i, i, p, p, p, p, p]
     lib.oracle_quant_mx.restype = i
+    lib.oracle_quant_v_mx.argtypes = [p, i, i, i, i, i, p, p, p]
+    lib.oracle_quant_v_mx.restype = i
+    lib.oracle_p_block_fp4.argtypes = [p, i, p, p]
+    lib.oracle_p_block_fp4.restype = None
     lib.oracle_qk_int32.argtypes = [p, p, i, i, i, i, i, i, p]
     lib.oracle_qk_int32.restype = i
     lib.oracle_attn_bwd.argtypes = [p, p, p, p, p, i, i, i, i, i, d, i, i, i, i, i, p, p, p, i]
@@ -163,6 +167,28 @@ class Oracle:
         if rc:
             raise ValueError("oracle_quant_mx: bad arguments")
         return r
+
+    def quant_v_mx(self, v, smooth_v=0) -> dict:
+        """Variant 3's V: E2M1 codes one per byte [B, H, d, Np] (tokens along the last axis),
+        E8M0 scales [B, H, d, Np/32] (one per channel and block of 32 tokens), v_mean [B, H, d]."""
+        v = _f16(v)
+        B, H, N, d = v.shape
+        Np = self.pad_len(N)
+        r = dict(v_codes=np.empty((B, H, d, Np), np.uint8), v_e8=np.empty((B, H, d, Np // 32), np.uint8),
+                 v_mean=np.empty((B, H, d), np.float32))
+        rc = self.lib.oracle_quant_v_mx(v.ctypes.data, B, H, N, d, int(smooth_v), r["v_codes"].ctypes.data,
+                                        r["v_e8"].ctypes.data, r["v_mean"].ctypes.data)
+        if rc:
+            raise ValueError("oracle_quant_v_mx: bad arguments")
+        return r
+
+    def p_block_fp4(self, p) -> tuple:
+        """Variant 3's MXFP4 rule for attention weights: p [n, 32] fp32 -> (codes [n, 32], e8 [n])."""
+        a = np.ascontiguousarray(p, dtype=np.float32).reshape(-1, 32)
+        codes = np.empty(a.shape, np.uint8)
+        e8 = np.empty(a.shape[0], np.uint8)
+        self.lib.oracle_p_block_fp4(a.ctypes.data, a.shape[0], codes.ctypes.data, e8.ctypes.data)
+        return codes, e8
 
     # ---- step 4
     def qk_int32(self, q_i8_head, k_i8_head, r0, nr, c0, nc) -> np.ndarray:

@@ -47,6 +47,9 @@
  * Variant 2 ([SA3]) replaces steps 3-5: Q and K' are quantised per token to MXFP4
  * (blocks of 32 channels), S = sum over blocks of 2^(eq + ek) * (E2M1 dot product),
  * s = sm_scale * S (no Q smoothing); steps 6-9 are those of variant 1.
+ * Variant 3 ([SA3]: FP4 attention) takes variant 2's scores and also runs P~ V in MXFP4:
+ * P~ per row in blocks of 32 keys (p_block_fp4) and V per channel in blocks of 32 tokens
+ * (quant_v_head_mx); attn_row_fp4 states the fp32 sequence that decides the P~ codes.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - means are exact: fp16 inputs are integer multiples of 2^-24, so the token
@@ -180,6 +183,31 @@ static uint8_t mx_block(const float* x, int n, uint8_t* codes) {
   return (uint8_t)code;
 }
 
+/* MXFP4 of one block of n attention weights P~ (variant 3; P~ in [0, 1]).  The pages give
+ * no format for P~.  The block is read as MXFP4 with the smallest shared exponent that
+ * holds the block's largest weight a without saturating, E = ceil(log2(a / 6)), instead
+ * of the OCP rule's floor(log2 a) - 2 (which maps a to [4, 8) and clips [6, 8) to 6):
+ *   E8M0 code = E + 127, clamped to [0, 254] (0 for an all-zero block); with
+ *   a = f * 2^e, f in [1, 2): E = e - 2, or e - 1 when f > 1.5;
+ *   elements E2M1(P~ / 2^(code - 127)), nearest even (the largest lies in (3, 6]).
+ * So a weight just below a power of two (1 - 2^-24, say) keeps its value up to the
+ * element grid, where the OCP rule would clip it to 6/8 of itself.
+ * Returns the E8M0 code. */
+static uint8_t p_block_fp4(const float* p, int n, uint8_t* codes) {
+  float a = 0.0f;
+  for (int i = 0; i < n; ++i) a = fmaxf(a, p[i]);
+  int code = 0;
+  if (a > 0.0f) {
+    int e;
+    const double f = 2.0 * frexp((double)a, &e); /* a = f * 2^(e-1), f in [1, 2) */
+    code = (e - 1) - 2 + (f > 1.5 ? 1 : 0) + 127;
+    if (code < 0) code = 0;
+    if (code > 254) code = 254;
+  }
+  for (int i = 0; i < n; ++i) codes[i] = oracle_e2m1_encode(ldexp((double)p[i], 127 - code));
+  return (uint8_t)code;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Step 1-3: means, smoothing, per-block INT8 quantisation                  */
 /* ------------------------------------------------------------------------ */
@@ -306,6 +334,31 @@ static void quant_v_head(const uint16_t* v, int N, int Np, int d, int smooth_v, 
   }
 }
 
+/* V in MXFP4 for one head (variant 3): per channel, blocks of 32 consecutive tokens
+ * (the contraction dimension of P~ V), the OCP rule of mx_block; tokens >= N are zeros.
+ * codes vt[d][Np] (one E2M1 code per byte), e8 [d][Np/32].  With smooth_v each channel
+ * first loses its exact token mean (vmean[d]; zeros otherwise). */
+static void quant_v_head_mx(const uint16_t* v, int N, int Np, int d, int smooth_v, uint8_t* vt, uint8_t* e8,
+                            float* vmean) {
+  float x[32];
+  for (int c = 0; c < d; ++c) {
+    const float mean = smooth_v ? exact_mean(v, d, 0, N, c) : 0.0f;
+    if (vmean) vmean[c] = mean;
+    for (int b = 0; b < Np / 32; ++b) {
+      for (int u = 0; u < 32; ++u) {
+        const int t = 32 * b + u;
+        if (t < N) {
+          const float y = (float)oracle_f16_decode(v[(size_t)t * d + c]);
+          x[u] = smooth_v ? y - mean : y;
+        } else {
+          x[u] = 0.0f;
+        }
+      }
+      e8[(size_t)c * (Np / 32) + b] = mx_block(x, 32, vt + (size_t)c * Np + 32 * b);
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Parameters and per-head preparation                                      */
 /* ------------------------------------------------------------------------ */
@@ -330,7 +383,8 @@ typedef struct {
   float* vs;         /* [d] (variant 1) */
   float* vm;         /* [d] (variant 1): v_mean, zeros without V smoothing */
   uint8_t *qc, *kc;  /* [Np][d] E2M1 codes (variant 2) */
-  uint8_t *qe, *ke;  /* [Np][d/32] E8M0 block scales (variant 2) */
+  uint8_t *qe, *ke;  /* [Np][d/32] E8M0 block scales (variants 2, 3) */
+  uint8_t* ve;       /* [d][Np/32] E8M0 scales of V (variant 3; vt holds E2M1 codes then) */
 } prep_t;
 
 static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -340,7 +394,7 @@ static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, c
   int nqg = (N + P->q_group - 1) / P->q_group;
   memset(h, 0, sizeof(*h));
   if (P->exact) return;
-  if (P->variant == 2) {
+  if (P->variant >= 2) {
     h->qc = (uint8_t*)malloc((size_t)Np * d);
     h->kc = (uint8_t*)malloc((size_t)Np * d);
     h->qe = (uint8_t*)malloc((size_t)Np * (d / 32));
@@ -358,18 +412,23 @@ static void prep_head(const params_t* P, const uint16_t* q, const uint16_t* k, c
     quant_head(k, N, Np, d, P->blk_k, P->blk_k, P->smooth_k ? 1 : 0, h->ki, h->ks, h->kmean, NULL);
     quant_head(q, N, Np, d, P->blk_q, P->q_group, P->smooth_q ? 2 : 0, h->qi, h->qs, NULL, h->qmean);
   }
-  if (P->variant >= 1) {
+  if (P->variant == 1 || P->variant == 2) {
     h->vt = (uint8_t*)malloc((size_t)d * Np);
     h->vs = (float*)malloc(sizeof(float) * (size_t)d);
     h->vm = (float*)malloc(sizeof(float) * (size_t)d);
     quant_v_head(v, N, Np, d, P->smooth_v, h->vt, h->vs, h->vm);
+  } else if (P->variant == 3) {
+    h->vt = (uint8_t*)malloc((size_t)d * Np);
+    h->ve = (uint8_t*)malloc((size_t)d * (Np / 32));
+    h->vm = (float*)malloc(sizeof(float) * (size_t)d);
+    quant_v_head_mx(v, N, Np, d, P->smooth_v, h->vt, h->ve, h->vm);
   }
 }
 
 static void free_prep(prep_t* h) {
   free(h->qi); free(h->ki); free(h->qs); free(h->ks); free(h->kmean); free(h->qmean);
   free(h->vt); free(h->vs); free(h->vm);
-  free(h->qc); free(h->kc); free(h->qe); free(h->ke);
+  free(h->qc); free(h->kc); free(h->qe); free(h->ke); free(h->ve);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -422,6 +481,21 @@ static float qsmooth_term(const qmfix_t* f, const int8_t* khat, int d, float ksc
   return w3 * b;
 }
 
+/* MXFP4 score of query i and key j (variants 2 and 3): per 32-channel block the exact
+ * E2M1 dot product times both block scales, summed exactly (fp64 holds every partial
+ * sum), then rounded once to fp32. */
+static float mx_score(const prep_t* h, int d, int i, int j) {
+  const int nb = d / 32;
+  double acc = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    double blk = 0.0;
+    for (int cc = 32 * b; cc < 32 * b + 32; ++cc)
+      blk += oracle_e2m1_decode(h->qc[(size_t)i * d + cc]) * oracle_e2m1_decode(h->kc[(size_t)j * d + cc]);
+    acc += ldexp(blk, (int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb + b] - 254);
+  }
+  return (float)acc;
+}
+
 /* O row i of one head for variants 1 and 2 (fp64, before the final fp16 rounding).
  *
  * The FP8 code of P~ * 448 is an integer that floating point decides, so it is decided
@@ -461,16 +535,7 @@ static void attn_row_fp8(const params_t* P, const prep_t* h, int i, double* o, d
     for (int j = j0; j < j1; ++j) {
       float S, c;
       if (P->variant == 2) {
-        /* per 32-channel block: exact E2M1 dot product times both block scales */
-        const int nb = d / 32;
-        double acc = 0.0;
-        for (int b = 0; b < nb; ++b) {
-          double blk = 0.0;
-          for (int cc = 32 * b; cc < 32 * b + 32; ++cc)
-            blk += oracle_e2m1_decode(h->qc[(size_t)i * d + cc]) * oracle_e2m1_decode(h->kc[(size_t)j * d + cc]);
-          acc += ldexp(blk, (int)h->qe[(size_t)i * nb + b] + (int)h->ke[(size_t)j * nb + b] - 254);
-        }
-        S = (float)acc;
+        S = mx_score(h, d, i, j);
         c = kscale;
       } else {
         S = (float)dot_i8(h->qi + (size_t)i * d, h->ki + (size_t)j * d, d);
@@ -511,10 +576,77 @@ static void attn_row_fp8(const params_t* P, const prep_t* h, int i, double* o, d
   for (int c = 0; c < d; ++c) o[c] = o[c] * (double)h->vs[c] / (448.0 * l) + (double)h->vm[c];
 }
 
+/* O row i of one head for variant 3 (fp64, before the final fp16 rounding): the scores
+ * of variant 2, and P~ V with both operands in MXFP4 ([SA3]: FP4 attention).
+ *
+ * P~ is decided in fp32 like the FP8 codes of variants 1 and 2, with the shift of P~
+ * itself (no 448):
+ *   c = kscale = sm_scale * log2(e);  t_j = c * S_ij;  m = running max of t over the
+ *   visible keys of the tiles so far;  z_j = fmaf(S_ij, c, -m);  P~_j = 2^(z_j) rounded
+ *   to fp32 (P~ <= 1, and P~ = 1 exactly at the running max).
+ * Each aligned block of 32 keys (bkv is a multiple of 32) is one MX block of the row,
+ * coded by p_block_fp4 with masked keys as zeros.  V is MXFP4 per channel over blocks of
+ * 32 tokens (quant_v_head_mx), so both operands of P~ V share the same key blocks.
+ * fp64 from there: alpha = 2^(m_old - m_new), l sums the unrounded fp32 P~ (R-11),
+ * O = alpha * O + sum_j Pdec_j * Vdec_j per tile (a fresh sum per tile), and the
+ * epilogue O / l (+ v_mean). */
+static void attn_row_fp4(const params_t* P, const prep_t* h, int i, double* o, double* work) {
+  const int N = P->N, d = P->d, bkv = P->bkv, Np = oracle_pad_len(N);
+  double* inner = work + 2 * bkv; /* the per-tile accumulator, d entries */
+  const float c = (float)P->sm_scale * 1.4426950408889634f;
+  float m = -INFINITY;
+  double l = 0.0;
+  for (int cc = 0; cc < d; ++cc) o[cc] = 0.0;
+  float Sf[256], pf[256];
+  uint8_t pc[256];
+  double pdec[256];
+
+  for (int j0 = 0; j0 < N; j0 += bkv) {
+    if (P->causal && j0 > i) break;
+    int j1 = j0 + bkv < N ? j0 + bkv : N;
+    if (P->causal && j1 > i + 1) j1 = i + 1;
+    float tmax = -INFINITY;
+    for (int j = j0; j < j1; ++j) {
+      Sf[j - j0] = mx_score(h, d, i, j);
+      const float t = c * Sf[j - j0];
+      if (t > tmax) tmax = t;
+    }
+    const float mnew = tmax > m ? tmax : m;
+    const double alpha = exp2((double)m - (double)mnew);
+    double wsum = 0.0;
+    for (int u = 0; u < bkv; ++u) pf[u] = 0.0f; /* masked keys and keys >= N: P~ = 0 */
+    for (int j = j0; j < j1; ++j) {
+      pf[j - j0] = (float)exp2((double)fmaf(Sf[j - j0], c, -mnew));
+      wsum += (double)pf[j - j0];
+    }
+    /* MX blocks of 32 keys: codes and their values */
+    for (int b0 = 0; b0 < bkv; b0 += 32) {
+      const uint8_t e = p_block_fp4(pf + b0, 32, pc + b0);
+      for (int u = b0; u < b0 + 32; ++u) pdec[u] = ldexp(oracle_e2m1_decode(pc[u]), (int)e - 127);
+    }
+    l = alpha * l + wsum;
+    for (int cc = 0; cc < d; ++cc) {
+      double acc = 0.0;
+      const uint8_t* vrow = h->vt + (size_t)cc * Np;
+      const uint8_t* erow = h->ve + (size_t)cc * (Np / 32);
+      for (int j = j0; j < j1; ++j)
+        acc += pdec[j - j0] * ldexp(oracle_e2m1_decode(vrow[j]), (int)erow[j / 32] - 127);
+      inner[cc] = acc;
+    }
+    for (int cc = 0; cc < d; ++cc) o[cc] = alpha * o[cc] + inner[cc];
+    m = mnew;
+  }
+  for (int cc = 0; cc < d; ++cc) o[cc] = o[cc] / l + (double)h->vm[cc];
+}
+
 /* O row i of one head (fp64, before the final fp16 rounding).
  * work: 2 * bkv + d doubles of scratch. */
 static void attn_row(const params_t* P, const prep_t* h, const uint16_t* q, const uint16_t* k,
                      const uint16_t* v, int i, double* o, double* work) {
+  if (P->variant == 3 && !P->exact) {
+    attn_row_fp4(P, h, i, o, work);
+    return;
+  }
   if (P->variant >= 1 && !P->exact) {
     attn_row_fp8(P, h, i, o, work);
     return;
@@ -663,8 +795,9 @@ static int check_params(const params_t* P) {
   if (P->bkv > 256 || P->d > 256) return -1; /* the row functions keep one tile and one row on the stack */
   if (P->q_group < 1 || P->blk_q % P->q_group) return -1;
   if (P->causal != 0 && P->causal != 1) return -1;
-  if (P->variant < 0 || P->variant > 2) return -1;
-  if (P->variant == 2 && (P->d % 32 || P->smooth_q)) return -1; /* MX blocks of 32; no Q smoothing */
+  if (P->variant < 0 || P->variant > 3) return -1;
+  if (P->variant >= 2 && (P->d % 32 || P->smooth_q)) return -1; /* MX blocks of 32; no Q smoothing */
+  if (P->variant == 3 && P->bkv % 32) return -1;                 /* tiles of whole P~ blocks */
   if (P->smooth_v != 0 && P->smooth_v != 1) return -1;
   if (!(P->sm_scale > 0.0) || !isfinite(P->sm_scale)) return -1;
   if ((int64_t)P->d * 127 * 127 > 2147483647LL) return -1; /* int32 bound of S */
@@ -803,6 +936,26 @@ int oracle_quant_mx(const uint16_t* q, const uint16_t* k, int B, int H, int N, i
     quant_head_mx(q + g * hs, N, Np, d, 0, q_codes + g * hp, q_e8 + g * he, NULL);
   }
   return 0;
+}
+
+/*
+ * Variant 3's V for all heads: v_codes [G][d][Np] (one E2M1 code per byte),
+ * v_e8 [G][d][Np/32] E8M0, v_mean [G][d] (zeros unless smooth_v).
+ */
+int oracle_quant_v_mx(const uint16_t* v, int B, int H, int N, int d, int smooth_v, uint8_t* v_codes,
+                      uint8_t* v_e8, float* v_mean) {
+  if (B < 1 || H < 1 || N < 1 || d < 1 || (smooth_v != 0 && smooth_v != 1)) return -1;
+  const int Np = oracle_pad_len(N), G = B * H;
+  const size_t hs = (size_t)N * d;
+  for (int g = 0; g < G; ++g)
+    quant_v_head_mx(v + g * hs, N, Np, d, smooth_v, v_codes + (size_t)g * d * Np,
+                    v_e8 + (size_t)g * d * (Np / 32), v_mean + (size_t)g * d);
+  return 0;
+}
+
+/* The MXFP4 rule of P~ (p_block_fp4) on n_blocks blocks of 32 fp32 weights. */
+void oracle_p_block_fp4(const float* p, int n_blocks, uint8_t* codes, uint8_t* e8) {
+  for (int b = 0; b < n_blocks; ++b) e8[b] = p_block_fp4(p + 32 * b, 32, codes + 32 * b);
 }
 
 /* Array forms of the codecs (for tests). */

@@ -14,6 +14,7 @@ import pytest
 import oracle as oracle_pkg
 from oracle import Oracle
 from tests import test_oracle_bwd_pins as bw
+from tests import test_oracle_fp4pv_pins as fp4
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "oracle.c")
@@ -57,6 +58,21 @@ MUTANTS = {
     "mx k not smoothed": ("quant_head_mx(k, N, Np, d, P->smooth_k ? 1 : 0,", "quant_head_mx(k, N, Np, d, 0,"),
     "v absmax before smoothing": ("      if (smooth_v) x = x - mean;\n      a = fmaxf(a, fabsf(x));",
                                   "      a = fmaxf(a, fabsf(x));"),
+    # MXFP4 P~V (variant 3)
+    "fp4 p rule saturates": ("code = (e - 1) - 2 + (f > 1.5 ? 1 : 0) + 127;", "code = (e - 1) - 2 + 127;"),
+    "fp4 p blocks of 64 keys": ("for (int b0 = 0; b0 < bkv; b0 += 32) {\n      const uint8_t e = p_block_fp4(pf + b0, 32, pc + b0);\n"
+                                "      for (int u = b0; u < b0 + 32; ++u)",
+                                "for (int b0 = 0; b0 < bkv; b0 += 64) {\n      const uint8_t e = p_block_fp4(pf + b0, 64, pc + b0);\n"
+                                "      for (int u = b0; u < b0 + 64; ++u)"),
+    "fp4 l sums the decoded p": ("l = alpha * l + wsum;",
+                                 "{ double s2 = 0.0; for (int u = 0; u < bkv; ++u) s2 += pdec[u]; l = alpha * l + s2; }"),
+    "fp4 rescale dropped": ("o[cc] = alpha * o[cc] + inner[cc];", "o[cc] = o[cc] + inner[cc];"),
+    "fp4 v scale of the wrong block": ("(int)erow[j / 32] - 127", "(int)erow[j / 64] - 127"),
+    "fp4 v mean not added back": ("o[cc] = o[cc] / l + (double)h->vm[cc];", "o[cc] = o[cc] / l;"),
+    "fp4 p shift keeps 448": ("pf[j - j0] = (float)exp2((double)fmaf(Sf[j - j0], c, -mnew));",
+                              "pf[j - j0] = (float)exp2((double)fmaf(Sf[j - j0], c, kLog2_448f - mnew));"),
+    "fp4 v tokens shifted": ("const int t = 32 * b + u;", "const int t = 32 * b + u + 1;"),
+    "fp4 v smoothing skipped": ("x[u] = smooth_v ? y - mean : y;", "x[u] = y;"),
     # backward
     "bwd D without the V-mean shift": ("if (!P->exact && P->smooth_v) D -= g * (double)vmean[c];", ""),
     "bwd dS sign": ("const double dsv = p * (dp - D);", "const double dsv = p * (D - dp);"),
@@ -116,6 +132,18 @@ def _battery(orc):
     for causal in (0, 1):
         yield f"mx lossless c{causal}", lambda causal=causal: pins.test_mx_lossless_inputs_match_exact_attention(orc, causal)
     yield "mx k smoothing", lambda: pins.test_mx_k_smoothing_removes_the_channel_offset_error(orc)
+    yield "fp4 p rule", lambda: fp4.test_p_block_scale_is_the_smallest_that_does_not_saturate(orc)
+    yield "fp4 p below a power of two", lambda: fp4.test_p_block_keeps_a_weight_just_below_a_power_of_two(orc)
+    yield "fp4 v blocks", lambda: fp4.test_v_mx_blocks_run_along_the_tokens(orc)
+    yield "fp4 v smoothing", lambda: fp4.test_v_mx_smoothing_subtracts_the_exact_token_mean(orc)
+    for causal in (0, 1):
+        yield f"fp4 q zero c{causal}", lambda causal=causal: fp4.test_q_zero_gives_the_mean_of_the_visible_v(orc, causal)
+        yield f"fp4 lossless c{causal}", (
+            lambda causal=causal: fp4.test_lossless_inputs_match_base2_softmax_attention(orc, causal))
+        yield f"fp4 l unrounded c{causal}", lambda causal=causal: fp4.test_l_sums_the_unrounded_p(orc, causal)
+        yield f"fp4 const v c{causal}", lambda causal=causal: fp4.test_v_smoothing_returns_a_constant_v_exactly(orc, causal)
+    yield "fp4 v scaling", lambda: fp4.test_power_of_two_scaling_of_v_scales_o(orc)
+    yield "fp4 vs fp64", lambda: fp4.test_fp4_attention_tracks_fp64_attention_config1(orc)
     for a in [(37, 32, 0), (37, 32, 1)]:
         yield f"bwd exact {a}", lambda a=a: bw.test_exact_mode_equals_autograd(orc, *a)
     for causal in (0, 1):
