@@ -19,7 +19,8 @@
  *    so the codes are reproducible;
  *   "SageAttention3: Microscaling FP4 Attention for Inference and An Exploration
  *    of 8-Bit Training" (abstract): FP4 attention on matrix units, taken here as
- *    variant 2 (MXFP4 Q K^T on the scaled FP4 MFMA, P~ V as variant 1).
+ *    variant 2 (MXFP4 Q K^T on the scaled FP4 MFMA, P~ V as variant 1) and variant 3
+ *    (P~ V in MXFP4 as well, both operands in blocks of 32 keys).
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, allocated and owned by the caller.
@@ -60,9 +61,13 @@ enum {
   SAGE_VARIANT_INT8QK_FP16PV = 0, /* SageAttention: INT8 Q K^T, FP16 P~ V (fp32 accumulation) */
   SAGE_VARIANT_INT8QK_FP8PV = 1,  /* SageAttention2-style: + Q smoothing, FP8 P~ and V; each key tile's
                                      P~ V products summed by the matrix unit into the fp32 O */
-  SAGE_VARIANT_MXFP4QK_FP8PV = 2  /* SageAttention3-style FP4 scores: per-token MXFP4 Q and K' (OCP
+  SAGE_VARIANT_MXFP4QK_FP8PV = 2, /* SageAttention3-style FP4 scores: per-token MXFP4 Q and K' (OCP
                                      microscaling, blocks of 32 channels), P~ V as variant 1; no Q
                                      smoothing */
+  SAGE_VARIANT_MXFP4QK_FP4PV = 3  /* SageAttention3-style FP4 attention: the scores of variant 2, and
+                                     P~ V on the scaled FP4 MFMA with P~ and V in MXFP4 over blocks
+                                     of 32 keys (see sage_quant_v_mx for V, sage_attn_fwd_qf16_fp4
+                                     for P~) */
 };
 
 /* Optional knobs.  Pass NULL for the defaults; set struct_size = sizeof(sage_params). */
@@ -72,7 +77,7 @@ typedef struct {
   int blk_k;    /* tokens per K scale block: 16, 32, 64 or 128 (default 64) */
   int smooth_k; /* subtract the token mean of K (default 1) */
   int smooth_q; /* subtract the block mean of Q and add its term back (default: variant == 1) */
-  int smooth_v; /* FP8 P~V variants (1, 2): subtract the token mean of V before FP8, add it to O
+  int smooth_v; /* variants 1-3: subtract the token mean of V before FP8 / MXFP4, add it to O
                    (SageAttention2 abstract, "smooth Q and V"; default 0) */
   int q_group;  /* rows per Q scale: 0 (= blk_q, default) or a power of two <= blk_q.
                    The SageAttention2 abstracts quantise Q and K at thread- / warp-level
@@ -277,6 +282,39 @@ size_t sage_attn_bwd_workspace_bytes(int B, int H, int N, int d, const sage_para
 int sage_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   float* dq, float* dk, float* dv, int B, int H, int N, int d, int causal, float sm_scale,
                   const sage_params* p, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * V of variant 3 in MXFP4 along the tokens (SageAttention3 abstract: FP4 attention; the
+ * block format is read as OCP MXFP4, as for Q and K): for each channel c, every block of
+ * 32 consecutive tokens gets the E8M0 code floor(log2 max|x|) - 2 + 127 clamped to
+ * [0, 254] (0 for an all-zero block) and E2M1 elements of x / 2^(code - 127), nearest
+ * even, saturating at 6; x = V (or V - v_mean with smooth_v, v_mean the exact token mean
+ * of sage_quant_v_ex); tokens >= N are zeros.
+ *   v_f4 [B,H,d,Np/2] bytes: two codes per byte along the tokens, the lower in the low
+ *     nibble (16-byte aligned);
+ *   v_e8 [B,H,Np/32,d] E8M0 codes, the scale of channel c at position
+ *     (c % 32) * (d/32) + c / 32 (4-byte aligned);
+ *   v_mean [B,H,d] fp32, written with smooth_v (may be NULL otherwise).
+ * ws: with smooth_v, sage_workspace_bytes(B, H, N, d, 3, p) bytes with p->smooth_v = 1
+ * suffice (only the token sums are used); may be NULL without it.
+ */
+int sage_quant_v_mx(const void* v, int B, int H, int N, int d, int smooth_v, uint8_t* v_f4, uint8_t* v_e8,
+                    float* v_mean, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The attention kernel that sage_attn_fwd runs for variant 3: Q is fp16 and quantised in
+ * the kernel to MXFP4 (the sage_quant_qk_mx rule); K from sage_quant_qk_mx; V from
+ * sage_quant_v_mx (same smooth_v as p).  Scores as variant 2; then, per query row and
+ * 64-key tile, with c = sm_scale * log2(e) and m the running maximum of c * S over the
+ * visible keys so far: P~_j = 2^fma(S_j, c, -m) in fp32 (<= 1), and each block of 32 keys
+ * becomes MXFP4 with the smallest power-of-two scale 2^E that holds its largest weight a
+ * without saturation (E8M0 code = E + 127, E = ceil(log2(a / 6)); 0 for a block of zeros;
+ * elements E2M1(P~ / 2^E), nearest even).  O accumulates the E2M1 x E2M1 products with
+ * both scales in fp32, rescaled when m moves; l sums the unrounded P~; O / l (+ v_mean).
+ */
+int sage_attn_fwd_qf16_fp4(const void* q, const uint8_t* k_f4, const uint8_t* k_e8, const uint8_t* v_f4,
+                           const uint8_t* v_e8, const float* v_mean, void* o, int B, int H, int N, int d,
+                           int causal, float sm_scale, const sage_params* p, void* stream);
 
 /*
  * Test surface: the int32 products S = Qhat Khat^T that the attention kernel forms,

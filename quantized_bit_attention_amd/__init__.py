@@ -7,7 +7,8 @@ computation runs in the HIP kernels of libsage.so; there is no other path.
 
 Method (pages): "SageAttention: Accurate 8-Bit Attention for Plug-and-play
 Inference Acceleration" (summary page, "Summary", "Interesting ideas" I1/I3) and
-"SageAttention2 ..." (abstract: Q smoothing, FP8 P~/V, two-level accumulation).
+"SageAttention2 ..." (abstract: Q smoothing, FP8 P~/V, two-level accumulation) and
+"SageAttention3 ..." (abstract: FP4 attention; variants 2 and 3 in MXFP4).
 """
 from __future__ import annotations
 
@@ -17,14 +18,16 @@ import os
 
 import torch
 
-__all__ = ["attn", "attn_noalloc", "attn_fwd_train", "attn_bwd", "quant_qk", "quant_v", "attn_prequant", "attn_qf16", "quant_qk_mx", "attn_prequant_mx",
-           "attn_qf16_mx",
+__all__ = ["attn", "attn_noalloc", "attn_fwd_train", "attn_bwd", "quant_qk", "quant_v", "attn_prequant", "attn_qf16",
+           "quant_qk_mx", "attn_prequant_mx", "attn_qf16_mx", "quant_v_mx", "attn_qf16_fp4",
            "debug_qk_int32", "workspace_bytes",
-           "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4"]
+           "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4",
+           "VARIANT_FP4PV"]
 
 VARIANT_FP16PV = 0
 VARIANT_FP8PV = 1
 VARIANT_MXFP4 = 2
+VARIANT_FP4PV = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsage.so")
@@ -70,6 +73,8 @@ def _load():
         "sage_quant_qk_mx": ([P, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "sage_attn_fwd_prequant_mx": ([P, P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_attn_fwd_qf16_mx": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
+        "sage_quant_v_mx": ([P, I, I, I, I, I, P, P, P, P, S, P], I),
+        "sage_attn_fwd_qf16_fp4": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_debug_qk_int32": ([P, P, I, I, I, I, P, I, P, P], I),
         "sage_attn_fwd_noalloc": ([P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
         "sage_attn_fwd_train": ([P, P, P, P, P, I, I, I, I, I, F, PP, P, S, P], I),
@@ -189,7 +194,7 @@ def attn(q, k, v, causal=False, sm_scale=None, variant=VARIANT_FP16PV, blk_q=128
 
     An empty input (B, H or N zero) returns the empty output without a launch.
 
-    smooth_v (FP8 P~V variants 1 and 2) subtracts V's token mean before FP8 and adds it to O.
+    smooth_v (variants 1-3) subtracts V's token mean before FP8 / MXFP4 and adds it to O.
     q_group: rows per Q scale (0 = blk_q; 1 = per token)."""
     B, H, N, d = _check_qkv(q, k, v)
     if sm_scale is None:
@@ -448,6 +453,47 @@ def _check_mx_operands(qk, vq, B, H, N, d, dev, smooth_v, with_q):
     _check_tensor(vq["v_scale"], "v_scale", (B, H, d), torch.float32, dev)
     if smooth_v:
         _check_tensor(vq["v_mean"], "v_mean", (B, H, d), torch.float32, dev)
+
+
+def quant_v_mx(v, smooth_v=False) -> dict:
+    """Variant 3's V in MXFP4 along the tokens: v_f4 [B, H, d, Np/2] (two E2M1 codes per byte, the
+    lower token in the low nibble), v_e8 [B, H, Np/32, d] (E8M0, channel c at (c % 32) * (d/32) +
+    c / 32), v_mean [B, H, d] (the token mean taken out with smooth_v, else zeros)."""
+    B, H, N, d = _check_qkv(v)
+    dev = v.device
+    Np = pad_len(N)
+    r = dict(v_f4=torch.empty((B, H, d, Np // 2), dtype=torch.uint8, device=dev),
+             v_e8=torch.empty((B, H, Np // 32, d), dtype=torch.uint8, device=dev),
+             v_mean=torch.zeros((B, H, d), dtype=torch.float32, device=dev))
+    lib = _load()
+    ws = _workspace(lib.sage_workspace_bytes(B, H, N, d, VARIANT_FP8PV, None), dev, None)
+    rc = lib.sage_quant_v_mx(_ptr(v), B, H, N, d, int(bool(smooth_v)), _ptr(r["v_f4"]), _ptr(r["v_e8"]),
+                             _ptr(r["v_mean"]), _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "sage_quant_v_mx")
+    return r
+
+
+def attn_qf16_fp4(q, qk: dict, vq: dict, causal=False, sm_scale=None, smooth_v=False, out=None):
+    """Variant-3 attention (MXFP4 scores and MXFP4 P~V) on fp16 q (quantised inside the kernel),
+    the K of quant_qk_mx() and the V of quant_v_mx()."""
+    B, H, N, d = _check_qkv(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    Np = pad_len(N)
+    _check_tensor(qk["k_f4"], "k_f4", (B, H, Np, d // 2), torch.uint8, q.device)
+    _check_tensor(qk["k_e8"], "k_e8", (B, H, Np, d // 32), torch.uint8, q.device)
+    _check_tensor(vq["v_f4"], "v_f4", (B, H, d, Np // 2), torch.uint8, q.device)
+    _check_tensor(vq["v_e8"], "v_e8", (B, H, Np // 32, d), torch.uint8, q.device)
+    if smooth_v:
+        _check_tensor(vq["v_mean"], "v_mean", (B, H, d), torch.float32, q.device)
+    out = _check_out(out, q.shape, q.device)
+    p = _params(128, 64, True, False, smooth_v)
+    rc = _load().sage_attn_fwd_qf16_fp4(
+        _ptr(q), _ptr(qk["k_f4"]), _ptr(qk["k_e8"]), _ptr(vq["v_f4"]), _ptr(vq["v_e8"]),
+        _ptr(vq["v_mean"]) if smooth_v else None, _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale),
+        ctypes.byref(p), _stream(q.device))
+    _check(rc, "sage_attn_fwd_qf16_fp4")
+    return out
 
 
 def debug_qk_int32(q_i8, k_i8, N, tiles) -> torch.Tensor:

@@ -71,9 +71,9 @@ int read_params(const sage_params* p, int variant, Params* out) {
       (r.smooth_v != 0 && r.smooth_v != 1))
     return fail(SAGE_ERR_INVALID_ARG, "smooth_k / smooth_q / smooth_v must be 0 or 1");
   if (r.smooth_v && variant == SAGE_VARIANT_INT8QK_FP16PV)
-    return fail(SAGE_ERR_UNSUPPORTED, "smooth_v applies to the FP8 P~V variants only");
-  if (r.smooth_q && variant == SAGE_VARIANT_MXFP4QK_FP8PV)
-    return fail(SAGE_ERR_UNSUPPORTED, "the MXFP4 variant quantises Q per token without smoothing (smooth_q must be 0)");
+    return fail(SAGE_ERR_UNSUPPORTED, "smooth_v applies to the FP8 / FP4 P~V variants only");
+  if (r.smooth_q && (variant == SAGE_VARIANT_MXFP4QK_FP8PV || variant == SAGE_VARIANT_MXFP4QK_FP4PV))
+    return fail(SAGE_ERR_UNSUPPORTED, "the MXFP4 variants quantise Q per token without smoothing (smooth_q must be 0)");
   if (r.q_group == 0) r.q_group = r.blk_q;
   if (!pow2(r.q_group) || r.q_group > r.blk_q)
     return fail(SAGE_ERR_UNSUPPORTED, "q_group must be 0 or a power of two <= blk_q (got %d)", r.q_group);
@@ -95,16 +95,17 @@ int check_ptr(const void* p, size_t align, const char* name) {
   return SAGE_OK;
 }
 
-// Variant 0 without Q smoothing, and variant 2, quantise Q inside the attention kernel.
-bool fuse_q(int variant, const Params& p) { return (variant == 0 && !p.smooth_q) || variant == 2; }
+// Variant 0 without Q smoothing, and variants 2 and 3, quantise Q inside the attention kernel.
+bool fuse_q(int variant, const Params& p) { return (variant == 0 && !p.smooth_q) || variant >= 2; }
 
-bool valid_variant(int variant) { return variant >= 0 && variant <= 2; }
+bool valid_variant(int variant) { return variant >= 0 && variant <= 3; }
 
-// Workspace layout (each piece 256-byte aligned).  Variant 2 keeps its packed E2M1
-// codes in q_i8 / k_i8 (d/2 bytes per row) and its E8M0 scales in q_e8 / k_e8.
+// Workspace layout (each piece 256-byte aligned).  Variants 2 and 3 keep their packed
+// E2M1 codes in q_i8 / k_i8 (d/2 bytes per row) and their E8M0 scales in q_e8 / k_e8;
+// variant 3 keeps V's E2M1 pairs in v_f8 (d rows of Np/2 bytes) and its scales in v_e8.
 struct Layout {
   size_t ksum, vsum, vmax, vmin, q_i8, k_i8, q_scale, k_scale, k_mean, q_mean, v_f8, v_scale, v_mean, q_e8, k_e8,
-      total;
+      v_e8, total;
 };
 
 size_t up(size_t x) { return (x + 255) / 256 * 256; }
@@ -115,7 +116,7 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
-  const bool fp8v = variant != 0, mx = variant == 2;
+  const bool fp8v = variant != 0, mx = variant >= 2, v4 = variant == 3;
   L.ksum = take(G * ns * d * sizeof(long long));
   L.vsum = take(fp8v ? G * ns * d * sizeof(long long) : 0);
   L.vmax = take(fp8v ? G * ns * d * sizeof(float) : 0);
@@ -127,11 +128,12 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   L.k_scale = take(mx ? 0 : G * nkb * sizeof(float));
   L.k_mean = take(G * d * sizeof(float));
   L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
-  L.v_f8 = take(fp8v ? G * d * Np : 0);
-  L.v_scale = take(fp8v ? G * d * sizeof(float) : 0);
+  L.v_f8 = take(fp8v ? G * d * (v4 ? Np / 2 : Np) : 0);
+  L.v_scale = take(fp8v && !v4 ? G * d * sizeof(float) : 0);
   L.v_mean = take(p.smooth_v ? G * d * sizeof(float) : 0);
   L.q_e8 = take(mx && !fq ? G * Np * (d / 32) : 0);
   L.k_e8 = take(mx ? G * Np * (d / 32) : 0);
+  L.v_e8 = take(v4 ? G * (Np / 32) * d : 0);
   L.total = off;
   return L;
 }
@@ -213,7 +215,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   int rc;
   if ((rc = check_shape(B, H, N, d))) return rc;
   if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (!valid_variant(variant)) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0, 1 or 2");
+  if (!valid_variant(variant)) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0, 1, 2 or 3");
   if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   Params p;
@@ -234,7 +236,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
     if (e != hipSuccess) return hip_fail(e, "statistics kernel");
   }
   const bool fq = fuse_q(variant, p);
-  if (variant == 2) {
+  if (variant >= 2) {
     // (Q is quantised by the attention kernel itself)
     e = sage::launch_quant_mx(d, k, G, N, Np, at<long long>(ws, L.ksum), p.smooth_k, at<uint8_t>(ws, L.k_i8),
                               at<uint8_t>(ws, L.k_e8), at<float>(ws, L.k_mean), st);
@@ -248,7 +250,11 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
     e = sage::launch_quant(d, qa, st);
     if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
   }
-  if (variant != 0) {
+  if (variant == 3) {
+    e = sage::launch_quant_v_mx(d, v, G, N, Np, stats.vsum, p.smooth_v, at<uint8_t>(ws, L.v_f8),
+                                at<uint8_t>(ws, L.v_e8), p.smooth_v ? at<float>(ws, L.v_mean) : nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "MXFP4 V quantisation kernel");
+  } else if (variant != 0) {
     e = sage::launch_quant_v(d, v, G, N, Np, stats, p.smooth_v, at<uint8_t>(ws, L.v_f8), at<float>(ws, L.v_scale),
                              p.smooth_v ? at<float>(ws, L.v_mean) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "V quantisation kernel");
@@ -257,14 +263,15 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   a.q = fq ? (const uint16_t*)q : nullptr;
   a.q_i8 = fq ? nullptr : at<int8_t>(ws, L.q_i8);
   a.k_i8 = at<int8_t>(ws, L.k_i8);
-  a.q_scale = fq || variant == 2 ? nullptr : at<float>(ws, L.q_scale);
-  a.k_scale = variant == 2 ? nullptr : at<float>(ws, L.k_scale);
+  a.q_scale = fq || variant >= 2 ? nullptr : at<float>(ws, L.q_scale);
+  a.k_scale = variant >= 2 ? nullptr : at<float>(ws, L.k_scale);
   a.q_mean = p.smooth_q ? at<float>(ws, L.q_mean) : nullptr;
-  a.q_e8 = nullptr;  // variant 2 quantises Q in the kernel
-  a.k_e8 = variant == 2 ? at<uint8_t>(ws, L.k_e8) : nullptr;
+  a.q_e8 = nullptr;  // variants 2 and 3 quantise Q in the kernel
+  a.k_e8 = variant >= 2 ? at<uint8_t>(ws, L.k_e8) : nullptr;
   a.v = (const uint16_t*)v;
   a.v_f8 = variant != 0 ? at<uint8_t>(ws, L.v_f8) : nullptr;
-  a.v_scale = variant != 0 ? at<float>(ws, L.v_scale) : nullptr;
+  a.v_e8 = variant == 3 ? at<uint8_t>(ws, L.v_e8) : nullptr;
+  a.v_scale = variant == 1 || variant == 2 ? at<float>(ws, L.v_scale) : nullptr;
   a.v_mean = p.smooth_v ? at<float>(ws, L.v_mean) : nullptr;
   a.o = (uint16_t*)o;
   a.lse = lse;
@@ -427,7 +434,7 @@ int sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, 
   int rc;
   // the argument checks of sage_attn_fwd_ex, then the size check, before any HIP call
   if ((rc = check_shape(B, H, N, d))) return rc;
-  if (!valid_variant(variant)) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0, 1 or 2");
+  if (!valid_variant(variant)) return fail(SAGE_ERR_INVALID_ARG, "variant must be 0, 1, 2 or 3");
   Params p;
   if ((rc = read_params(pp, variant, &p))) return rc;
   const size_t need = layout(B, H, N, d, variant, p).total;
@@ -671,6 +678,58 @@ int sage_attn_fwd_qf16_mx(const void* q, const uint8_t* k_f4, const uint8_t* k_e
   a.v_mean = p.smooth_v ? v_mean : nullptr;
   a.o = (uint16_t*)o;
   hipError_t e = sage::launch_attn(d, 2, causal, 0, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+int sage_quant_v_mx(const void* v, int B, int H, int N, int d, int smooth_v, uint8_t* v_f4, uint8_t* v_e8,
+                    float* v_mean, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (smooth_v != 0 && smooth_v != 1) return fail(SAGE_ERR_INVALID_ARG, "smooth_v must be 0 or 1");
+  if ((rc = check_ptr(v, 16, "v")) || (rc = check_ptr(v_f4, 16, "v_f4")) || (rc = check_ptr(v_e8, 4, "v_e8")))
+    return rc;
+  if (smooth_v && (rc = check_ptr(v_mean, 4, "v_mean (required with smooth_v)"))) return rc;
+  const size_t G = (size_t)B * H, ns = ceil_div(N, sage::kStatRows);
+  const size_t i64 = up(G * ns * d * sizeof(long long)), f32 = up(G * ns * d * sizeof(float));
+  hipStream_t st = (hipStream_t)stream;
+  if (smooth_v) {
+    // the token sums of V from the statistics pass (V given as K too; its K sums go unused)
+    if ((rc = check_ws(ws, ws_bytes, 2 * i64 + 2 * f32))) return rc;
+    const sage::StatsOut stats{at<long long>(ws, 0), at<long long>(ws, i64), at<float>(ws, 2 * i64),
+                               at<float>(ws, 2 * i64 + f32)};
+    hipError_t e = sage::launch_stats(d, v, v, true, (int)G, N, stats, st);
+    if (e != hipSuccess) return hip_fail(e, "statistics kernel");
+  }
+  hipError_t e = sage::launch_quant_v_mx(d, v, (int)G, N, pad_len(N), smooth_v ? at<long long>(ws, i64) : nullptr,
+                                         smooth_v, v_f4, v_e8, smooth_v ? v_mean : nullptr, st);
+  if (e != hipSuccess) return hip_fail(e, "MXFP4 V quantisation kernel");
+  return ok();
+}
+
+int sage_attn_fwd_qf16_fp4(const void* q, const uint8_t* k_f4, const uint8_t* k_e8, const uint8_t* v_f4,
+                           const uint8_t* v_e8, const float* v_mean, void* o, int B, int H, int N, int d, int causal,
+                           float sm_scale, const sage_params* pp, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, SAGE_VARIANT_MXFP4QK_FP4PV, &p))) return rc;
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k_f4, 16, "k_f4")) || (rc = check_ptr(k_e8, 4, "k_e8")) ||
+      (rc = check_ptr(v_f4, 16, "v_f4")) || (rc = check_ptr(v_e8, 4, "v_e8")) || (rc = check_ptr(o, 16, "o")))
+    return rc;
+  if (p.smooth_v && (rc = check_ptr(v_mean, 16, "v_mean (required with smooth_v)"))) return rc;
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
+  a.q = (const uint16_t*)q;
+  a.k_i8 = (const int8_t*)k_f4;
+  a.k_e8 = k_e8;
+  a.v_f8 = v_f4;
+  a.v_e8 = v_e8;
+  a.v_mean = p.smooth_v ? v_mean : nullptr;
+  a.o = (uint16_t*)o;
+  hipError_t e = sage::launch_attn(d, 3, causal, 0, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
 }

@@ -101,18 +101,21 @@ constexpr float kLazyLog2 = 8.0f;
 // partial sum l (the lane pair l, l^32 shares m; l is summed over the pair at the
 // end) and writes P~ already packed as the B operand of the P~V product:
 //  variant 0: pk[st*8 + u*4 + q] = fp16 pair (P~ of keys 8u+2q, 8u+2q+1 of block st);
-//  variant 1: pk[st*4 + w] = four E4M3 codes of P~ * 448 (keys 4w..4w+3 of block st).
+//  variant 1: pk[st*4 + w] = four E4M3 codes of P~ * 448 (keys 4w..4w+3 of block st);
+//  variant 3: pk[w] = eight E2M1 codes of the lane's 32 keys (s[st][i] is key kl + 16*st + i
+//  there), their MX block of P~, and pscale = its E8M0 scale code.
 // alpha is the factor the running O must be scaled by (rescale is false for the whole
 // wave when no lane needs it).
 // MASK: keys >= N, and keys > qi when causal, get P~ = 0 and stay out of the max.
 template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, typename SV>
 __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const float* bias, int kl, int N,
                                              int qi, float& m, float& l, uint32_t* pk, float& alpha,
-                                             bool& rescale, float lazy = kLazyLog2) {
+                                             bool& rescale, float lazy = kLazyLog2, uint32_t* pscale = nullptr) {
   // key kl + j is visible iff j <= jmax (keys < N, and <= qi when causal): one compare
   // against a constant per score
   const int jmax = (CAUSAL ? min(qi, N - 1) : N - 1) - kl;
-  auto keep = [&](int st, int i) { return !MASK || 32 * st + i <= jmax; };
+  constexpr int KST = VARIANT == 3 ? 16 : 32;  // key step between the two products
+  auto keep = [&](int st, int i) { return !MASK || KST * st + i <= jmax; };
   float x[2][16];
   float mt;
   if (SMOOTHQ) {
@@ -124,7 +127,7 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
         x[st][i] = fmaf((float)s[st][i], c[st], bias[32 * st + i]);
         mt = keep(st, i) ? fmaxf(mt, x[st][i]) : mt;
       }
-  } else if constexpr (VARIANT == 2) {
+  } else if constexpr (VARIANT >= 2) {
     // fp32 scores (MXFP4); c > 0, so max_j fl(c * S_j) = fl(c * max_j S_j)
     float mf[2];
 #pragma unroll
@@ -158,8 +161,51 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
   alpha = rescale ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;  // exp2(-inf) = 0 on the first tile
   m = mnew;
   l *= alpha;
-  const float shift = VARIANT == 0 ? -m : kLog2_448 - m;
+  const float shift = VARIANT == 0 || VARIANT == 3 ? -m : kLog2_448 - m;
   float psum[2] = {0.0f, 0.0f};
+  if constexpr (VARIANT == 3) {
+    // P~ = 2^fma(S, c, -m) <= 1; the lane's 32 keys are one MX block: its scale is the
+    // smallest power of two 2^E with max/2^E <= 6 (E8M0 code = biased exponent of the max
+    // - 2, + 1 when its mantissa exceeds 1.5), the elements E2M1(P~ / 2^E)
+    float pf[2][16];
+    float pm = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[st][i], c[st], shift));
+        if (MASK) pv = keep(st, i) ? pv : 0.0f;
+        pf[st][i] = pv;
+        psum[st] += pv;
+        pm = fmaxf(pm, pv);
+      }
+    const uint32_t pb = __float_as_uint(pm);
+    const int code = max((int)(pb >> 23) - 2 + ((pb & 0x7fffffu) > 0x400000u ? 1 : 0), 0);
+    float sc = __uint_as_float((uint32_t)max(code, 1) << 23);  // 2^(code - 127)
+    if (__builtin_amdgcn_ballot_w64(code == 0) != 0) {
+      // a block of zeros, or a largest weight below 2^-124 (scale code 0, 2^-127): such
+      // lanes scale by hand (exact) and convert with a unit scale
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pf[st][i] = code == 0 ? __builtin_amdgcn_ldexpf(pf[st][i], 127) : pf[st][i];
+      sc = code == 0 ? 1.0f : sc;
+    }
+    // the conversion divides by the scale (a power of two: exact) and rounds to nearest
+    // even, saturating at 6; pk[w] holds keys 8w .. 8w+7, the lower key in the low nibble
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* q8 = &pf[w >> 1][8 * (w & 1)];
+      uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q8[0], q8[1], sc, 0);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[2], q8[3], sc, 1);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[4], q8[5], sc, 2);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[6], q8[7], sc, 3);
+      pk[w] = word;
+    }
+    *pscale = (uint32_t)code;
+    l += psum[0] + psum[1];
+    return;
+  }
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -178,12 +224,10 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
         // the packs past the end of the interleaved block, so all 32 fp32 P~ of the lane
         // stay live across it (about 30 VGPRs, the third wave per SIMD at d = 64)
         asm volatile("" ::"v"(pk[st * 8 + i / 2]), "v"(pk[st * 8 + i / 2 + 1]));
-        // l sums the fp16 P~ that enter the product, two per dot instruction
-        psum[st] = sum_f16x2(pk[st * 8 + i / 2 + 1], sum_f16x2(pk[st * 8 + i / 2], psum[st]));
       } else {
-        psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
         pk[st * 4 + i / 4] = cvt_pk_fp8(pv[2], pv[3], cvt_pk_fp8(pv[0], pv[1], 0u, false), true);
       }
+      psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
     }
   l += psum[0] + psum[1];
 }
@@ -191,8 +235,8 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
 
 // Variant 0, unmasked tile: P~ against the row's current reference m, without the
 // tile's maximum.  The reference only has to keep P~ within fp16 and the sums
-// finite, so a tile whose P~ stay small keeps it: when every lane's 32 P~ (fp16) sum
-// to at most 2^kFastLog2, l gains that sum and pk holds the tile, and the function
+// finite, so a tile whose P~ stay small keeps it: when every lane's 32 P~ sum to at
+// most kFastSum = 2^10, l gains that sum and pk holds the tile, and the function
 // returns false.  Otherwise (a key far above m, or m = -inf on a row's first tile) it
 // returns true for the whole wave, leaves m and l untouched, and the caller recomputes
 // the tile with softmax_tile, which moves m to the running maximum.
@@ -211,7 +255,7 @@ __device__ __forceinline__ bool softmax_tile_fast(const i32x16* s, const float* 
       pk[st * 8 + i / 2] = pack_f16x2(p[0], p[1]);
       pk[st * 8 + i / 2 + 1] = pack_f16x2(p[2], p[3]);
       asm volatile("" ::"v"(pk[st * 8 + i / 2]), "v"(pk[st * 8 + i / 2 + 1]));  // as in softmax_tile
-      psum[st] = sum_f16x2(pk[st * 8 + i / 2 + 1], sum_f16x2(pk[st * 8 + i / 2], psum[st]));
+      psum[st] += (p[0] + p[1]) + (p[2] + p[3]);
     }
   const float t = psum[0] + psum[1];
   // also true for inf and NaN sums
@@ -297,9 +341,10 @@ __device__ __forceinline__ void interleave_schedule() {
   // halves); they are issued LEAD MFMAs ahead of their use, so the LDS latency (about
   // 200 cycles) overlaps the MFMAs and VALU work in between
   constexpr int LEAD = 2;
-  constexpr int MFMA = (VARIANT == 2 ? 2 * (D / 64) : 2 * (D / 32)) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
+  constexpr int MFMA = (VARIANT >= 2 ? 2 * (D / 64) : 2 * (D / 32)) + (VARIANT == 0 ? 4 * (D / 32) : D / 32);
   constexpr int VALU_PER = VARIANT == 0 ? (D == 128 ? 5 : 12)
                            : VARIANT == 1 ? (D == 128 ? 8 : 14)
+                           : VARIANT == 3 ? (D == 128 ? 22 : 40)
                                           : (D == 128 ? 20 : 16);
   // with Q smoothing the softmax first reads its 32 biases (8 reads of 16 bytes)
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD + (SMOOTHQ ? 8 : 0), 0);
@@ -317,9 +362,9 @@ __device__ __forceinline__ void interleave_schedule() {
 // rows are whole groups), or MXFP4 per 32-channel block (one lane's operand per block).
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
-  static_assert(!FUSEQ || ((VARIANT == 0 || VARIANT == 2) && !SMOOTHQ),
-                "in-kernel Q quantisation: variants 0 and 2, no Q smoothing");
-  static_assert(VARIANT != 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
+  static_assert(!FUSEQ || ((VARIANT == 0 || VARIANT >= 2) && !SMOOTHQ),
+                "in-kernel Q quantisation: variants 0, 2 and 3, no Q smoothing");
+  static_assert(VARIANT < 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
   constexpr int KD = qk_row_bytes<D, VARIANT>();  // bytes per Q / K row
   constexpr int NCT = D / 32;                       // 32-channel output tiles
@@ -358,7 +403,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
 
   const int8_t* __restrict__ qh = FUSEQ ? nullptr : a.q_i8 + (size_t)g * a.Np * KD;
   const int8_t* __restrict__ kh = a.k_i8 + (size_t)g * a.Np * KD;
-  const float* __restrict__ ksc = VARIANT == 2 ? nullptr : a.k_scale + (size_t)g * a.nkb;
+  const float* __restrict__ ksc = VARIANT >= 2 ? nullptr : a.k_scale + (size_t)g * a.nkb;
 
   const int ntiles_all = (N + kTileKV - 1) / kTileKV;
   const int wg_last_row = min(q0 + kAttnRows - 1, N - 1);
@@ -371,7 +416,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // 64*ks + 32*h .. +31 in qraw[4ks .. 4ks+3].  Rows >= N are zeros.
   uint4 qraw[FUSEQ ? D / 16 : 1];
   if constexpr (FUSEQ) {
-    constexpr int PER = VARIANT == 2 ? 4 : 2;  // 16-byte loads per k-step
+    constexpr int PER = VARIANT >= 2 ? 4 : 2;  // 16-byte loads per k-step
     const bool row_ok = wave_active && qi < N;
     const uint16_t* qsrc = a.q + ((size_t)g * N + (row_ok ? qi : 0)) * D + 8 * PER * h;
 #pragma unroll
@@ -388,12 +433,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const int kshift = __builtin_ctz(a.blk_k), qshift = __builtin_ctz(a.blk_q);
   // Q scale of this lane's row: one per group of q_group rows, so uniform over the wave
   // for groups of 32 rows or more (FUSEQ: set once the group's |Q| max is known)
-  float dq = (!FUSEQ && VARIANT != 2 && wave_active)
+  float dq = (!FUSEQ && VARIANT < 2 && wave_active)
                  ? a.q_scale[(size_t)g * a.nqg + (min(qi, N - 1) >> __builtin_ctz(a.q_group))]
                  : 0.0f;
   // variant 2: the MX scale bytes of this lane's query (rows >= N hold zeros)
   uint32_t qsw = 0;
-  if constexpr (VARIANT == 2 && !FUSEQ) {
+  if constexpr (VARIANT >= 2 && !FUSEQ) {
     if (wave_active) qsw = mx_lane_scales<D>(a.q_e8 + ((size_t)g * a.Np + qi) * (D / 32), h);
   }
 
@@ -419,8 +464,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // barrier also waits for the copies started before it.
   const TileCopy<D, VARIANT, kAttnWaves> copy(a.Np);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (size_t)a.Np * KD);
-  const __amdgpu_buffer_rsrc_t vrs = VARIANT == 0 ? make_rsrc(a.v + (size_t)g * N * D, (size_t)N * D * 2)
-                                                  : make_rsrc(a.v_f8 + (size_t)g * D * a.Np, (size_t)D * a.Np);
+  const __amdgpu_buffer_rsrc_t vrs =
+      VARIANT == 0   ? make_rsrc(a.v + (size_t)g * N * D, (size_t)N * D * 2)
+      : VARIANT == 3 ? make_rsrc(a.v_f8 + (size_t)g * D * (a.Np / 2), (size_t)D * (a.Np / 2))
+                     : make_rsrc(a.v_f8 + (size_t)g * D * a.Np, (size_t)D * a.Np);
 
   copy.k_tile(krs, 0, sK0);
   copy.v_tile(vrs, 0, a.Np, sV0);
@@ -454,7 +501,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   }
   wait_copies();
   __syncthreads();
-  if constexpr (FUSEQ && VARIANT == 2) {
+  if constexpr (FUSEQ && VARIANT >= 2) {
     // each k-step's 32 channels of this lane are one MX block
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) {
@@ -503,8 +550,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // between two register sets by tile parity.
   // (variant 2: S is fp32 from the scaled MFMA, c = sm_scale * log2(e), and kw holds
   // the MX scale bytes of this lane's key in each 32-key block of tile t+1)
-  constexpr int NPK = VARIANT == 0 ? 16 : 8;
-  using SAcc = std::conditional_t<VARIANT == 2, f32x16, i32x16>;
+  constexpr int NPK = VARIANT == 0 ? 16 : VARIANT == 3 ? 4 : 8;
+  using SAcc = std::conditional_t<VARIANT >= 2, f32x16, i32x16>;
   SAcc sA[2], sB[2];
   float cA[2], cB[2], kq[4];  // kq: raw K scales of tile t+1 (see tile_kscales)
   uint32_t kw[2];
@@ -512,28 +559,39 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   uint32_t pkA[NPK], pkB[NPK];
 #pragma unroll
   for (int i = 0; i < NPK; ++i) pkB[i] = 0u;  // P~(-1)
+  // variant 3: E8M0 scale codes of the P~ blocks (by tile parity) and of this lane's V
+  // channels (byte ct: channel 32*ct + l%32) for the V tiles in the two LDS slots; the
+  // zero P~(-1) and V slot of iteration 0 get unit scales (code 127)
+  uint32_t pscA = 127u, pscB = 127u;
+  uint32_t vsc[2] = {0x7f7f7f7fu, 0x7f7f7f7fu};
+  auto v_scales = [&](int t) -> uint32_t {
+    const uint8_t* e = a.v_e8 + ((size_t)g * (a.Np / 32) + 2 * t + h) * D + ql * (D / 32);
+    if constexpr (D == 128) return *reinterpret_cast<const uint32_t*>(e);
+    else return (uint32_t)*reinterpret_cast<const uint16_t*>(e);
+  };
   const float dqs = dq * a.kscale;
   // MX scale bytes of the keys this lane's A-operand rows hold in tile t (clamped into
   // the padded tensor; the pad rows carry zeros)
   auto mx_kscales = [&](int t, uint32_t* w) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int key = min(t * kTileKV + 32 * st + k_perm(ql), a.Np - 1);
+      const int key = min(t * kTileKV + k_row_key<VARIANT>(st, ql), a.Np - 1);
       w[st] = mx_lane_scales<D>(a.k_e8 + ((size_t)g * a.Np + key) * (D / 32), h);
     }
   };
   // S(t) for the K tile in sKt
   auto score_tile = [&](const int8_t* sKt, SAcc* out) {
-    if constexpr (VARIANT == 2)
+    if constexpr (VARIANT >= 2)
       qk_tile_mx<D>(sKt, sQw, lane, kw, qsw, out);
     else
       qk_tile<D>(sKt, sQw, lane, out);
   };
-  if constexpr (VARIANT == 2) {
+  if constexpr (VARIANT >= 2) {
     mx_kscales(0, kw);
     if (wave_active) score_tile(sK0, sA);  // tile 0 is visible to every row
     cA[0] = cA[1] = a.kscale;
     mx_kscales(1, kw);
+    if constexpr (VARIANT == 3) vsc[0] = v_scales(0);
   } else {
     if (wave_active) score_tile(sK0, sA);  // tile 0 is visible to every row
     tile_kscales(ksc, 0, last_key, kshift, kq);
@@ -550,12 +608,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // transpose-read base of this lane in a V tile (variant 0)
   const int vbase_off = pv_lane_offset<D>(lane);
 
-  // O += P~(t-1) V(t-1) from the V tile in slot sVp with P~ packed in pkp.
-  auto pv_tile = [&](const uint8_t* sVp, const uint32_t* pkp) {
+  // O += P~(t-1) V(t-1) from the V tile in slot sVp with P~ packed in pkp (variant 3:
+  // with the scale code psp of the P~ block and the V scale bytes vs).
+  auto pv_tile = [&](const uint8_t* sVp, const uint32_t* pkp, uint32_t psp = 0u, uint32_t vs = 0u) {
     if constexpr (VARIANT == 0) {
       // A operand V^T: a transpose read of 4 keys x 16 channels (one 128-byte block)
       // gives lane j of a 16-lane group channel C0 + j for 4 keys.
       pv_tile_f16<D>(sVp + vbase_off, pkp, o);
+    } else if constexpr (VARIANT == 3) {
+      // E2M1 x E2M1 with both MX scales: lane half h brings keys 32h .. 32h + 31 of the
+      // tile for its query (B) and for its channel (A, 16 bytes of the V^T slot)
+      const i32x4 p4 = {(int)pkp[0], (int)pkp[1], (int)pkp[2], (int)pkp[3]};
+      const i32x8 pb = __builtin_shufflevector(p4, p4, 0, 1, 2, 3, -1, -1, -1, -1);  // FP4 uses 4 registers
+      auto tile_ct = [&](auto ctc) {  // the scale byte select must be a constant
+        constexpr int ct = decltype(ctc)::value;
+        const i32x4 v4 = *reinterpret_cast<const i32x4*>(sVp + 16 * lane + ct * 1024);
+        const i32x8 va = __builtin_shufflevector(v4, v4, 0, 1, 2, 3, -1, -1, -1, -1);
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, o[ct], 4, 4, ct, (int)vs, 0, (int)psp);
+      };
+      tile_ct(std::integral_constant<int, 0>{});
+      tile_ct(std::integral_constant<int, 1>{});
+      if constexpr (NCT == 4) {
+        tile_ct(std::integral_constant<int, 2>{});
+        tile_ct(std::integral_constant<int, 3>{});
+      }
     } else {
       // the FP8 MFMA accumulates in fp32, straight into O: the fp32 outer accumulator of
       // two-level accumulation, already rescaled for this tile at the end of the last
@@ -586,6 +662,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     float* const cn = cur == 0 ? cB : cA;
     uint32_t* const pk = cur == 0 ? pkA : pkB;        // P~(t)
     const uint32_t* const pkp = cur == 0 ? pkB : pkA; // P~(t-1)
+    uint32_t* const psc = cur == 0 ? &pscA : &pscB;   // variant 3: block scale of P~(t)
+    const uint32_t psp = cur == 0 ? pscB : pscA;      //  and of P~(t-1)
 
     const bool compute = wave_active && t < T && t <= wave_last;
     const bool compute_next = wave_active && t + 1 <= wave_last && t + 1 < T;
@@ -594,7 +672,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     const bool pv_prev = wave_active && t - 1 <= wave_last;
     const bool full = (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw);
 
-    if constexpr (VARIANT == 2) {
+    if constexpr (VARIANT >= 2) {
       cn[0] = cn[1] = a.kscale;
     } else {
       cn[0] = dqs * kscale_of(kq, 0, h);  // tile t+1
@@ -607,7 +685,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     float alpha = 1.0f;
     bool rescale = false;
     const float* bias = SMOOTHQ ? sBc + ((qw - q0) >> qshift) * kTileKV + 16 * h : nullptr;
-    const int kl = t * kTileKV + 16 * h;  // key of register 0 of this lane
+    const int kl = t * kTileKV + (VARIANT == 3 ? 32 : 16) * h;  // key of register 0 of this lane
     if (compute && compute_next && pv_prev && full) {
       // Interior tile: one basic block, MFMA work (S(t+1), P~(t-1) V(t-1)) interleaved
       // with the softmax of tile t so the matrix and vector units run together.
@@ -616,9 +694,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       // d = 128, neutral at d = 64; variant 1 measured slower with it)
       if constexpr (VARIANT == 0) __builtin_amdgcn_s_setprio(3);
       if constexpr (VARIANT != 0) {
-        pv_tile(sVp, pkp);
+        pv_tile(sVp, pkp, psp, vsc[cur ^ 1]);
         score_tile(sKn, sn);
-        softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+        softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, kLazyLog2,
+                                                      psc);
         interleave_schedule<D, VARIANT, SMOOTHQ>();
       } else if constexpr (D == 128 && !SMOOTHQ) {
         score_tile(sKn, sn);
@@ -637,12 +716,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       }
     } else {
       if (compute_next) score_tile(sKn, sn);
-      if (pv_prev) pv_tile(sVp, pkp);
+      if (pv_prev) pv_tile(sVp, pkp, psp, vsc[cur ^ 1]);
       if (compute) {
         if (full)
-          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, kLazyLog2,
+                                                        psc);
         else
-          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale);
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, kLazyLog2,
+                                                       psc);
       }
     }
     if (rescale) {  // O already holds P~(t-1) V(t-1)
@@ -652,14 +733,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
 
     // K scales of tile t+2 for the next iteration: issued here, their latency overlaps
     // the barrier
-    if constexpr (VARIANT == 2)
+    if constexpr (VARIANT >= 2)
       mx_kscales(t + 2, kw);
     else
       tile_kscales(ksc, t + 2, last_key, kshift, kq);
     if (t < T) {
       wait_copies();
       __syncthreads();
-      if (t + 1 < T) copy.v_tile(vrs, t + 1, a.Np, sVp);
+      if (t + 1 < T) {
+        copy.v_tile(vrs, t + 1, a.Np, sVp);
+        if constexpr (VARIANT == 3) vsc[cur ^ 1] = v_scales(t + 1);  // read with V(t+1) at iteration t+2
+      }
     }
   };
 
@@ -673,9 +757,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   const float inv = 1.0f / l;
   if (qi >= N) return;
   // training: the row log-sum-exp, log(sum_j e^(s_ij)) = ln2 * (m + log2 l) (m and l are in
-  // base-2 units; variant 1 counts P~ * 448)
+  // base-2 units; variants 1 and 2 count P~ * 448)
   if (a.lse && h == 0)
-    a.lse[(size_t)g * N + qi] = 0.6931471805599453f * (m + __builtin_amdgcn_logf(l) - (VARIANT == 0 ? 0.0f : kLog2_448));
+    a.lse[(size_t)g * N + qi] =
+        0.6931471805599453f * (m + __builtin_amdgcn_logf(l) - (VARIANT == 1 || VARIANT == 2 ? kLog2_448 : 0.0f));
   uint16_t* orow = a.o + ((size_t)g * N + qi) * D;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
@@ -685,9 +770,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       float y[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) y[b] = o[ct][4 * a4 + b] * inv;
-      if (VARIANT != 0) {
+      if (VARIANT == 1 || VARIANT == 2) {  // variant 3's V scales sit inside the product
         const float4 dv = *reinterpret_cast<const float4*>(a.v_scale + (size_t)g * D + c0);
         y[0] *= dv.x; y[1] *= dv.y; y[2] *= dv.z; y[3] *= dv.w;
+      }
+      if (VARIANT != 0) {
         if (a.v_mean) {  // V smoothing: every row of P~ sums to one after the division by l
           const float4 vm = *reinterpret_cast<const float4*>(a.v_mean + (size_t)g * D + c0);
           y[0] += vm.x; y[1] += vm.y; y[2] += vm.z; y[3] += vm.w;
@@ -750,8 +837,12 @@ static hipError_t launch_dv(int causal, int smooth_q, const AttnArgs& a, hipStre
 }
 
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st) {
-  if (a.q) {  // fp16 Q, quantised in the kernel (variant 0 without Q smoothing, variant 2)
+  if (a.q) {  // fp16 Q, quantised in the kernel (variant 0 without Q smoothing, variants 2 and 3)
     if (variant == 1 || smooth_q) return hipErrorInvalidValue;
+    if (variant == 3) {
+      if (d == 64) return causal ? launch_one<64, 3, true, false, true>(a, st) : launch_one<64, 3, false, false, true>(a, st);
+      return causal ? launch_one<128, 3, true, false, true>(a, st) : launch_one<128, 3, false, false, true>(a, st);
+    }
     if (variant == 2) {
       if (d == 64) return causal ? launch_one<64, 2, true, false, true>(a, st) : launch_one<64, 2, false, false, true>(a, st);
       return causal ? launch_one<128, 2, true, false, true>(a, st) : launch_one<128, 2, false, false, true>(a, st);
@@ -759,6 +850,7 @@ hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnA
     if (d == 64) return causal ? launch_one<64, 0, true, false, true>(a, st) : launch_one<64, 0, false, false, true>(a, st);
     return causal ? launch_one<128, 0, true, false, true>(a, st) : launch_one<128, 0, false, false, true>(a, st);
   }
+  if (variant == 3) return hipErrorInvalidValue;  // variant 3 always quantises Q in the kernel
   if (variant == 2) {  // MXFP4 scores, never with Q smoothing
     if (smooth_q) return hipErrorInvalidValue;
     if (d == 64) return causal ? launch_one<64, 2, true, false>(a, st) : launch_one<64, 2, false, false>(a, st);

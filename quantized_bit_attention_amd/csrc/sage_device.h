@@ -149,10 +149,4 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// acc + (the two fp16 halves of h), the products and the sum in fp32 (v_dot2_f32_f16).
-__device__ __forceinline__ float sum_f16x2(uint32_t h, float acc) {
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), one, acc, false);
-}
-
 }  // namespace sage

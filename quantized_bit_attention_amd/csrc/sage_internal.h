@@ -29,7 +29,8 @@ struct AttnArgs {
   const float* k_scale;   // [G][nkb]
   const float* q_mean;    // [G][nqb][D] (variant 1 with Q smoothing)
   const uint16_t* v;      // [G][N][D] fp16 (variant 0)
-  const uint8_t* v_f8;    // [G][D][Np] (variant 1)
+  const uint8_t* v_f8;    // [G][D][Np] (variants 1, 2); variant 3: [G][D][Np/2] E2M1 pairs
+  const uint8_t* v_e8;    // [G][Np/32][D] MX scales of V (variant 3)
   const float* v_scale;   // [G][D] (variant 1)
   const float* v_mean;    // [G][D] (variants 1, 2 with V smoothing) or null
   const uint8_t* q_e8;    // [G][Np][D/32] MX block scales (variant 2; q_i8 / k_i8 then
@@ -62,6 +63,11 @@ hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const Stat
 // sums): codes [G][Np][D/2] (two E2M1 per byte), e8 [G][Np][D/32]; rows >= N zero.
 hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const long long* ksum_part, int smooth,
                            uint8_t* codes, uint8_t* e8, float* k_mean, hipStream_t st);
+// Variant 3: V to MXFP4 along the tokens, v_f4 [G][D][Np/2] (two E2M1 per byte),
+// v_e8 [G][Np/32][D] (channel c at (c % 32) * (D/32) + c / 32); vsum_part from the
+// statistics pass (used with smooth_v).
+hipError_t launch_quant_v_mx(int d, const void* v, int G, int N, int Np, const long long* vsum_part, int smooth_v,
+                             uint8_t* v_f4, uint8_t* v_e8, float* v_mean, hipStream_t st);
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st);
 // Backward (sage_bwd.hip).  Inputs [G][N][D] fp16 unless noted; the workspace pieces are
 // filled by the statistics pass (ksum, vsum), the quantisation pass (q_i8, k_i8 and their

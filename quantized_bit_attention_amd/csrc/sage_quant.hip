@@ -509,6 +509,76 @@ hipError_t launch_quant_mx(int d, const void* x, int G, int N, int Np, const lon
   return hipGetLastError();
 }
 
+// Variant 3: V -> MXFP4 along the tokens (the contraction dimension of P~ V): for each
+// channel, blocks of 32 consecutive tokens get one E8M0 scale and 32 E2M1 codes (the
+// OCP rule of mx_block_fp4), after the exact token mean with V smoothing.  Tokens >= N
+// are zeros.  One workgroup per (64-token tile, head): the tile goes through LDS as
+// fp32 so the fp16 reads run along the channels and each thread then codes one
+// (channel, 32-token block).
+//   v_f4 [G][D][Np/2]: two codes per byte, the lower token in the low nibble;
+//   v_e8 [G][Np/32][D]: the scale of channel c sits at (c % 32) * (D/32) + c / 32, so the
+//        D/32 scales one lane of the P~ V product needs (channels r, r+32, ..) are adjacent.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_v_mx_kernel(const uint16_t* __restrict__ v, int N, int Np,
+                                                              int nsplit, const long long* __restrict__ vsum_part,
+                                                              int smooth_v, uint8_t* __restrict__ v_f4,
+                                                              uint8_t* __restrict__ v_e8,
+                                                              float* __restrict__ v_mean) {
+  constexpr int TPR = D / 8;
+  constexpr int RPI = kThreads / TPR;
+  constexpr int TT = 64;  // tokens per tile
+  __shared__ float s_mean[D];
+  __shared__ float s_t[D][TT + 1];
+  const int ntiles = Np / TT;  // 1-D grid over (head, 64-token tile)
+  const int tile = blockIdx.x % ntiles, g = blockIdx.x / ntiles, tid = threadIdx.x;
+  if (tid < D) {
+    const float mean = smooth_v ? fixed24_mean(vsum_part[(size_t)g * nsplit * D + tid], N) : 0.0f;
+    s_mean[tid] = mean;
+    if (tile == 0 && v_mean) v_mean[(size_t)g * D + tid] = mean;
+  }
+  __syncthreads();
+  const int cg = tid % TPR, r0 = tid / TPR;
+  const size_t head = (size_t)g * N * D;
+  for (int rr = r0; rr < TT; rr += RPI) {
+    const int t = tile * TT + rr;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t < N) raw = *reinterpret_cast<const uint4*>(v + head + (size_t)t * D + cg * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const bool centre = smooth_v && t < N;  // padding tokens stay zero
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x2 h = __builtin_bit_cast(f16x2, w[j]);
+      const int c = cg * 8 + 2 * j;
+      s_t[c][rr] = centre ? (float)h[0] - s_mean[c] : (float)h[0];
+      s_t[c + 1][rr] = centre ? (float)h[1] - s_mean[c + 1] : (float)h[1];
+    }
+  }
+  __syncthreads();
+  if (tid < 2 * D) {
+    const int c = tid % D, b = tid / D;  // channel, 32-token block of the tile
+    float x[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) x[u] = s_t[c][32 * b + u];
+    uint4 packed;
+    const uint32_t code = mx_block_fp4(x, packed);
+    *reinterpret_cast<uint4*>(v_f4 + ((size_t)g * D + c) * (Np / 2) + tile * (TT / 2) + 16 * b) = packed;
+    v_e8[((size_t)g * (Np / 32) + 2 * tile + b) * D + (c % 32) * (D / 32) + c / 32] = (uint8_t)code;
+  }
+}
+
+hipError_t launch_quant_v_mx(int d, const void* v, int G, int N, int Np, const long long* vsum_part, int smooth_v,
+                             uint8_t* v_f4, uint8_t* v_e8, float* v_mean, hipStream_t st) {
+  const int grid = Np / 64 * G;
+  const int ns = stat_splits(N);
+  if (d == 64)
+    quant_v_mx_kernel<64><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, ns, vsum_part, smooth_v, v_f4, v_e8,
+                                                     v_mean);
+  else
+    quant_v_mx_kernel<128><<<grid, kThreads, 0, st>>>((const uint16_t*)v, N, Np, ns, vsum_part, smooth_v, v_f4, v_e8,
+                                                      v_mean);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_v(int d, const void* v, int G, int N, int Np, const StatsOut& stats, int smooth_v,
                           uint8_t* v_f8, float* v_scale, float* v_mean, hipStream_t st) {
   const int grid = Np / 64 * G;

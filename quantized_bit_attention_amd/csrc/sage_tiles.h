@@ -13,20 +13,31 @@ namespace sage {
 // (8 lanes of ds_read_b128, 16 lanes of ds_read_b64_tr_b16) covers one contiguous
 // 128-byte run, which is free of bank conflicts, and every operand address is the
 // lane's base plus a compile-time offset.
-// Bytes per Q / K row: D int8 codes, or D/2 bytes of two E2M1 codes (variant 2).
+// Bytes per Q / K row: D int8 codes, or D/2 bytes of two E2M1 codes (variants 2, 3).
 template <int D, int VARIANT>
-constexpr int qk_row_bytes() { return VARIANT == 2 ? D / 2 : D; }
+constexpr int qk_row_bytes() { return VARIANT >= 2 ? D / 2 : D; }
 
 template <int D, int VARIANT>
 struct Lds {
   static constexpr int K_BYTES = kTileKV * qk_row_bytes<D, VARIANT>();  // 64 keys
-  static constexpr int V_BYTES = VARIANT == 0 ? kTileKV * D * 2   // 64 keys x D fp16
-                                              : D * kTileKV;      // D channels x 64 keys fp8
+  static constexpr int V_BYTES = VARIANT == 0   ? kTileKV * D * 2     // 64 keys x D fp16
+                                 : VARIANT == 3 ? D * kTileKV / 2     // D channels x 64 keys E2M1
+                                                : D * kTileKV;        // D channels x 64 keys fp8
 };
 
 // Row of the K tile that feeds A-operand row r: accumulator register i of lane half h
 // then holds key 16h + i of the 32-key block.
 __device__ __forceinline__ int k_perm(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// Key (within the 64-key tile) of A-operand row r of the S^T product of 32-key block st.
+// Variants 0-2: key 32*st + k_perm(r), so register i of lane half h is key 32*st + 16h + i.
+// Variant 3 interleaves the two products so that lane half h holds the 32 consecutive
+// keys 32h .. 32h + 31 (register i of product st is key 32h + 16*st + i): one MX block of
+// P~ per lane, the k-slots of its half of the FP4 P~ V operand.
+template <int VARIANT>
+__device__ __forceinline__ int k_row_key(int st, int r) {
+  return VARIANT == 3 ? 32 * ((r >> 2) & 1) + 16 * st + 4 * (r >> 3) + (r & 3) : 32 * st + k_perm(r);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -60,7 +71,7 @@ struct TileCopy {
   static constexpr int KD = qk_row_bytes<D, VARIANT>();  // bytes per K row
   static constexpr int CPR = KD / 16;
   static constexpr int K_COPIES = kTileKV * CPR / 64;                                      // 1 KB each
-  static constexpr int V_COPIES = (VARIANT == 0 ? kTileKV * 2 * D : D * kTileKV) / 16 / 64;
+  static constexpr int V_COPIES = Lds<D, VARIANT>::V_BYTES / 16 / 64;
   static constexpr int K_PER_WAVE = (K_COPIES + NWAVES - 1) / NWAVES;
   static constexpr int V_PER_WAVE = (V_COPIES + NWAVES - 1) / NWAVES;
   // memory distance between copy c and copy c + NWAVES of a lane (see the layouts above)
@@ -74,7 +85,7 @@ struct TileCopy {
     {
       const int s = (wave % K_COPIES) * 64 + lane;
       const int x = s & 31, rest = s >> 5;
-      koff = (uint32_t)(32 * (rest / CPR) + k_perm(x)) * KD + (rest % CPR) * 16;
+      koff = (uint32_t)k_row_key<VARIANT>(rest / CPR, x) * KD + (rest % CPR) * 16;
     }
     {
       const int s = (wave % V_COPIES) * 64 + lane;
@@ -82,12 +93,17 @@ struct TileCopy {
         constexpr int BPR = D / 16;
         const int w = s & 7, blk = s >> 3;
         voff = (uint32_t)(4 * (blk / BPR) + (w >> 1)) * (2 * D) + 2 * (16 * (blk % BPR) + 8 * (w & 1));
+      } else if (VARIANT == 3) {
+        // copy c: channels 32c .. 32c + 31; lane l takes channel 32c + l%32, keys 32h .. 32h + 31
+        // of the tile (h = l/32), the 16 bytes its P~ V operand reads
+        voff = (uint32_t)(32 * (s >> 6) + (lane & 31)) * (uint32_t)(Np / 2) + 16 * (lane >> 5);
       } else {
         const int y = s & 31, rest = s >> 5;
         voff = (uint32_t)(32 * (rest >> 2) + y) * Np + 16 * (rest & 3);
       }
     }
     static_assert((NWAVES * 2) % CPR == 0, "K copies of one wave must step by whole 32-key blocks");
+    static_assert(VARIANT != 3 || (K_PER_WAVE == 1 && V_PER_WAVE == 1), "variant 3: one K and one V copy per wave");
     static_assert(VARIANT != 0 || (NWAVES * 8) % (D / 16) == 0, "V copies must step by whole key rows");
     static_assert(VARIANT == 0 || (NWAVES * 2) % 4 == 0, "V^T copies must step by whole channel rows");
   }
@@ -113,6 +129,8 @@ struct TileCopy {
       if (V_COPIES % NWAVES == 0 || c < V_COPIES) {
         if (VARIANT == 0)
           copy16_to_lds(vrs, voff + i * V_STEP + (uint32_t)(t * kTileKV * 2 * D), 0u, sV + c * 1024);
+        else if (VARIANT == 3)
+          copy16_to_lds(vrs, voff, (uint32_t)(t * kTileKV / 2), sV + c * 1024);
         else
           copy16_to_lds(vrs, voff + i * V_STEP * (uint32_t)Np, (uint32_t)(t * kTileKV), sV + c * 1024);
       }

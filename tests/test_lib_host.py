@@ -50,8 +50,8 @@ def test_pure_helpers(lib):
     assert lib.sage_pad_len(1) == 128 and lib.sage_pad_len(128) == 128 and lib.sage_pad_len(17776) == 17792
     assert lib.sage_pad_len(0) == -1
     assert lib.sage_kv_tile(0, 64) == 64 and lib.sage_kv_tile(1, 128) == 64
-    assert lib.sage_kv_tile(2, 64) == 64
-    assert lib.sage_kv_tile(3, 64) < 0 and lib.sage_kv_tile(0, 96) < 0
+    assert lib.sage_kv_tile(2, 64) == 64 and lib.sage_kv_tile(3, 128) == 64
+    assert lib.sage_kv_tile(4, 64) < 0 and lib.sage_kv_tile(0, 96) < 0
     assert lib.sage_version() >= 100
 
 
@@ -81,6 +81,13 @@ def test_workspace_size(lib):
     v2 = (up(G * ns * d * 8) * 2 + up(G * ns * d * 4) * 2 + up(G * Np * d // 2) + up(G * d * 4)
           + up(G * d * Np) + up(G * d * 4) + up(G * Np * d // 32))
     assert sage.workspace_bytes(B, H, N, d, 2) == v2
+    # MXFP4 P~V variant: as variant 2, but V in packed E2M1 (Np/2 bytes per channel) with one
+    # E8M0 scale per channel and 32 tokens, and no per-channel FP8 scales
+    v3 = (up(G * ns * d * 8) * 2 + up(G * ns * d * 4) * 2 + up(G * Np * d // 2) + up(G * d * 4)
+          + up(G * d * Np // 2) + up(G * Np * d // 32) + up(G * (Np // 32) * d))
+    assert sage.workspace_bytes(B, H, N, d, 3) == v3
+    assert sage.workspace_bytes(B, H, N, d, 3, smooth_v=True) == v3 + up(G * d * 4)
+    assert sage.workspace_bytes(B, H, N, d, 3, smooth_q=True) == 0
     assert sage.workspace_bytes(1, 1, 0, 64, 0) == 0
     assert sage.workspace_bytes(1, 1, 64, 80, 0) == 0
 
@@ -99,7 +106,8 @@ def attn(lib, q=A, k=A, v=A, o=A, B=1, H=1, N=64, d=64, causal=0, sm=0.125, vari
     (dict(B=0), -1, "B, H, N"),
     (dict(B=1 << 12, H=1 << 8, N=1 << 10, d=128), -1, "2^31"),
     (dict(causal=2), -1, "causal"),
-    (dict(variant=3), -1, "variant"),
+    (dict(variant=4), -1, "variant"),
+    (dict(variant=-1), -1, "variant"),
     (dict(sm=0.0), -1, "sm_scale"),
     (dict(sm=float("nan")), -1, "sm_scale"),
     (dict(sm=float("inf")), -1, "sm_scale"),
