@@ -35,15 +35,16 @@ FP4_PEAK_TOPS = 10100.0
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["quantized_bit_attention_amd/csrc/sage_attn.hip", "quantized_bit_attention_amd/csrc/sage_device.h",
                   "quantized_bit_attention_amd/csrc/sage_tiles.h"]
-VARIANT_TAG = {0: "_int8qk_fp16pv", 1: "_int8qk_fp8pv", 2: "_mxfp4qk_fp8pv"}
+VARIANT_TAG = {0: "_int8qk_fp16pv", 1: "_int8qk_fp8pv", 2: "_mxfp4qk_fp8pv", 3: "_mxfp4qk_fp4pv"}
 
 
 def mfma_ceiling_tops(variant: int) -> float:
     """The attention kernel's matrix-unit ceiling for its own operand types: half of the
-    counted operations are Q K^T (INT8, or FP4 in variant 2), half P~ V (FP16 in variant 0,
-    FP8 otherwise), so the ceiling is the harmonic combination of the two peaks."""
-    qk = FP4_PEAK_TOPS if variant == 2 else INT8_PEAK_TOPS
-    pv = FP16_PEAK_TOPS if variant == 0 else FP8_PEAK_TOPS
+    counted operations are Q K^T (INT8, or FP4 in variants 2 and 3), half P~ V (FP16 in
+    variant 0, FP4 in variant 3, FP8 otherwise), so the ceiling is the harmonic combination
+    of the two peaks."""
+    qk = FP4_PEAK_TOPS if variant >= 2 else INT8_PEAK_TOPS
+    pv = FP16_PEAK_TOPS if variant == 0 else FP4_PEAK_TOPS if variant == 3 else FP8_PEAK_TOPS
     return 1.0 / (0.5 / qk + 0.5 / pv)
 
 
@@ -92,11 +93,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = the headline workload)")
-    ap.add_argument("--variant", type=int, choices=(0, 1, 2), default=None,
-                    help="0: INT8 QK + FP16 P~V, 1: INT8 QK + Q smoothing + FP8 P~V, 2: MXFP4 QK + FP8 P~V "
-                         "(default: the workload's)")
+    ap.add_argument("--variant", type=int, choices=(0, 1, 2, 3), default=None,
+                    help="0: INT8 QK + FP16 P~V, 1: INT8 QK + Q smoothing + FP8 P~V, 2: MXFP4 QK + FP8 P~V, "
+                         "3: MXFP4 QK + MXFP4 P~V (default: the workload's)")
     ap.add_argument("--smooth-v", action="store_true",
-                    help="variants 1 and 2 (FP8 P~V): subtract V's token mean before FP8 and add it back")
+                    help="variants 1-3: subtract V's token mean before FP8 / MXFP4 and add it back")
     ap.add_argument("--q-group", type=int, default=0,
                     help="rows per Q scale (0: one per Q block; 1: per token)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -128,7 +129,8 @@ def main():
     variant = cfg["variant"] if args.variant is None else args.variant
     smooth_v = bool(args.smooth_v)
     if smooth_v and variant == 0:
-        print("bench.py: --smooth-v needs an FP8 P~V variant (--variant 1 or 2, or --config 5)", file=sys.stderr)
+        print("bench.py: --smooth-v needs an FP8 / FP4 P~V variant (--variant 1, 2 or 3, or --config 5)",
+              file=sys.stderr)
         sys.exit(2)
     q_group = args.q_group
     opts = dict(causal=bool(causal), variant=variant, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_v=smooth_v,
@@ -157,12 +159,16 @@ def main():
     # the attention kernel alone, as the step launches it (same stream, same launch
     # configuration): variants 0 and 2 quantise Q inside the kernel, variant 1 reads the
     # pre-quantised Q; variants 1 and 2 read the FP8 V
-    if variant == 2:
+    if variant >= 2:
         qk = sage.quant_qk_mx(q, k)
     else:
         qk = sage.quant_qk(q, k, blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=variant == 1, q_group=q_group)
-    vq = sage.quant_v(v, smooth_v=smooth_v) if variant != 0 else None
-    if variant == 2:
+    vq = (sage.quant_v_mx(v, smooth_v=smooth_v) if variant == 3 else
+          sage.quant_v(v, smooth_v=smooth_v) if variant != 0 else None)
+    if variant == 3:
+        def kernel():
+            sage.attn_qf16_fp4(q, qk, vq, causal=bool(causal), smooth_v=smooth_v, out=out)
+    elif variant == 2:
         def kernel():
             sage.attn_qf16_mx(q, qk, vq, causal=bool(causal), smooth_v=smooth_v, out=out)
     elif variant == 0:
@@ -207,7 +213,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int8+fp16", "int8+fp8", "mxfp4+fp8")[variant],
+        "dtype": ("int8+fp16", "int8+fp8", "mxfp4+fp8", "mxfp4")[variant],
         "data": "synthetic (seeded SplitMix64/Box-Muller; K with per-channel offsets)",
         "config": {"workload": f"{cfg['name']} B={B} H={H} N={N} d={d}", "B": B, "H": H, "N": N, "d": d,
                    "causal": causal, "variant": variant, "blk_q": cfg["blk_q"], "blk_k": cfg["blk_k"],
@@ -216,7 +222,8 @@ def main():
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_tops": round(attn_tops, 2),
         # the attention kernel against the matrix-unit ceiling of its own operand types
-        # (variant 0: INT8 + FP16 = 3333 TOPS; 1: INT8 + FP8 = 5000; 2: FP4 + FP8 = 6689)
+        # (variant 0: INT8 + FP16 = 3333 TOPS; 1: INT8 + FP8 = 5000; 2: FP4 + FP8 = 6689;
+        # 3: FP4 + FP4 = 10100)
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": round(ceiling, 1),
                      "unit": "TOPS", "frac": round(attn_tops / ceiling, 4),
                      "frac_of_int8_peak": round(attn_tops / INT8_PEAK_TOPS, 4),
