@@ -157,8 +157,8 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
 
     # the attention kernel alone, as the step launches it (same stream, same launch
-    # configuration): variants 0 and 2 quantise Q inside the kernel, variant 1 reads the
-    # pre-quantised Q; variants 1 and 2 read the FP8 V
+    # configuration): every variant quantises Q inside the kernel; variants 1-3 read the
+    # quantised V
     if variant >= 2:
         qk = sage.quant_qk_mx(q, k)
     else:
@@ -177,7 +177,8 @@ def main():
                            q_group=q_group)
     else:
         def kernel():
-            sage.attn_prequant(qk, v, N, vq=vq, out=out, **opts)
+            sage.attn_qf16_fp8(q, qk, vq, causal=bool(causal), blk_q=cfg["blk_q"], blk_k=cfg["blk_k"], smooth_q=True,
+                               smooth_v=smooth_v, q_group=q_group, out=out)
     for _ in range(3):
         kernel()
     torch.cuda.synchronize()

@@ -146,9 +146,9 @@ int sage_quant_v_ex(const void* v, int B, int H, int N, int d, int smooth_v, uin
 
 /*
  * o = SageAttention(q, k, v): the whole plug-and-play forward (quantisation kernels
- * plus the attention kernel; for variant 0 without Q smoothing, and for variant 2,
- * the attention kernel quantises Q itself, see sage_attn_fwd_qf16 and
- * sage_attn_fwd_qf16_mx).  causal: key j is visible to query i iff j <= i.
+ * plus the attention kernel; the attention kernel quantises Q itself, see
+ * sage_attn_fwd_qf16, sage_attn_fwd_qf16_fp8, sage_attn_fwd_qf16_mx and
+ * sage_attn_fwd_qf16_fp4).  causal: key j is visible to query i iff j <= i.
  * sm_scale: softmax scale (finite, > 0; normally 1/sqrt(d)), applied when the int32
  * scores are dequantised.  variant: SAGE_VARIANT_*.  ws: device workspace of at
  * least sage_workspace_bytes(...) bytes.
@@ -194,6 +194,18 @@ int sage_attn_fwd_prequant(const int8_t* q_i8, const int8_t* k_i8, const float* 
                            const sage_params* p, void* stream);
 
 /*
+ * The attention kernel that sage_attn_fwd runs for variant 1: Q is fp16 and each
+ * workgroup quantises its own rows in its prologue with the rule of sage_quant_qk (same
+ * codes and scales; with p->smooth_q (the default for this variant) the exact mean of each
+ * Q block of blk_q rows is taken out first and its term added back to the scores); K
+ * comes from sage_quant_qk (same p), V from sage_quant_v(_ex) (same smooth_v).  Used to
+ * time the fused kernel by itself.
+ */
+int sage_attn_fwd_qf16_fp8(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_f8,
+                           const float* v_scale, const float* v_mean, void* o, int B, int H, int N, int d,
+                           int causal, float sm_scale, const sage_params* p, void* stream);
+
+/*
  * Per-token MXFP4 of Q and K for the MXFP4 variant (SageAttention3 abstract: FP4
  * attention; the block format is read as OCP Microscaling MXFP4):
  *   K' = K - k_mean with smooth_k (the sage_quant_qk rule for k_mean), Q unsmoothed;
@@ -231,11 +243,11 @@ int sage_attn_fwd_qf16_mx(const void* q, const uint8_t* k_f4, const uint8_t* k_e
                           int causal, float sm_scale, const sage_params* p, void* stream);
 
 /*
- * The attention kernel that sage_attn_fwd runs for variant 0 without Q smoothing: Q
- * is fp16 and each workgroup quantises its own rows per group of q_group rows
- * (default blk_q; the sage_quant_qk rule above, same codes and scales); K comes pre-quantised from
- * sage_quant_qk (k_i8, k_scale, same p); v is fp16.  Variant 0 only: p->smooth_q = 1
- * returns SAGE_ERR_UNSUPPORTED.  Used to time the fused kernel by itself, and for
+ * The attention kernel that sage_attn_fwd runs for variant 0: Q is fp16 and each
+ * workgroup quantises its own rows per group of q_group rows (default blk_q; the
+ * sage_quant_qk rule above, same codes and scales, with p->smooth_q the block means
+ * taken out first and their term added back); K comes pre-quantised from sage_quant_qk
+ * (k_i8, k_scale, same p); v is fp16.  Used to time the fused kernel by itself, and for
  * callers that keep K quantised across calls.
  */
 int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, const void* v,

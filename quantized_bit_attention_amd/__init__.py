@@ -19,6 +19,7 @@ import os
 import torch
 
 __all__ = ["attn", "attn_noalloc", "attn_fwd_train", "attn_bwd", "quant_qk", "quant_v", "attn_prequant", "attn_qf16",
+           "attn_qf16_fp8",
            "quant_qk_mx", "attn_prequant_mx", "attn_qf16_mx", "quant_v_mx", "attn_qf16_fp4",
            "debug_qk_int32", "workspace_bytes",
            "kv_tile", "pad_len", "SageError", "library_path", "VARIANT_FP16PV", "VARIANT_FP8PV", "VARIANT_MXFP4",
@@ -70,6 +71,7 @@ def _load():
         "sage_attn_fwd_ex": ([P, P, P, P, I, I, I, I, I, F, I, PP, P, S, P], I),
         "sage_attn_fwd_prequant": ([P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, PP, P], I),
         "sage_attn_fwd_qf16": ([P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
+        "sage_attn_fwd_qf16_fp8": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_quant_qk_mx": ([P, P, I, I, I, I, I, P, P, P, P, P, P, S, P], I),
         "sage_attn_fwd_prequant_mx": ([P, P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
         "sage_attn_fwd_qf16_mx": ([P, P, P, P, P, P, P, I, I, I, I, I, F, PP, P], I),
@@ -373,8 +375,10 @@ def attn_prequant(qk: dict, v, N, causal=False, sm_scale=None, variant=VARIANT_F
     return out
 
 
-def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, q_group=0, out=None):
-    """Variant 0 attention on fp16 q (quantised inside the kernel) and the K of quant_qk()."""
+def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, q_group=0, smooth_q=False,
+              out=None):
+    """Variant 0 attention on fp16 q (quantised inside the kernel, with Q smoothing if asked) and
+    the K of quant_qk()."""
     B, H, N, d = _check_qkv(q, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
@@ -382,10 +386,34 @@ def attn_qf16(q, qk: dict, v, causal=False, sm_scale=None, blk_q=128, blk_k=64, 
     _check_tensor(qk["k_i8"], "k_i8", (B, H, Np, d), torch.int8, q.device)
     _check_tensor(qk["k_scale"], "k_scale", (B, H, -(-N // blk_k)), torch.float32, q.device)
     out = _check_out(out, q.shape, q.device)
-    p = _params(blk_q, blk_k, True, False, False, q_group)
+    p = _params(blk_q, blk_k, True, smooth_q, False, q_group)
     rc = _load().sage_attn_fwd_qf16(_ptr(q), _ptr(qk["k_i8"]), _ptr(qk["k_scale"]), _ptr(v), _ptr(out), B, H, N, d,
                                     int(bool(causal)), float(sm_scale), ctypes.byref(p), _stream(q.device))
     _check(rc, "sage_attn_fwd_qf16")
+    return out
+
+
+def attn_qf16_fp8(q, qk: dict, vq: dict, causal=False, sm_scale=None, blk_q=128, blk_k=64, smooth_q=True,
+                  smooth_v=False, q_group=0, out=None):
+    """Variant 1 attention on fp16 q (quantised, with Q smoothing by default, inside the kernel),
+    the K of quant_qk() and the V of quant_v()."""
+    B, H, N, d = _check_qkv(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    Np = pad_len(N)
+    _check_tensor(qk["k_i8"], "k_i8", (B, H, Np, d), torch.int8, q.device)
+    _check_tensor(qk["k_scale"], "k_scale", (B, H, -(-N // blk_k)), torch.float32, q.device)
+    _check_tensor(vq["v_f8"], "v_f8", (B, H, d, Np), torch.uint8, q.device)
+    _check_tensor(vq["v_scale"], "v_scale", (B, H, d), torch.float32, q.device)
+    if smooth_v:
+        _check_tensor(vq["v_mean"], "v_mean", (B, H, d), torch.float32, q.device)
+    out = _check_out(out, q.shape, q.device)
+    p = _params(blk_q, blk_k, True, smooth_q, smooth_v, q_group)
+    rc = _load().sage_attn_fwd_qf16_fp8(
+        _ptr(q), _ptr(qk["k_i8"]), _ptr(qk["k_scale"]), _ptr(vq["v_f8"]), _ptr(vq["v_scale"]),
+        _ptr(vq["v_mean"]) if smooth_v else None, _ptr(out), B, H, N, d, int(bool(causal)), float(sm_scale),
+        ctypes.byref(p), _stream(q.device))
+    _check(rc, "sage_attn_fwd_qf16_fp8")
     return out
 
 

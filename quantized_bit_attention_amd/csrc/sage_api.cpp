@@ -95,8 +95,13 @@ int check_ptr(const void* p, size_t align, const char* name) {
   return SAGE_OK;
 }
 
-// Variant 0 without Q smoothing, and variants 2 and 3, quantise Q inside the attention kernel.
-bool fuse_q(int variant, const Params& p) { return (variant == 0 && !p.smooth_q) || variant >= 2; }
+// The whole call quantises Q inside the attention kernel for every variant (INT8 with or
+// without Q smoothing, MXFP4); the pre-quantised entry points read the quantisation pass's Q.
+bool fuse_q(int variant, const Params& p) {
+  (void)variant;
+  (void)p;
+  return true;
+}
 
 bool valid_variant(int variant) { return variant >= 0 && variant <= 3; }
 
@@ -127,7 +132,7 @@ Layout layout(int B, int H, int N, int d, int variant, const Params& p) {
   L.q_scale = take(fq || mx ? 0 : G * nqg * sizeof(float));
   L.k_scale = take(mx ? 0 : G * nkb * sizeof(float));
   L.k_mean = take(G * d * sizeof(float));
-  L.q_mean = take(p.smooth_q ? G * nqb * d * sizeof(float) : 0);
+  L.q_mean = take(p.smooth_q && !fq ? G * nqb * d * sizeof(float) : 0);
   L.v_f8 = take(fp8v ? G * d * (v4 ? Np / 2 : Np) : 0);
   L.v_scale = take(fp8v && !v4 ? G * d * sizeof(float) : 0);
   L.v_mean = take(p.smooth_v ? G * d * sizeof(float) : 0);
@@ -245,7 +250,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
     sage::QuantArgs qa = quant_args(q, k, B, H, N, d, p, fq ? nullptr : at<int8_t>(ws, L.q_i8),
                                     at<int8_t>(ws, L.k_i8), fq ? nullptr : at<float>(ws, L.q_scale),
                                     at<float>(ws, L.k_scale), at<float>(ws, L.k_mean),
-                                    p.smooth_q ? at<float>(ws, L.q_mean) : nullptr, at<long long>(ws, L.ksum));
+                                    p.smooth_q && !fq ? at<float>(ws, L.q_mean) : nullptr, at<long long>(ws, L.ksum));
     qa.with_q = fq ? 0 : 1;
     e = sage::launch_quant(d, qa, st);
     if (e != hipSuccess) return hip_fail(e, "quantisation kernel");
@@ -265,7 +270,7 @@ int attn_common(const void* q, const void* k, const void* v, void* o, int B, int
   a.k_i8 = at<int8_t>(ws, L.k_i8);
   a.q_scale = fq || variant >= 2 ? nullptr : at<float>(ws, L.q_scale);
   a.k_scale = variant >= 2 ? nullptr : at<float>(ws, L.k_scale);
-  a.q_mean = p.smooth_q ? at<float>(ws, L.q_mean) : nullptr;
+  a.q_mean = p.smooth_q && !fq ? at<float>(ws, L.q_mean) : nullptr;
   a.q_e8 = nullptr;  // variants 2 and 3 quantise Q in the kernel
   a.k_e8 = variant >= 2 ? at<uint8_t>(ws, L.k_e8) : nullptr;
   a.v = (const uint16_t*)v;
@@ -587,7 +592,6 @@ int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, 
     return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   Params p;
   if ((rc = read_params(pp, 0, &p))) return rc;
-  if (p.smooth_q) return fail(SAGE_ERR_UNSUPPORTED, "sage_attn_fwd_qf16 quantises Q without smoothing (smooth_q must be 0)");
   if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k_i8, 16, "k_i8")) || (rc = check_ptr(k_scale, 4, "k_scale")) ||
       (rc = check_ptr(v, 16, "v")) || (rc = check_ptr(o, 16, "o")))
     return rc;
@@ -597,7 +601,34 @@ int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, 
   a.k_scale = k_scale;
   a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o;
-  hipError_t e = sage::launch_attn(d, 0, causal, 0, a, (hipStream_t)stream);
+  hipError_t e = sage::launch_attn(d, 0, causal, p.smooth_q, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+int sage_attn_fwd_qf16_fp8(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_f8,
+                           const float* v_scale, const float* v_mean, void* o, int B, int H, int N, int d, int causal,
+                           float sm_scale, const sage_params* pp, void* stream) {
+  int rc;
+  if ((rc = check_shape(B, H, N, d))) return rc;
+  if (causal != 0 && causal != 1) return fail(SAGE_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(SAGE_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  Params p;
+  if ((rc = read_params(pp, SAGE_VARIANT_INT8QK_FP8PV, &p))) return rc;
+  if ((rc = check_ptr(q, 16, "q")) || (rc = check_ptr(k_i8, 16, "k_i8")) || (rc = check_ptr(k_scale, 4, "k_scale")) ||
+      (rc = check_ptr(v_f8, 16, "v_f8")) || (rc = check_ptr(v_scale, 16, "v_scale")) || (rc = check_ptr(o, 16, "o")))
+    return rc;
+  if (p.smooth_v && (rc = check_ptr(v_mean, 16, "v_mean (required with smooth_v)"))) return rc;
+  sage::AttnArgs a = attn_args(B, H, N, p, sm_scale);
+  a.q = (const uint16_t*)q;
+  a.k_i8 = k_i8;
+  a.k_scale = k_scale;
+  a.v_f8 = v_f8;
+  a.v_scale = v_scale;
+  a.v_mean = p.smooth_v ? v_mean : nullptr;
+  a.o = (uint16_t*)o;
+  hipError_t e = sage::launch_attn(d, 1, causal, p.smooth_q, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
 }

@@ -356,14 +356,14 @@ __device__ __forceinline__ void interleave_schedule() {
   }
 }
 
-// FUSEQ (variant 0 without Q smoothing, and variant 2): Q arrives as fp16 and each
-// workgroup quantises its own rows into the LDS operand tile, with the rule of the
-// quantisation pass: INT8 per group of q_group = 1 .. 128 rows (the workgroup's 128
-// rows are whole groups), or MXFP4 per 32-channel block (one lane's operand per block).
+// FUSEQ: Q arrives as fp16 and each workgroup quantises its own rows into the LDS
+// operand tile, with the rule of the quantisation pass: INT8 per group of q_group =
+// 1 .. 128 rows (the workgroup's 128 rows are whole groups; with Q smoothing the exact
+// mean of each Q block of blk_q rows is taken out first), or MXFP4 per 32-channel block
+// (one lane's operand per block).
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
-  static_assert(!FUSEQ || ((VARIANT == 0 || VARIANT >= 2) && !SMOOTHQ),
-                "in-kernel Q quantisation: variants 0, 2 and 3, no Q smoothing");
+  static_assert(!FUSEQ || VARIANT <= 1 || !SMOOTHQ, "in-kernel Q quantisation with Q smoothing: INT8 Q only");
   static_assert(VARIANT < 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
   constexpr int KD = qk_row_bytes<D, VARIANT>();  // bytes per Q / K row
@@ -382,6 +382,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sBias0[SMOOTHQ ? NSUB * kTileKV : 1];
   __shared__ __attribute__((aligned(16))) float sBias1[SMOOTHQ ? NSUB * kTileKV : 1];
   __shared__ float sAmax[kAttnWaves];  // FUSEQ: |Q| max of each wave's rows
+  __shared__ float sQmean[FUSEQ && SMOOTHQ ? NSUB * D : 1];    // FUSEQ with Q smoothing: the block means
+  __shared__ double sQsum[FUSEQ && SMOOTHQ ? kAttnWaves * D : 1];  //  and each wave's column sums
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, ql = lane & 31;
@@ -442,14 +444,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     if (wave_active) qsw = mx_lane_scales<D>(a.q_e8 + ((size_t)g * a.Np + qi) * (D / 32), h);
   }
 
-  if constexpr (SMOOTHQ) {
-    // wave sb splits the mean of the workgroup's Q block sb (up to 4 blocks; the others
-    // get zero limbs)
-    static_assert(NSUB == kAttnWaves, "one wave per Q block of the workgroup");
-    const int sb = wave, qb = (q0 >> qshift) + sb;
-    split_qmean<D>(a.q_mean + ((size_t)g * a.nqb + qb) * D, sb * a.blk_q < kAttnRows && qb < a.nqb, sQl, sQs, sb);
-  }
-
   f32x16 o[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) o[ct] = f32x16{};
@@ -476,19 +470,98 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // it; clear that slot (0 times a stale NaN pattern would not be 0)
   for (int e = tid; e < L::V_BYTES / 16; e += kAttnThreads)
     reinterpret_cast<uint4*>(sV1)[e] = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (FUSEQ && VARIANT == 0) {
-    // |Q| max: with the sign bits cleared, fp16 bit patterns order like the values, so a
-    // packed 16-bit integer max finds it exactly
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    u16x2 mx = {0, 0};
+  if constexpr (FUSEQ && SMOOTHQ) {
+    // The exact means of the workgroup's Q blocks, by the quantisation pass's rule: the
+    // sum of the fp16 values is exact in fp64 (they are multiples of 2^-24 below 2^16, so
+    // a sum of up to 128 needs 47 bits), and sum / count rounds once to fp64, then to
+    // fp32.  Each wave sums its 32 rows: it stages half of its channels at a time in its
+    // own part of the Q operand tile (written with codes only later) and lane l adds
+    // channel l of the half down the rows.
+    uint16_t* const stage = reinterpret_cast<uint16_t*>(sQw);  // 32 rows x D/2 fp16
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // lane (ql, h) holds channels 32*(i/2) + 16h + 8*(i%2) .. +7 in qraw[i]: this half
+      // covers channels [half*D/2, half*D/2 + D/2)
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        const int c0 = 32 * (i >> 1) + 16 * h + 8 * (i & 1);
+        if (c0 / (D / 2) == half)
+          *reinterpret_cast<uint4*>(stage + ql * (D / 2) + c0 - half * (D / 2)) = qraw[i];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      if (lane < D / 2) {
+        double sum = 0.0;
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) sum += (double)(float)__builtin_bit_cast(_Float16, stage[r * (D / 2) + lane]);
+        sQsum[wave * D + half * (D / 2) + lane] = sum;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    if (tid < D) {
+      for (int sb = 0; sb < (kAttnRows >> qshift); ++sb) {
+        const int r0 = sb << qshift, r1 = min(r0 + a.blk_q, N - q0);
+        double sum = 0.0;
+        for (int w = r0 >> 5; w < (r0 + a.blk_q) >> 5; ++w) sum += sQsum[w * D + tid];
+        sQmean[sb * D + tid] = r1 > r0 ? (float)(sum / (double)(r1 - r0)) : 0.0f;
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (SMOOTHQ) {
+    // wave sb splits the mean of the workgroup's Q block sb (up to 4 blocks; the others
+    // get zero limbs)
+    static_assert(NSUB == kAttnWaves, "one wave per Q block of the workgroup");
+    const int sb = wave, qb = (q0 >> qshift) + sb;
+    const float* qm = FUSEQ ? sQmean + sb * D : a.q_mean + ((size_t)g * a.nqb + qb) * D;
+    split_qmean<D>(qm, sb * a.blk_q < kAttnRows && qb < a.nqb, sQl, sQs, sb);
+  }
+
+  // FUSEQ with Q smoothing: the smoothed fp32 values of this lane's fp16 Q, xs[8i + j] =
+  // channel 32*(i/2) + 16h + 8*(i%2) + j minus its block mean; rows >= N are zero, as in
+  // the quantisation pass
+  float xs[FUSEQ && SMOOTHQ ? D / 2 : 1];
+  if constexpr (FUSEQ && SMOOTHQ) {
+    const bool row_ok = wave_active && qi < N;
+    const float* mrow = sQmean + ((32 * wave + ql) >> qshift) * D;
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
+      const int c0 = 32 * (i >> 1) + 16 * h + 8 * (i & 1);
+      const float4 m0 = *reinterpret_cast<const float4*>(mrow + c0);
+      const float4 m1 = *reinterpret_cast<const float4*>(mrow + c0 + 4);
+      const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
       const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
+      for (int u = 0; u < 4; ++u) {
+        const f16x2 hv = __builtin_bit_cast(f16x2, w[u]);
+        xs[8 * i + 2 * u] = row_ok ? (float)hv[0] - mv[2 * u] : 0.0f;
+        xs[8 * i + 2 * u + 1] = row_ok ? (float)hv[1] - mv[2 * u + 1] : 0.0f;
+      }
     }
-    const u16x2 mb = {__builtin_elementwise_max(mx[0], mx[1]), 0};
-    const float lm = (float)__builtin_bit_cast(f16x2, mb)[0];  // this lane's half of row qi
+  }
+  if constexpr (FUSEQ && VARIANT <= 1) {
+    float lm;  // this lane's half of row qi: its |Q| max
+    if constexpr (SMOOTHQ) {
+      lm = 0.0f;
+#pragma unroll
+      for (int j = 0; j < D / 2; ++j) lm = fmaxf(lm, fabsf(xs[j]));
+    } else {
+      // with the sign bits cleared, fp16 bit patterns order like the values, so a packed
+      // 16-bit integer max finds the |Q| max exactly
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      u16x2 mx = {0, 0};
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
+      }
+      const u16x2 mb = {__builtin_elementwise_max(mx[0], mx[1]), 0};
+      lm = (float)__builtin_bit_cast(f16x2, mb)[0];
+    }
     const float am = wave_max(lm);
     if (lane == 0) sAmax[wave] = am;
     if (a.q_group < 32) {
@@ -521,7 +594,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint4*>(sQw + ks * 1024 + 16 * lane) = packed;
     }
   }
-  if constexpr (FUSEQ && VARIANT == 0) {
+  if constexpr (FUSEQ && VARIANT <= 1) {
     // a group of 32 rows or more spans waves w0 .. w0 + q_group/32 - 1
     float amax = dq;
     if (a.q_group >= 32) {
@@ -536,11 +609,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       uint32_t pk4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint4 src = qraw[2 * ks + u / 2];
+        const int i = 2 * ks + u / 2, j0 = 2 * (u & 1);  // qraw[i], words j0 and j0 + 1
+        const uint4 src = qraw[i];
         const uint32_t w0v = (u & 1) ? src.z : src.x, w1v = (u & 1) ? src.w : src.y;
         const f16x2 h0 = __builtin_bit_cast(f16x2, w0v), h1 = __builtin_bit_cast(f16x2, w1v);
-        pk4[u] = pack_bytes4(i8_code_int((float)h0[0], r), i8_code_int((float)h0[1], r),
-                             i8_code_int((float)h1[0], r), i8_code_int((float)h1[1], r));
+        float x[4] = {(float)h0[0], (float)h0[1], (float)h1[0], (float)h1[1]};
+        if constexpr (SMOOTHQ) {
+          x[0] = xs[8 * i + 2 * j0];
+          x[1] = xs[8 * i + 2 * j0 + 1];
+          x[2] = xs[8 * i + 2 * j0 + 2];
+          x[3] = xs[8 * i + 2 * j0 + 3];
+        }
+        pk4[u] = pack_bytes4(i8_code_int(x[0], r), i8_code_int(x[1], r), i8_code_int(x[2], r), i8_code_int(x[3], r));
       }
       *reinterpret_cast<uint4*>(sQw + ks * 1024 + 16 * lane) = make_uint4(pk4[0], pk4[1], pk4[2], pk4[3]);
     }
@@ -837,8 +917,21 @@ static hipError_t launch_dv(int causal, int smooth_q, const AttnArgs& a, hipStre
 }
 
 hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnArgs& a, hipStream_t st) {
-  if (a.q) {  // fp16 Q, quantised in the kernel (variant 0 without Q smoothing, variants 2 and 3)
-    if (variant == 1 || smooth_q) return hipErrorInvalidValue;
+  if (a.q) {  // fp16 Q, quantised in the kernel (variants 0 and 1 with or without Q smoothing, 2, 3)
+    if (variant <= 1) {
+      auto one = [&](auto dc, auto vc) -> hipError_t {
+        constexpr int DD = decltype(dc)::value, VV = decltype(vc)::value;
+        if (causal)
+          return smooth_q ? launch_one<DD, VV, true, true, true>(a, st) : launch_one<DD, VV, true, false, true>(a, st);
+        return smooth_q ? launch_one<DD, VV, false, true, true>(a, st) : launch_one<DD, VV, false, false, true>(a, st);
+      };
+      if (d == 64)
+        return variant == 0 ? one(std::integral_constant<int, 64>{}, std::integral_constant<int, 0>{})
+                            : one(std::integral_constant<int, 64>{}, std::integral_constant<int, 1>{});
+      return variant == 0 ? one(std::integral_constant<int, 128>{}, std::integral_constant<int, 0>{})
+                          : one(std::integral_constant<int, 128>{}, std::integral_constant<int, 1>{});
+    }
+    if (smooth_q) return hipErrorInvalidValue;
     if (variant == 3) {
       if (d == 64) return causal ? launch_one<64, 3, true, false, true>(a, st) : launch_one<64, 3, false, false, true>(a, st);
       return causal ? launch_one<128, 3, true, false, true>(a, st) : launch_one<128, 3, false, false, true>(a, st);
@@ -847,8 +940,7 @@ hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnA
       if (d == 64) return causal ? launch_one<64, 2, true, false, true>(a, st) : launch_one<64, 2, false, false, true>(a, st);
       return causal ? launch_one<128, 2, true, false, true>(a, st) : launch_one<128, 2, false, false, true>(a, st);
     }
-    if (d == 64) return causal ? launch_one<64, 0, true, false, true>(a, st) : launch_one<64, 0, false, false, true>(a, st);
-    return causal ? launch_one<128, 0, true, false, true>(a, st) : launch_one<128, 0, false, false, true>(a, st);
+    return hipErrorInvalidValue;
   }
   if (variant == 3) return hipErrorInvalidValue;  // variant 3 always quantises Q in the kernel
   if (variant == 2) {  // MXFP4 scores, never with Q smoothing

@@ -658,6 +658,50 @@ def test_fused_q_quantisation_matches_quant_pass(sage, cfg, shape, blk_q, blk_k,
     assert torch.equal(whole, pre)
 
 
+FUSED_SMOOTH = [
+    # variant, recipe cfg, shape overrides, blk_q, blk_k, causal, q_group, smooth_v
+    (1, 5, dict(N=333, B=1, H=2), 128, 64, 1, 0, 0),
+    (1, 5, dict(N=1000, B=1, H=2), 64, 32, 0, 0, 1),
+    (1, 1, dict(N=200, B=1, H=2), 32, 64, 1, 0, 0),
+    (1, 3, dict(N=300, B=1, H=2), 128, 16, 0, 1, 0),
+    (1, 2, dict(N=257, B=1, H=2), 64, 64, 1, 8, 1),
+    (1, 4, dict(N=129, B=2, H=1), 128, 64, 0, 32, 0),
+    (0, 2, dict(N=333, B=1, H=2), 128, 64, 1, 0, 0),
+    (0, 3, dict(N=200, B=1, H=2), 32, 32, 0, 4, 0),
+]
+
+
+@pytest.mark.parametrize("variant,cfg,shape,blk_q,blk_k,causal,q_group,smooth_v", FUSED_SMOOTH)
+def test_fused_smoothed_q_matches_quant_pass(sage, variant, cfg, shape, blk_q, blk_k, causal, q_group, smooth_v):
+    """With Q smoothing the attention kernel takes each Q block's exact mean and quantises the
+    smoothed rows itself: the whole call, the fused kernel alone and the quantisation pass +
+    pre-quantised kernel give the same bits.  One Q block is all zeros; one has an offset
+    larger than its spread."""
+    c = workloads.make_inputs(cfg, **shape)
+    q = c["q"].copy()
+    q[0, 0, :blk_q] = 0
+    q[0, -1, blk_q:2 * blk_q] += np.float16(6.0)
+    say(f"fused smoothed Q v{variant} {q.shape} blk_q={blk_q} blk_k={blk_k} causal={causal} q_group={q_group} "
+        f"smooth_v={smooth_v}")
+    qd, kd, vd = dev(q), dev(c["k"]), dev(c["v"])
+    N = q.shape[2]
+    kw = dict(causal=bool(causal), blk_q=blk_q, blk_k=blk_k, q_group=q_group, smooth_q=True)
+    qk = sage.quant_qk(qd, kd, blk_q=blk_q, blk_k=blk_k, smooth_q=True, q_group=q_group)
+    if variant == 1:
+        whole = sage.attn(qd, kd, vd, variant=1, smooth_v=bool(smooth_v), **kw)
+        vq = sage.quant_v(vd, smooth_v=bool(smooth_v))
+        fused = sage.attn_qf16_fp8(qd, qk, vq, smooth_v=bool(smooth_v), **kw)
+        pre = sage.attn_prequant(qk, vd, N, variant=1, vq=vq, smooth_v=bool(smooth_v), **kw)
+    else:
+        whole = sage.attn(qd, kd, vd, variant=0, **kw)
+        fused = sage.attn_qf16(qd, qk, vd, **kw)
+        pre = sage.attn_prequant(qk, vd, N, variant=0, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(whole.float()).all()
+    assert torch.equal(whole, fused)
+    assert torch.equal(whole, pre)
+
+
 @pytest.mark.parametrize("variant", [0, 1, 2])
 def test_attn_maximum_size_sampled_heads(sage, orc, variant):
     """B*H*pad_len(N)*d one tile short of 2^31 (131071 heads of N = 100, d = 128): offsets

@@ -63,17 +63,15 @@ def test_workspace_size(lib):
     up = lambda x: (x + 255) // 256 * 256
     expect = up(G * 16 * d * 8) + up(G * Np * d) + up(G * 64 * 4) + up(G * d * 4)
     assert sage.workspace_bytes(B, H, N, d, 0) == expect
-    # with Q smoothing the quantisation pass writes int8 Q, its scales and block means
-    assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) == (expect + up(G * Np * d) + up(G * 32 * 4)
-                                                                  + up(G * 32 * d * 4))
+    # with Q smoothing the attention kernel also takes the block means itself
+    assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) == expect
     v1 = sage.workspace_bytes(B, H, N, d, 1)
     assert v1 > expect   # V in FP8 + q means
     # V smoothing adds the [G, d] fp32 means; it has no meaning for the fp16 P~V variant
     assert sage.workspace_bytes(B, H, N, d, 1, smooth_v=True) == v1 + up(G * d * 4)
     assert sage.workspace_bytes(B, H, N, d, 0, smooth_v=True) == 0
-    # per-token Q scales: the quantisation pass writes one scale per row
-    assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True, q_group=1) == (
-        sage.workspace_bytes(B, H, N, d, 0, smooth_q=True) - up(G * 32 * 4) + up(G * N * 4))
+    # per-token Q scales: formed in the kernel as well
+    assert sage.workspace_bytes(B, H, N, d, 0, smooth_q=True, q_group=1) == expect
     assert sage.workspace_bytes(B, H, N, d, 0, q_group=3) == 0
     # MXFP4 variant: K and V statistics, packed E2M1 K (d/2 bytes per row), its E8M0 scales
     # (d/32 per row), k_mean, FP8 V and its scales; the attention kernel quantises Q itself
@@ -187,8 +185,20 @@ def test_other_entry_points_reject(lib):
     assert rc == -1 and b"v_mean" in lib.sage_last_error()
     rc = lib.sage_debug_qk_int32(A, A, 1, 1, 64, 64, A, 0, A, None)
     assert rc == -1 and b"n_tiles" in lib.sage_last_error()
-    # the fused-Q kernel quantises Q without smoothing only
-    rc = lib.sage_attn_fwd_qf16(A, A, A, A, A, 1, 1, 64, 64, 0, 0.125, ctypes.byref(sage._params(smooth_q=True)), None)
+    # the fused-Q kernels check their operands before any launch
+    rc = lib.sage_attn_fwd_qf16_fp8(A, A, A, None, A, None, A, 1, 1, 64, 64, 0, 0.125, None, None)
+    assert rc == -1 and b"v_f8 is NULL" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16_fp8(A, A, A, A, A, None, A, 1, 1, 64, 64, 0, 0.125,
+                                    ctypes.byref(sage._params(smooth_v=True)), None)
+    assert rc == -1 and b"v_mean" in lib.sage_last_error()
+    rc = lib.sage_quant_v_mx(A, 1, 1, 64, 64, 1, A, A, None, A, 1 << 20, None)
+    assert rc == -1 and b"v_mean" in lib.sage_last_error()
+    rc = lib.sage_quant_v_mx(A, 1, 1, 64, 64, 1, A, A, A, A, 16, None)
+    assert rc == -3 and b"too small" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16_fp4(A, A, A, A, None, None, A, 1, 1, 64, 64, 0, 0.125, None, None)
+    assert rc == -1 and b"v_e8 is NULL" in lib.sage_last_error()
+    rc = lib.sage_attn_fwd_qf16_fp4(A, A, A, A, A, None, A, 1, 1, 64, 64, 0, 0.125,
+                                    ctypes.byref(sage._params(smooth_q=True)), None)
     assert rc == -2 and b"smooth_q" in lib.sage_last_error()
     rc = lib.sage_attn_fwd_qf16(A, None, A, A, A, 1, 1, 64, 64, 0, 0.125, None, None)
     assert rc == -1 and b"k_i8 is NULL" in lib.sage_last_error()
