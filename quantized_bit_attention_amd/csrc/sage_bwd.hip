@@ -41,6 +41,7 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or query rows (dQ) per workgroup
 constexpr float kPScale = 256.0f;         // P enters the fp16 products as 2^8 P
+constexpr float kLog2PScale = 8.0f;
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -51,6 +52,14 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
   return x;
+}
+
+// Workgroup ids are dealt round-robin over the 8 XCDs, each with its own L2; renumber
+// them so each XCD walks a contiguous range of (head, block) pairs and the tiles of a
+// head stay in one L2 while its blocks run.
+__device__ __forceinline__ int xcd_block(int total) {
+  const int b = blockIdx.x;
+  return (total & 7) == 0 ? (b & 7) * (total >> 3) + (b >> 3) : b;
 }
 
 // sigma = 2^(14 - e), 2^e the first power of two above 2 max|dO_i| max|V'_j| (1 when the bound is 0),
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int nkb = a.Np / kBwdRows;
-  const int g = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int g = xcd_block(a.G * nkb) / nkb, kb = xcd_block(a.G * nkb) % nkb;
   const int k0 = kb * kBwdRows, kw = k0 + 32 * wave, key = kw + (lane & 31);
   const int N = a.N, Np = a.Np;
 
@@ -242,9 +251,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       vb_op[ks] = *reinterpret_cast<const i32x4*>(vr + 32 * ks);
     }
   }
-  // the key's K scale times sm_scale * log2(e), and its V' scale
+  // the key's K scale times sm_scale * log2(e), and its V' scale.  The loop forms
+  // 2^8 P = 2^(s c + 8 - L) and sigma dS = (2^8 P) x with x = sigma 2^-8 (dP - D), so the
+  // scales 2^8 and sigma 2^-8 (powers of two) ride on the per-row L and D and on this
+  // key's V' scale.
   const float ck = a.kscale * a.k_scale[(size_t)g * a.nkb + min(key, N - 1) / a.blk_k];
-  const float dvk = a.v_scale[(size_t)g * Np + key];
+  const float sig8 = sigma * (1.0f / kPScale);
+  const float dvs = a.v_scale[(size_t)g * Np + key] * sig8;
 
   f32x16 dv[NCT], dk[NCT];
 #pragma unroll
@@ -267,8 +280,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     copy.v_tile(gfrs, t, Np, sGf);
     if (tid < kTileKV) {
       const size_t r = (size_t)g * Np + t * kTileKV + tid;
-      sL[tid] = a.lse2[r];
-      sD[tid] = a.dvec[r];
+      sL[tid] = kLog2PScale - a.lse2[r];  // pad rows: L = +inf, so 2^8 P = 0
+      sD[tid] = a.dvec[r] * sig8;
       sGs[tid] = a.do_scale[r];
     }
     wait_copies();
@@ -276,41 +289,44 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int r0 = t * kTileKV;
     // this wave's keys are all beyond the tile's last row: nothing to add
     const bool active = !CAUSAL || r0 + kTileKV - 1 >= kw;
-    if (active) {
+    // causal: only a tile with a row before one of the wave's keys needs the mask
+    const bool diag = CAUSAL && r0 < kw + 31;
+    auto block = [&](int st) {
       const float c = a.q_scale[(size_t)g * a.nqb + min(r0, N - 1) / a.blk_q] * ck;
+      const i32x16 s = i8_block_regb<D>(sQ, st, kb_op, lane);
+      const i32x16 dp = i8_block_regb<D>(sG, st, vb_op, lane);
+      // rows 32*st + 16*h + i of the tile
+      const float4* pl = reinterpret_cast<const float4*>(sL + 32 * st + 16 * h);
+      const float4* pd = reinterpret_cast<const float4*>(sD + 32 * st + 16 * h);
+      const float4* pg = reinterpret_cast<const float4*>(sGs + 32 * st + 16 * h);
+      uint32_t pkp[8], pks[8];
+      // row r0 + 32 st + 16 h + i sees the key iff i >= thr
+      const int thr = diag ? key - (r0 + 32 * st + 16 * h) : -1;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const i32x16 s = i8_block_regb<D>(sQ, st, kb_op, lane);
-        const i32x16 dp = i8_block_regb<D>(sG, st, vb_op, lane);
-        // rows 32*st + 16*h + i of the tile
-        const float4* pl = reinterpret_cast<const float4*>(sL + 32 * st + 16 * h);
-        const float4* pd = reinterpret_cast<const float4*>(sD + 32 * st + 16 * h);
-        const float4* pg = reinterpret_cast<const float4*>(sGs + 32 * st + 16 * h);
-        uint32_t pkp[8], pks[8];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 L4 = pl[q4], D4 = pd[q4], G4 = pg[q4];
+        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+        const float Gr[4] = {G4.x, G4.y, G4.z, G4.w};
+        float p[4], ds[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 L4 = pl[q4], D4 = pd[q4], G4 = pg[q4];
-          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
-          const float Gr[4] = {G4.x, G4.y, G4.z, G4.w};
-          float p[4], ds[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int i = 4 * q4 + b;
-            const int row = r0 + 32 * st + 16 * h + i;
-            float pv = __builtin_amdgcn_exp2f(fmaf((float)s[i], c, -Lr[b]));
-            if (CAUSAL) pv = row >= key ? pv : 0.0f;
-            const float dpv = (float)dp[i] * (Gr[b] * dvk);
-            p[b] = pv;
-            ds[b] = pv * (dpv - Dr[b]);
-          }
-          pkp[2 * q4] = pack_f16x2(kPScale * p[0], kPScale * p[1]);
-          pkp[2 * q4 + 1] = pack_f16x2(kPScale * p[2], kPScale * p[3]);
-          pks[2 * q4] = pack_f16x2(sigma * ds[0], sigma * ds[1]);
-          pks[2 * q4 + 1] = pack_f16x2(sigma * ds[2], sigma * ds[3]);
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * q4 + b;
+          float pv = __builtin_amdgcn_exp2f(fmaf((float)s[i], c, Lr[b]));  // 2^8 P
+          if (CAUSAL) pv = i >= thr ? pv : 0.0f;
+          p[b] = pv;
+          ds[b] = pv * fmaf((float)dp[i], Gr[b] * dvs, -Dr[b]);          // sigma dS
         }
-        f16_block<D>(sGf + vb, pkp, st, dv);
-        f16_block<D>(sQf + vb, pks, st, dk);
+        pkp[2 * q4] = pack_f16x2(p[0], p[1]);
+        pkp[2 * q4 + 1] = pack_f16x2(p[2], p[3]);
+        pks[2 * q4] = pack_f16x2(ds[0], ds[1]);
+        pks[2 * q4 + 1] = pack_f16x2(ds[2], ds[3]);
       }
+      f16_block<D>(sGf + vb, pkp, st, dv);
+      f16_block<D>(sQf + vb, pks, st, dk);
+    };
+    if (active) {
+      block(0);
+      block(1);
     }
     __syncthreads();
   }
@@ -346,7 +362,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
   const int nqt = a.Np / kBwdRows;
-  const int g = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  const int g = xcd_block(a.G * nqt) / nqt, qt = xcd_block(a.G * nqt) % nqt;
   const int q0 = qt * kBwdRows, qw = q0 + 32 * wave, qi = qw + ql;
   const int N = a.N, Np = a.Np;
 
@@ -358,7 +374,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   load_q_tile<D>(make_rsrc(a.q_i8 + (size_t)g * Np * D, (size_t)Np * D), qw, sQw);
   load_q_tile<D>(make_rsrc(a.do_i8 + (size_t)g * Np * D, (size_t)Np * D), qw, sGw);
   const size_t rq = (size_t)g * Np + qi;
-  const float l2 = a.lse2[rq], drow = a.dvec[rq], gsc = a.do_scale[rq];
+  // sigma dS = P x with x = sigma (dP - D): sigma (a power of two) rides on the row's D
+  // and dO scale
+  const float l2 = a.lse2[rq], drs = a.dvec[rq] * sigma, gss = a.do_scale[rq] * sigma;
   const float cq = a.kscale * a.q_scale[(size_t)g * a.nqb + min(qi, N - 1) / a.blk_q];
 
   f32x16 dq[NCT];
@@ -386,7 +404,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     tile_kscales(a.k_scale + (size_t)g * a.nkb, t, last_key, kshift, kq);
     wait_copies();
     __syncthreads();
-    if (qw < N && t <= wave_last) {
+    auto tile = [&](bool full) {
       i32x16 s[2], dp[2];
       qk_tile<D>(sK, sQw, lane, s);
       qk_tile<D>(sV, sGw, lane, dp);
@@ -395,6 +413,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int st = 0; st < 2; ++st) {
         const float c = cq * kscale_of(kq, st, h);
         const float4* pv4 = reinterpret_cast<const float4*>(sVs + 32 * st + 16 * h);
+        // key t*64 + 32 st + 16 h + i carries weight iff i <= thr: keys past N, and past
+        // the row when causal, carry none
+        const int thr = full ? 15 : (CAUSAL ? min(N - 1, qi) : N - 1) - (t * kTileKV + 32 * st + 16 * h);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const float4 V4 = pv4[q4];
@@ -403,18 +424,19 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int i = 4 * q4 + b;
-            const int kj = t * kTileKV + 32 * st + 16 * h + i;
             float pv = __builtin_amdgcn_exp2f(fmaf((float)s[st][i], c, -l2));
-            // keys past N, and past the row when causal, carry no weight
-            pv = (kj < N && (!CAUSAL || kj <= qi)) ? pv : 0.0f;
-            const float dpv = (float)dp[st][i] * (gsc * Vr[b]);
-            ds[b] = pv * (dpv - drow);
+            pv = i <= thr ? pv : 0.0f;
+            ds[b] = pv * fmaf((float)dp[st][i], gss * Vr[b], -drs);  // sigma dS
           }
-          pk[st * 8 + 2 * q4] = pack_f16x2(sigma * ds[0], sigma * ds[1]);
-          pk[st * 8 + 2 * q4 + 1] = pack_f16x2(sigma * ds[2], sigma * ds[3]);
+          pk[st * 8 + 2 * q4] = pack_f16x2(ds[0], ds[1]);
+          pk[st * 8 + 2 * q4 + 1] = pack_f16x2(ds[2], ds[3]);
         }
       }
       pv_tile_f16<D>(sKf + vb, pk, dq);
+    };
+    if (qw < N && t <= wave_last) {
+      // only the tail tile and, causal, tiles with a key after the wave's first row mask
+      tile((t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw));
     }
     __syncthreads();
   }
