@@ -349,15 +349,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 128 query rows of one head (wave w: rows 32w .. 32w+31), 64-key tiles.
+// The wave's Qhat and dOhat rows are the B operands, held in registers; the K, V' and K'
+// tiles go through two LDS slots, tile t+1 copied while tile t is worked on.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int NCT = D / 32;
-  __shared__ __attribute__((aligned(16))) int8_t sK[kTileKV * D];       // Khat tile (k_tile layout)
-  __shared__ __attribute__((aligned(16))) int8_t sV[kTileKV * D];       // V'hat tile (k_tile layout)
-  __shared__ __attribute__((aligned(16))) uint8_t sKf[kTileKV * D * 2];  // K' fp16 tile (v_tile layout)
-  __shared__ __attribute__((aligned(16))) int8_t sQo[kBwdRows * D];     // per wave: Qhat rows (B operand)
-  __shared__ __attribute__((aligned(16))) int8_t sGo[kBwdRows * D];     // per wave: dOhat rows (B operand)
-  __shared__ __attribute__((aligned(16))) float sVs[kTileKV];  // INT8 scales of the tile's V' rows
+  // two slots per tile kind, as separate LDS objects: the loop body is instantiated per
+  // slot parity, so the compiler can tell the slot being filled from the slot being read
+  __shared__ __attribute__((aligned(16))) int8_t sK0[kTileKV * D];       // Khat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sK1[kTileKV * D];
+  __shared__ __attribute__((aligned(16))) int8_t sV0[kTileKV * D];       // V'hat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sV1[kTileKV * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sKf0[kTileKV * D * 2];  // K' fp16 tile (v_tile layout)
+  __shared__ __attribute__((aligned(16))) uint8_t sKf1[kTileKV * D * 2];
+  __shared__ __attribute__((aligned(16))) float sVs0[kTileKV];  // INT8 scales of the tile's V' rows
+  __shared__ __attribute__((aligned(16))) float sVs1[kTileKV];
   __shared__ float sRed[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
@@ -368,11 +374,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const float sigma = bwd_sigma(a.nrm + (size_t)g * (Np / 64) * 2, Np / 64, sRed);
 
-  int8_t* const sQw = sQo + wave * D * 32;
-  int8_t* const sGw = sGo + wave * D * 32;
-  // qw < Np: every wave's 32 rows lie in the padded tensors
-  load_q_tile<D>(make_rsrc(a.q_i8 + (size_t)g * Np * D, (size_t)Np * D), qw, sQw);
-  load_q_tile<D>(make_rsrc(a.do_i8 + (size_t)g * Np * D, (size_t)Np * D), qw, sGw);
+  // B operands: bytes 32 ks + 16 h .. +15 of this lane's Qhat and dOhat row for k-step ks
+  // (qi < Np; pad rows are zero)
+  i32x4 qb[D / 32], gb[D / 32];
+  {
+    const int8_t* qr = a.q_i8 + ((size_t)g * Np + qi) * D + 16 * h;
+    const int8_t* gr = a.do_i8 + ((size_t)g * Np + qi) * D + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      qb[ks] = *reinterpret_cast<const i32x4*>(qr + 32 * ks);
+      gb[ks] = *reinterpret_cast<const i32x4*>(gr + 32 * ks);
+    }
+  }
   const size_t rq = (size_t)g * Np + qi;
   // sigma dS = P x with x = sigma (dP - D): sigma (a power of two) rides on the row's D
   // and dO scale
@@ -394,51 +407,84 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wave_last = CAUSAL ? min(ntiles - 1, min(qw + 31, N - 1) / kTileKV) : ntiles - 1;
   const unsigned last_key = (unsigned)(N - 1);
   const int kshift = __builtin_ctz(a.blk_k);
+  const float* const vsc = a.v_scale + (size_t)g * Np;  // Np >= 64 * ntiles
 
-  for (int t = 0; t < T; ++t) {
-    copy.k_tile(krs, t, sK);
-    copy.k_tile(vrs, t, sV);
-    copy.v_tile(kfrs, t, Np, sKf);
-    if (tid < kTileKV) sVs[tid] = a.v_scale[(size_t)g * Np + t * kTileKV + tid];
+  // S^T and dP^T of tile t (Khat, V'hat in sK, sV), dS packed as P~, dQ^T += K'^T dS^T
+  auto tile = [&](int t, const int8_t* sK, const int8_t* sV, const uint8_t* sKf, const float* sVs, bool full) {
     float kq[4];
     tile_kscales(a.k_scale + (size_t)g * a.nkb, t, last_key, kshift, kq);
-    wait_copies();
-    __syncthreads();
-    auto tile = [&](bool full) {
-      i32x16 s[2], dp[2];
-      qk_tile<D>(sK, sQw, lane, s);
-      qk_tile<D>(sV, sGw, lane, dp);
-      uint32_t pk[16];
+    constexpr int CPR = D / 16;
+    const int8_t* kbase = sK + 16 * lane;
+    const int8_t* vbase = sV + 16 * lane;
+    i32x16 s[2] = {i32x16{}, i32x16{}}, dp[2] = {i32x16{}, i32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const float c = cq * kscale_of(kq, st, h);
-        const float4* pv4 = reinterpret_cast<const float4*>(sVs + 32 * st + 16 * h);
-        // key t*64 + 32 st + 16 h + i carries weight iff i <= thr: keys past N, and past
-        // the row when causal, carry none
-        const int thr = full ? 15 : (CAUSAL ? min(N - 1, qi) : N - 1) - (t * kTileKV + 32 * st + 16 * h);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 V4 = pv4[q4];
-          const float Vr[4] = {V4.x, V4.y, V4.z, V4.w};
-          float ds[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int i = 4 * q4 + b;
-            float pv = __builtin_amdgcn_exp2f(fmaf((float)s[st][i], c, -l2));
-            pv = i <= thr ? pv : 0.0f;
-            ds[b] = pv * fmaf((float)dp[st][i], gss * Vr[b], -drs);  // sigma dS
-          }
-          pk[st * 8 + 2 * q4] = pack_f16x2(ds[0], ds[1]);
-          pk[st * 8 + 2 * q4 + 1] = pack_f16x2(ds[2], ds[3]);
-        }
+        s[st] = mfma_i8(*reinterpret_cast<const i32x4*>(kbase + (st * CPR + 2 * ks) * 512), qb[ks], s[st]);
+        dp[st] = mfma_i8(*reinterpret_cast<const i32x4*>(vbase + (st * CPR + 2 * ks) * 512), gb[ks], dp[st]);
       }
-      pv_tile_f16<D>(sKf + vb, pk, dq);
-    };
-    if (qw < N && t <= wave_last) {
-      // only the tail tile and, causal, tiles with a key after the wave's first row mask
-      tile((t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw));
+    uint32_t pk[16];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const float c = cq * kscale_of(kq, st, h);
+      const float4* pv4 = reinterpret_cast<const float4*>(sVs + 32 * st + 16 * h);
+      // key t*64 + 32 st + 16 h + i carries weight iff i <= thr: keys past N, and past
+      // the row when causal, carry none
+      const int thr = full ? 15 : (CAUSAL ? min(N - 1, qi) : N - 1) - (t * kTileKV + 32 * st + 16 * h);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 V4 = pv4[q4];
+        const float Vr[4] = {V4.x, V4.y, V4.z, V4.w};
+        float ds[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * q4 + b;
+          float pv = __builtin_amdgcn_exp2f(fmaf((float)s[st][i], c, -l2));
+          pv = i <= thr ? pv : 0.0f;
+          ds[b] = pv * fmaf((float)dp[st][i], gss * Vr[b], -drs);  // sigma dS
+        }
+        pk[st * 8 + 2 * q4] = pack_f16x2(ds[0], ds[1]);
+        pk[st * 8 + 2 * q4 + 1] = pack_f16x2(ds[2], ds[3]);
+      }
     }
+    pv_tile_f16<D>(sKf + vb, pk, dq);
+  };
+
+  // step t: tile t sits in slot t % 2; the barrier also ends every wave's reads of
+  // slot (t + 1) % 2 (tile t - 1), which then takes tile t + 1
+  auto step = [&](int t, auto parity) __attribute__((always_inline)) {
+    constexpr int cur = decltype(parity)::value;
+    const int8_t* const cK = cur ? sK1 : sK0;
+    const int8_t* const cV = cur ? sV1 : sV0;
+    const uint8_t* const cKf = cur ? sKf1 : sKf0;
+    const float* const cVs = cur ? sVs1 : sVs0;
+    int8_t* const nK = cur ? sK0 : sK1;
+    int8_t* const nV = cur ? sV0 : sV1;
+    uint8_t* const nKf = cur ? sKf0 : sKf1;
+    float* const nVs = cur ? sVs0 : sVs1;
+    wait_copies();
     __syncthreads();
+    float vnext = 0.0f;
+    if (t + 1 < T) {
+      copy.k_tile(krs, t + 1, nK);
+      copy.k_tile(vrs, t + 1, nV);
+      copy.v_tile(kfrs, t + 1, Np, nKf);
+      if (tid < kTileKV) vnext = vsc[(t + 1) * kTileKV + tid];
+    }
+    // only the tail tile and, causal, tiles with a key after the wave's first row mask
+    if (qw < N && t <= wave_last)
+      tile(t, cK, cV, cKf, cVs, (t + 1) * kTileKV <= N && (!CAUSAL || t * kTileKV + kTileKV - 1 <= qw));
+    if (t + 1 < T && tid < kTileKV) nVs[tid] = vnext;
+  };
+
+  copy.k_tile(krs, 0, sK0);
+  copy.k_tile(vrs, 0, sV0);
+  copy.v_tile(kfrs, 0, Np, sKf0);
+  if (tid < kTileKV) sVs0[tid] = vsc[tid];
+  for (int t = 0; t < T; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (qi >= N) return;
