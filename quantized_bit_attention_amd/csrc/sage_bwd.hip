@@ -92,54 +92,66 @@ __device__ __forceinline__ float bwd_sigma(const float* nrm, int nblk, float* sR
 
 // ---------------------------------------------------------------------------
 // preparation: one workgroup per (head, 64 tokens); wave w takes tokens 16w .. 16w+15,
-// lane l channels l and l + 64 (D = 128) or l (D = 64).
+// a token D/8 lanes with 8 consecutive channels each (16-byte loads), so a wave works on
+// 512/D tokens at a time.  Pad tokens run the same arithmetic on zeros, which gives zero
+// codes, scales and D'.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  constexpr int CPL = D / 64;  // channels per lane
+  constexpr int LPR = D / 8;       // lanes per token
+  constexpr int RPP = 64 / LPR;    // tokens per pass of a wave
   const int nblk = a.Np / 64;
   const int g = blockIdx.x / nblk, blk = blockIdx.x % nblk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, c0 = 8 * (lane % LPR);  // token of the pass, first channel
   __shared__ float sRed[8];
   // exact token means of K and V (split 0 of the statistics pass holds the head's sums)
-  float kmean[CPL], vmean[CPL];
+  float kmean[8], vmean[8];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
-    kmean[j] = a.smooth_k ? fixed24_mean(a.ksum[(size_t)g * a.nsplit * D + c], a.N) : 0.0f;
-    vmean[j] = fixed24_mean(a.vsum[(size_t)g * a.nsplit * D + c], a.N);
+  for (int j = 0; j < 8; ++j) {
+    kmean[j] = a.smooth_k ? fixed24_mean(a.ksum[(size_t)g * a.nsplit * D + c0 + j], a.N) : 0.0f;
+    vmean[j] = fixed24_mean(a.vsum[(size_t)g * a.nsplit * D + c0 + j], a.N);
   }
-  float gmax = 0.0f, vmax = 0.0f;
-  for (int r = 0; r < 16; ++r) {
-    const int t = blk * 64 + 16 * wave + r;
-    const size_t row = (size_t)g * a.Np + t;
-    if (t >= a.N) {  // pad rows: zero codes and scales, no weight in dK / dV (log-sum-exp +inf)
+  // reductions over the LPR lanes of a token (aligned groups of consecutive lanes)
+  auto gmax = [](float x) {
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        a.v_i8[row * D + c] = 0;
-        a.do_i8[row * D + c] = 0;
-        a.kp[row * D + c] = 0;
-      }
-      if (lane == 0) {
-        a.v_scale[row] = 0.0f;
-        a.do_scale[row] = 0.0f;
-        a.dvec[row] = 0.0f;
-        a.lse2[row] = INFINITY;
-      }
-      continue;
-    }
-    const size_t src = ((size_t)g * a.N + t) * D;
-    float vv[CPL], gg[CPL];
+    for (int off = 1; off < LPR; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+  };
+  auto gsum = [](float x) {
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+  };
+  auto gsum64 = [](double x) {
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+  };
+  float gmx = 0.0f, vmx = 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 16 / RPP; ++pass) {
+    const int t = blk * 64 + 16 * wave + pass * RPP + sub;
+    const bool ok = t < a.N;
+    const size_t row = (size_t)g * a.Np + t;
+    const size_t src = ((size_t)g * a.N + (ok ? t : 0)) * D + c0;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    const uint4 vraw = ok ? *reinterpret_cast<const uint4*>(a.v + src) : z;
+    const uint4 graw = ok ? *reinterpret_cast<const uint4*>(a.dout + src) : z;
+    const uint4 oraw = ok ? *reinterpret_cast<const uint4*>(a.o + src) : z;
+    const uint4 kraw = ok ? *reinterpret_cast<const uint4*>(a.k + src) : z;
+    const f16x8 v8 = __builtin_bit_cast(f16x8, vraw), g8 = __builtin_bit_cast(f16x8, graw);
+    const f16x8 o8 = __builtin_bit_cast(f16x8, oraw), k8 = __builtin_bit_cast(f16x8, kraw);
+    float vv[8], gg[8];
+    uint32_t kp[4];
     float va = 0.0f, ga = 0.0f, vn = 0.0f, gn = 0.0f;
     double dsum = 0.0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      const float vx = (float)__builtin_bit_cast(_Float16, a.v[src + c]) - vmean[j];
-      const float gx = (float)__builtin_bit_cast(_Float16, a.dout[src + c]);
-      const float ox = (float)__builtin_bit_cast(_Float16, a.o[src + c]);
-      const float kx = (float)__builtin_bit_cast(_Float16, a.k[src + c]) - kmean[j];
-      a.kp[row * D + c] = __builtin_bit_cast(uint16_t, (_Float16)kx);
+    for (int j = 0; j < 8; ++j) {
+      const float vx = ok ? (float)v8[j] - vmean[j] : 0.0f;
+      const float gx = (float)g8[j], ox = (float)o8[j];
+      const float kx = ok ? (float)k8[j] - kmean[j] : 0.0f;
+      if (j & 1) kp[j >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)kx) << 16;
+      else kp[j >> 1] = __builtin_bit_cast(uint16_t, (_Float16)kx);
       vv[j] = vx;
       gg[j] = gx;
       va = fmaxf(va, fabsf(vx));
@@ -149,30 +161,33 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       // exact products of fp16 values; the fp64 sum of the row is exact for ordinary data
       dsum += (double)gx * (double)ox - (double)gx * (double)vmean[j];
     }
-    va = wave_max(va);
-    ga = wave_max(ga);
-    vn = wave_sum(vn);
-    gn = wave_sum(gn);
-    dsum = wave_sum_f64(dsum);
+    va = gmax(va);
+    ga = gmax(ga);
+    vn = gsum(vn);
+    gn = gsum(gn);
+    dsum = gsum64(dsum);
     const float vr = i8_factor(va), gr = i8_factor(ga);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      a.v_i8[row * D + c] = (int8_t)i8_code_int(vv[j], vr);
-      a.do_i8[row * D + c] = (int8_t)i8_code_int(gg[j], gr);
-    }
-    if (lane == 0) {
+    *reinterpret_cast<uint4*>(a.kp + row * D + c0) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
+    *reinterpret_cast<uint2*>(a.v_i8 + row * D + c0) =
+        make_uint2(pack_bytes4(i8_code_int(vv[0], vr), i8_code_int(vv[1], vr), i8_code_int(vv[2], vr), i8_code_int(vv[3], vr)),
+                   pack_bytes4(i8_code_int(vv[4], vr), i8_code_int(vv[5], vr), i8_code_int(vv[6], vr), i8_code_int(vv[7], vr)));
+    *reinterpret_cast<uint2*>(a.do_i8 + row * D + c0) =
+        make_uint2(pack_bytes4(i8_code_int(gg[0], gr), i8_code_int(gg[1], gr), i8_code_int(gg[2], gr), i8_code_int(gg[3], gr)),
+                   pack_bytes4(i8_code_int(gg[4], gr), i8_code_int(gg[5], gr), i8_code_int(gg[6], gr), i8_code_int(gg[7], gr)));
+    if (c0 == 0) {
       a.v_scale[row] = i8_scale(va);
       a.do_scale[row] = i8_scale(ga);
       a.dvec[row] = (float)dsum;
-      a.lse2[row] = a.lse[(size_t)g * a.N + t] * 1.4426950408889634f;
+      // pad rows: +inf, which gives them P = 0
+      a.lse2[row] = ok ? a.lse[(size_t)g * a.N + t] * 1.4426950408889634f : INFINITY;
     }
-    gmax = fmaxf(gmax, __builtin_sqrtf(gn));
-    vmax = fmaxf(vmax, __builtin_sqrtf(vn));
+    gmx = fmaxf(gmx, __builtin_sqrtf(gn));
+    vmx = fmaxf(vmx, __builtin_sqrtf(vn));
   }
+  const float gmax_w = wave_max(gmx), vmax_w = wave_max(vmx);
   if (lane == 0) {
-    sRed[2 * wave] = gmax;
-    sRed[2 * wave + 1] = vmax;
+    sRed[2 * wave] = gmax_w;
+    sRed[2 * wave + 1] = vmax_w;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
