@@ -580,6 +580,34 @@ def test_attn_degenerate_inputs(sage, orc, variant):
             check_o(f"{name} v{variant} c{causal}", g, o)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_attn_rising_scores_interior_tiles(sage, orc, d, causal):
+    """Variant 0's interior tiles form P~ against the row's running reference and fall back
+    to the tile maximum when a lane's 32 weights sum past 2^10.  Keys along one direction
+    with an oscillating, rising weight f(j) put the scores of later tiles up to ~20 (base 2)
+    above the reference or far below it, so along every row some interior tiles are kept
+    with large P~ and others are recomputed; rows differ in scale and (causal) in prefix."""
+    rng = np.random.default_rng(17)
+    N = 1000
+    sm = 1.0 / np.sqrt(d)
+    a = np.sqrt(20.0 / (sm * 1.4426950408889634))  # |u|^2 sm log2(e) = 20
+    u = rng.standard_normal(d)
+    u *= a / np.linalg.norm(u)
+    j = np.arange(N)
+    f = 0.6 * np.sin(j / 37.0) + 0.4 * j / N
+    q = np.empty((1, 2, N, d), np.float16)
+    k = np.empty((1, 2, N, d), np.float16)
+    for hh in range(2):
+        q[0, hh] = (u[None, :] * (0.5 + j / N)[:, None] + 0.05 * rng.standard_normal((N, d))).astype(np.float16)
+        k[0, hh] = (u[None, :] * f[:, None] + 0.05 * rng.standard_normal((N, d))).astype(np.float16)
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float16)
+    say(f"attn rising scores d={d} causal={causal}")
+    g = host(sage.attn(dev(q), dev(k), dev(v), causal=bool(causal), variant=0))
+    o = orc.attn(q, k, v, causal=causal, variant=0, bkv=sage.kv_tile(0, d))
+    check_o(f"rising d{d} c{causal}", g, o)
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 0, 64), (0, 2, 16, 128), (2, 0, 8, 64)])
 @pytest.mark.parametrize("variant", [0, 1, 2])
 def test_attn_empty_inputs(sage, shape, variant):
