@@ -234,32 +234,54 @@ __device__ __forceinline__ void f16_block(const uint8_t* vbase, const uint32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 128 keys of one head (wave w: keys 32w .. 32w+31), 64-row query tiles.
+// dK, dV: workgroup = 256 keys of one head (wave w: keys 32w .. 32w+31), one workgroup per
+// CU, 64-row query tiles through two LDS slots: the copies of tile t+1 (the INT8 and fp16
+// Q and dO tiles and the tile's row values) run while tile t is worked on.  Np is a
+// multiple of 128, so the last workgroup of a head may have waves past the padded tensor:
+// they take part in the copies and barriers only.
+constexpr int kKvWaves = 8, kKvThreads = 64 * kKvWaves, kKvKeys = 32 * kKvWaves;
+
+// 64 consecutive floats (one per lane) from a [Np] float array of the head into LDS.
+__device__ __forceinline__ void copy_row_values(__amdgpu_buffer_rsrc_t rs, int t, float* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, 4u * (threadIdx.x & 63),
+                                           (uint32_t)(t * kTileKV * 4), 0, 0);
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NCT = D / 32;
-  __shared__ __attribute__((aligned(16))) int8_t sQ[kTileKV * D];      // Qhat tile (k_tile layout)
-  __shared__ __attribute__((aligned(16))) int8_t sG[kTileKV * D];      // dOhat tile (k_tile layout)
-  __shared__ __attribute__((aligned(16))) uint8_t sQf[kTileKV * D * 2];  // Q fp16 tile (v_tile layout)
-  __shared__ __attribute__((aligned(16))) uint8_t sGf[kTileKV * D * 2];  // dO fp16 tile (v_tile layout)
-  __shared__ __attribute__((aligned(16))) float sL[kTileKV];  // log2-sum-exp of the tile's rows
-  __shared__ __attribute__((aligned(16))) float sD[kTileKV];  // D' of the rows
-  __shared__ __attribute__((aligned(16))) float sGs[kTileKV];  // INT8 scales of the dO rows
-  __shared__ float sRed[8];
+  // two slots per tile kind, as separate LDS objects (the step is instantiated per slot
+  // parity, so the compiler can tell the slot being filled from the slot being read)
+  __shared__ __attribute__((aligned(16))) int8_t sQ0[kTileKV * D];      // Qhat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sQ1[kTileKV * D];
+  __shared__ __attribute__((aligned(16))) int8_t sG0[kTileKV * D];      // dOhat tile (k_tile layout)
+  __shared__ __attribute__((aligned(16))) int8_t sG1[kTileKV * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sQf0[kTileKV * D * 2];  // Q fp16 tile (v_tile layout)
+  __shared__ __attribute__((aligned(16))) uint8_t sQf1[kTileKV * D * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t sGf0[kTileKV * D * 2];  // dO fp16 tile (v_tile layout)
+  __shared__ __attribute__((aligned(16))) uint8_t sGf1[kTileKV * D * 2];
+  __shared__ __attribute__((aligned(16))) float sL0[kTileKV];  // 8 - log2-sum-exp of the rows
+  __shared__ __attribute__((aligned(16))) float sL1[kTileKV];
+  __shared__ __attribute__((aligned(16))) float sD0[kTileKV];  // sigma 2^-8 D' of the rows
+  __shared__ __attribute__((aligned(16))) float sD1[kTileKV];
+  __shared__ __attribute__((aligned(16))) float sGs0[kTileKV];  // INT8 scales of the dO rows
+  __shared__ __attribute__((aligned(16))) float sGs1[kTileKV];
+  __shared__ float sRed[2 * kKvWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int nkb = a.Np / kBwdRows;
+  const int nkb = (a.Np + kKvKeys - 1) / kKvKeys;
   const int g = xcd_block(a.G * nkb) / nkb, kb = xcd_block(a.G * nkb) % nkb;
-  const int k0 = kb * kBwdRows, kw = k0 + 32 * wave, key = kw + (lane & 31);
+  const int k0 = kb * kKvKeys, kw = k0 + 32 * wave, key = kw + (lane & 31);
   const int N = a.N, Np = a.Np;
+  const bool has_keys = kw < Np;  // kw and Np are multiples of 32
 
   const float sigma = bwd_sigma(a.nrm + (size_t)g * (Np / 64) * 2, Np / 64, sRed);
 
   // B operands of this wave: Khat and V'hat rows of its 32 keys (pad rows are zero)
   i32x4 kb_op[D / 32], vb_op[D / 32];
   {
-    const int8_t* kr = a.k_i8 + ((size_t)g * Np + key) * D + 16 * h;
-    const int8_t* vr = a.v_i8 + ((size_t)g * Np + key) * D + 16 * h;
+    const int8_t* kr = a.k_i8 + ((size_t)g * Np + (has_keys ? key : 0)) * D + 16 * h;
+    const int8_t* vr = a.v_i8 + ((size_t)g * Np + (has_keys ? key : 0)) * D + 16 * h;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       kb_op[ks] = *reinterpret_cast<const i32x4*>(kr + 32 * ks);
@@ -272,48 +294,77 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // key's V' scale.
   const float ck = a.kscale * a.k_scale[(size_t)g * a.nkb + min(key, N - 1) / a.blk_k];
   const float sig8 = sigma * (1.0f / kPScale);
-  const float dvs = a.v_scale[(size_t)g * Np + key] * sig8;
+  const float dvs = a.v_scale[(size_t)g * Np + min(key, Np - 1)] * sig8;
 
   f32x16 dv[NCT], dk[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) dv[ct] = dk[ct] = f32x16{};
 
-  const TileCopy<D, 0, kBwdWaves> copy(Np);
+  const TileCopy<D, 0, kKvWaves> copy(Np);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.q_i8 + (size_t)g * Np * D, (size_t)Np * D);
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(a.do_i8 + (size_t)g * Np * D, (size_t)Np * D);
   const __amdgpu_buffer_rsrc_t qfrs = make_rsrc(a.q + (size_t)g * N * D, (size_t)N * D * 2);
   const __amdgpu_buffer_rsrc_t gfrs = make_rsrc(a.dout + (size_t)g * N * D, (size_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + (size_t)g * Np, (size_t)Np * 4);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(a.dvec + (size_t)g * Np, (size_t)Np * 4);
+  const __amdgpu_buffer_rsrc_t gsrs = make_rsrc(a.do_scale + (size_t)g * Np, (size_t)Np * 4);
   const int vb = pv_lane_offset<D>(lane);
 
-  // causal: rows below the workgroup's first key see none of its keys
+  // causal: rows below the workgroup's first key see none of its keys (t0 is even)
   const int t0 = CAUSAL ? k0 / kTileKV : 0;
   const int T = (N + kTileKV - 1) / kTileKV;
-  for (int t = t0; t < T; ++t) {
-    copy.k_tile(qrs, t, sQ);
-    copy.k_tile(grs, t, sG);
-    copy.v_tile(qfrs, t, Np, sQf);
-    copy.v_tile(gfrs, t, Np, sGf);
-    if (tid < kTileKV) {
-      const size_t r = (size_t)g * Np + t * kTileKV + tid;
-      sL[tid] = kLog2PScale - a.lse2[r];  // pad rows: L = +inf, so 2^8 P = 0
-      sD[tid] = a.dvec[r] * sig8;
-      sGs[tid] = a.do_scale[r];
+
+  // copies of tile t into one slot; wave 0 also brings the tile's 64 row values
+  auto issue = [&](int t, int8_t* q, int8_t* gq, uint8_t* qf, uint8_t* gf, float* L, float* Dv, float* Gs) {
+    copy.k_tile(qrs, t, q);
+    copy.k_tile(grs, t, gq);
+    copy.v_tile(qfrs, t, Np, qf);
+    copy.v_tile(gfrs, t, Np, gf);
+    if (wave == 0) {
+      copy_row_values(lrs, t, L);
+      copy_row_values(drs, t, Dv);
+      copy_row_values(gsrs, t, Gs);
     }
+  };
+  // wave 0, once its copies have landed: the row values become 8 - L (pad rows: L = +inf,
+  // so 2^8 P = 0) and sigma 2^-8 D'; no other wave reads the slot before the next barrier
+  auto fix_rows = [&](float* L, float* Dv) {
+    if (wave == 0) {
+      wait_copies();
+      L[lane] = kLog2PScale - L[lane];
+      Dv[lane] *= sig8;
+    }
+  };
+
+  auto step = [&](int t, auto parity) __attribute__((always_inline)) {
+    constexpr int cur = decltype(parity)::value;
+    const int8_t* const cQ = cur ? sQ1 : sQ0;
+    const int8_t* const cG = cur ? sG1 : sG0;
+    const uint8_t* const cQf = cur ? sQf1 : sQf0;
+    const uint8_t* const cGf = cur ? sGf1 : sGf0;
+    const float* const cL = cur ? sL1 : sL0;
+    const float* const cD = cur ? sD1 : sD0;
+    const float* const cGs = cur ? sGs1 : sGs0;
+    // tile t is in place; every wave is done with tile t-1, whose slot takes tile t+1
     wait_copies();
     __syncthreads();
+    if (t + 1 < T) {
+      if (cur) issue(t + 1, sQ0, sG0, sQf0, sGf0, sL0, sD0, sGs0);
+      else issue(t + 1, sQ1, sG1, sQf1, sGf1, sL1, sD1, sGs1);
+    }
     const int r0 = t * kTileKV;
     // this wave's keys are all beyond the tile's last row: nothing to add
-    const bool active = !CAUSAL || r0 + kTileKV - 1 >= kw;
+    const bool active = has_keys && (!CAUSAL || r0 + kTileKV - 1 >= kw);
     // causal: only a tile with a row before one of the wave's keys needs the mask
     const bool diag = CAUSAL && r0 < kw + 31;
     auto block = [&](int st) {
       const float c = a.q_scale[(size_t)g * a.nqb + min(r0, N - 1) / a.blk_q] * ck;
-      const i32x16 s = i8_block_regb<D>(sQ, st, kb_op, lane);
-      const i32x16 dp = i8_block_regb<D>(sG, st, vb_op, lane);
+      const i32x16 s = i8_block_regb<D>(cQ, st, kb_op, lane);
+      const i32x16 dp = i8_block_regb<D>(cG, st, vb_op, lane);
       // rows 32*st + 16*h + i of the tile
-      const float4* pl = reinterpret_cast<const float4*>(sL + 32 * st + 16 * h);
-      const float4* pd = reinterpret_cast<const float4*>(sD + 32 * st + 16 * h);
-      const float4* pg = reinterpret_cast<const float4*>(sGs + 32 * st + 16 * h);
+      const float4* pl = reinterpret_cast<const float4*>(cL + 32 * st + 16 * h);
+      const float4* pd = reinterpret_cast<const float4*>(cD + 32 * st + 16 * h);
+      const float4* pg = reinterpret_cast<const float4*>(cGs + 32 * st + 16 * h);
       uint32_t pkp[8], pks[8];
       // row r0 + 32 st + 16 h + i sees the key iff i >= thr
       const int thr = diag ? key - (r0 + 32 * st + 16 * h) : -1;
@@ -336,14 +387,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         pks[2 * q4] = pack_f16x2(ds[0], ds[1]);
         pks[2 * q4 + 1] = pack_f16x2(ds[2], ds[3]);
       }
-      f16_block<D>(sGf + vb, pkp, st, dv);
-      f16_block<D>(sQf + vb, pks, st, dk);
+      f16_block<D>(cGf + vb, pkp, st, dv);
+      f16_block<D>(cQf + vb, pks, st, dk);
     };
     if (active) {
       block(0);
       block(1);
     }
-    __syncthreads();
+    if (t + 1 < T) {
+      if (cur) fix_rows(sL0, sD0);
+      else fix_rows(sL1, sD1);
+    }
+  };
+
+  if (t0 < T) {
+    issue(t0, sQ0, sG0, sQf0, sGf0, sL0, sD0, sGs0);
+    fix_rows(sL0, sD0);
+  }
+  for (int t = t0; t < T; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (key >= N) return;
@@ -523,13 +586,13 @@ static hipError_t launch_bwd_d(int causal, const BwdArgs& a, hipStream_t st) {
   bwd_prep_kernel<D><<<G * (a.Np / 64), 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = G * (a.Np / kBwdRows);
+  const int grid_kv = G * ((a.Np + kKvKeys - 1) / kKvKeys), grid_q = G * (a.Np / kBwdRows);
   if (causal) {
-    bwd_dkdv_kernel<D, true><<<grid, kBwdThreads, 0, st>>>(a);
-    bwd_dq_kernel<D, true><<<grid, kBwdThreads, 0, st>>>(a);
+    bwd_dkdv_kernel<D, true><<<grid_kv, kKvThreads, 0, st>>>(a);
+    bwd_dq_kernel<D, true><<<grid_q, kBwdThreads, 0, st>>>(a);
   } else {
-    bwd_dkdv_kernel<D, false><<<grid, kBwdThreads, 0, st>>>(a);
-    bwd_dq_kernel<D, false><<<grid, kBwdThreads, 0, st>>>(a);
+    bwd_dkdv_kernel<D, false><<<grid_kv, kKvThreads, 0, st>>>(a);
+    bwd_dq_kernel<D, false><<<grid_q, kBwdThreads, 0, st>>>(a);
   }
   return hipGetLastError();
 }
