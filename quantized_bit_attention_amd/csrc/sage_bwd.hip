@@ -234,12 +234,15 @@ __device__ __forceinline__ void f16_block(const uint8_t* vbase, const uint32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 256 keys of one head (wave w: keys 32w .. 32w+31), one workgroup per
-// CU, 64-row query tiles through two LDS slots: the copies of tile t+1 (the INT8 and fp16
-// Q and dO tiles and the tile's row values) run while tile t is worked on.  Np is a
-// multiple of 128, so the last workgroup of a head may have waves past the padded tensor:
-// they take part in the copies and barriers only.
-constexpr int kKvWaves = 8, kKvThreads = 64 * kKvWaves, kKvKeys = 32 * kKvWaves;
+// dK, dV: workgroup = 32 keys per wave of one head (wave w: keys 32w .. 32w+31), 64-row
+// query tiles through two LDS slots: the copies of tile t+1 (the INT8 and fp16 Q and dO
+// tiles and the tile's row values) run while tile t is worked on.  8 waves at d = 128
+// (96 KB of LDS, one workgroup per CU, two waves per SIMD); 4 at d = 64, whose registers
+// leave room for three waves per SIMD (three workgroups per CU).  Np is a multiple of
+// 128, so the last workgroup of a head may have waves past the padded tensor: they take
+// part in the copies and barriers only.
+template <int D> constexpr int kv_waves() { return D == 128 ? 8 : 4; }
+template <int D> constexpr int kv_keys() { return 32 * kv_waves<D>(); }
 
 // 64 consecutive floats (one per lane) from a [Np] float array of the head into LDS.
 __device__ __forceinline__ void copy_row_values(__amdgpu_buffer_rsrc_t rs, int t, float* dst) {
@@ -248,7 +251,8 @@ __device__ __forceinline__ void copy_row_values(__amdgpu_buffer_rsrc_t rs, int t
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kv_waves<D>(), D == 128 ? 1 : 3) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int kKvWaves = kv_waves<D>(), kKvKeys = kv_keys<D>();
   constexpr int NCT = D / 32;
   // two slots per tile kind, as separate LDS objects (the step is instantiated per slot
   // parity, so the compiler can tell the slot being filled from the slot being read)
@@ -586,12 +590,12 @@ static hipError_t launch_bwd_d(int causal, const BwdArgs& a, hipStream_t st) {
   bwd_prep_kernel<D><<<G * (a.Np / 64), 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid_kv = G * ((a.Np + kKvKeys - 1) / kKvKeys), grid_q = G * (a.Np / kBwdRows);
+  const int grid_kv = G * ((a.Np + kv_keys<D>() - 1) / kv_keys<D>()), grid_q = G * (a.Np / kBwdRows);
   if (causal) {
-    bwd_dkdv_kernel<D, true><<<grid_kv, kKvThreads, 0, st>>>(a);
+    bwd_dkdv_kernel<D, true><<<grid_kv, 64 * kv_waves<D>(), 0, st>>>(a);
     bwd_dq_kernel<D, true><<<grid_q, kBwdThreads, 0, st>>>(a);
   } else {
-    bwd_dkdv_kernel<D, false><<<grid_kv, kKvThreads, 0, st>>>(a);
+    bwd_dkdv_kernel<D, false><<<grid_kv, 64 * kv_waves<D>(), 0, st>>>(a);
     bwd_dq_kernel<D, false><<<grid_q, kBwdThreads, 0, st>>>(a);
   }
   return hipGetLastError();
