@@ -107,7 +107,10 @@ constexpr float kLazyLog2 = 8.0f;
 // alpha is the factor the running O must be scaled by (rescale is false for the whole
 // wave when no lane needs it).
 // MASK: keys >= N, and keys > qi when causal, get P~ = 0 and stay out of the max.
-template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, typename SV>
+// DEFER0 (variant 3, unmasked interior tiles): leave the packed weights of a P~ block with
+// scale code 0 for fp4_code0_fix after the interleaved block, so that block stays one
+// basic block.
+template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, bool DEFER0 = false, typename SV>
 __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const float* bias, int kl, int N,
                                              int qi, float& m, float& l, uint32_t* pk, float& alpha,
                                              bool& rescale, float lazy = kLazyLog2, uint32_t* pscale = nullptr) {
@@ -181,26 +184,29 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
       }
     const uint32_t pb = __float_as_uint(pm);
     const int code = max((int)(pb >> 23) - 2 + ((pb & 0x7fffffu) > 0x400000u ? 1 : 0), 0);
-    float sc = __uint_as_float((uint32_t)max(code, 1) << 23);  // 2^(code - 127)
-    if (__builtin_amdgcn_ballot_w64(code == 0) != 0) {
-      // a block of zeros, or a largest weight below 2^-124 (scale code 0, 2^-127): such
-      // lanes scale by hand (exact) and convert with a unit scale
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pf[st][i] = code == 0 ? __builtin_amdgcn_ldexpf(pf[st][i], 127) : pf[st][i];
-      sc = code == 0 ? 1.0f : sc;
-    }
+    const float sc = __uint_as_float((uint32_t)max(code, 1) << 23);  // 2^(code - 127)
     // the conversion divides by the scale (a power of two: exact) and rounds to nearest
     // even, saturating at 6; pk[w] holds keys 8w .. 8w+7, the lower key in the low nibble
+    auto convert = [&](float scale, float mul, uint32_t* out) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float* q8 = &pf[w >> 1][8 * (w & 1)];
-      uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q8[0], q8[1], sc, 0);
-      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[2], q8[3], sc, 1);
-      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[4], q8[5], sc, 2);
-      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[6], q8[7], sc, 3);
-      pk[w] = word;
+      for (int w = 0; w < 4; ++w) {
+        const float* q8 = &pf[w >> 1][8 * (w & 1)];
+        uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q8[0] * mul, q8[1] * mul, scale, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[2] * mul, q8[3] * mul, scale, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[4] * mul, q8[5] * mul, scale, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[6] * mul, q8[7] * mul, scale, 3);
+        out[w] = word;
+      }
+    };
+    convert(sc, 1.0f, pk);
+    if (!DEFER0 && __builtin_amdgcn_ballot_w64(code == 0) != 0) {
+      // a block of zeros, or a largest weight below 2^-124 (scale code 0, 2^-127): such
+      // lanes scale by 2^127 by hand (exact) and convert with a unit scale.  Only the
+      // packed words are redone, so the common path keeps the weights where they are.
+      uint32_t pk0[4];
+      convert(1.0f, 0x1.0p127f, pk0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pk[w] = code == 0 ? pk0[w] : pk[w];
     }
     *pscale = (uint32_t)code;
     l += psum[0] + psum[1];
@@ -232,6 +238,28 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
   l += psum[0] + psum[1];
 }
 
+
+// Variant 3, unmasked tile whose softmax deferred the rare scale code 0 (a P~ block whose
+// largest weight is below 2^-124, or all zero): the lanes with that code redo their P~
+// from S exactly as softmax_tile formed it (2^fma(S, c, -m) with the updated m), scale it
+// by 2^127 by hand (exact) and convert with a unit scale.
+__device__ __forceinline__ void fp4_code0_fix(const f32x16* s, const float* c, float m, uint32_t code,
+                                              uint32_t* pk) {
+  float pf[2][16];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pf[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], c[st], -m)) * 0x1.0p127f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float* q8 = &pf[w >> 1][8 * (w & 1)];
+    uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q8[0], q8[1], 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[2], q8[3], 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[4], q8[5], 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q8[6], q8[7], 1.0f, 3);
+    pk[w] = code == 0u ? word : pk[w];
+  }
+}
 
 // Variant 0, unmasked tile: P~ against the row's current reference m, without the
 // tile's maximum.  The reference only has to keep P~ within fp16 and the sums
@@ -643,6 +671,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
   // channels (byte ct: channel 32*ct + l%32) for the V tiles in the two LDS slots; the
   // zero P~(-1) and V slot of iteration 0 get unit scales (code 127)
   uint32_t pscA = 127u, pscB = 127u;
+  bool fp4_fix_pending = false;  // variant 3: P~ of the last tile needs fp4_code0_fix
   uint32_t vsc[2] = {0x7f7f7f7fu, 0x7f7f7f7fu};
   auto v_scales = [&](int t) -> uint32_t {
     const uint8_t* e = a.v_e8 + ((size_t)g * (a.Np / 32) + 2 * t + h) * D + ql * (D / 32);
@@ -741,10 +770,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
     float* const c = cur == 0 ? cA : cB;
     float* const cn = cur == 0 ? cB : cA;
     uint32_t* const pk = cur == 0 ? pkA : pkB;        // P~(t)
-    const uint32_t* const pkp = cur == 0 ? pkB : pkA; // P~(t-1)
+    uint32_t* const pkp = cur == 0 ? pkB : pkA;       // P~(t-1)
     uint32_t* const psc = cur == 0 ? &pscA : &pscB;   // variant 3: block scale of P~(t)
     const uint32_t psp = cur == 0 ? pscB : pscA;      //  and of P~(t-1)
 
+    if constexpr (VARIANT == 3) {
+      // P~(t-1) of an interior tile that took scale code 0 (its S, c and the row's m are
+      // still those of tile t-1 here)
+      if (fp4_fix_pending) {
+        fp4_code0_fix(sn, cn, m, psp, pkp);
+        fp4_fix_pending = false;
+      }
+    }
     const bool compute = wave_active && t < T && t <= wave_last;
     const bool compute_next = wave_active && t + 1 <= wave_last && t + 1 < T;
     // P~(-1) and the V slot read at t = 0 are zeros, so iteration 0 may run the
@@ -776,9 +813,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
       if constexpr (VARIANT != 0) {
         pv_tile(sVp, pkp, psp, vsc[cur ^ 1]);
         score_tile(sKn, sn);
-        softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, kLazyLog2,
-                                                      psc);
+        softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false, VARIANT == 3>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale,
+                                                                     kLazyLog2, psc);
         interleave_schedule<D, VARIANT, SMOOTHQ>();
+        // variant 3: a P~ block with scale code 0 is repaired at the start of the next
+        // iteration, ahead of its interleaved block (a branch here would split this one)
+        if constexpr (VARIANT == 3) fp4_fix_pending = __builtin_amdgcn_ballot_w64(*psc == 0u) != 0;
       } else if constexpr (!SMOOTHQ) {
         // (at d = 64 this holds the kernel to two waves per SIMD, 197 VGPRs: 3-5 % faster
         // than the general softmax at three waves, which would spill under a 168 cap)
