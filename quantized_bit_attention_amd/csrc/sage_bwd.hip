@@ -19,16 +19,18 @@
 // Kernels (all on [G = B*H heads][N][D] tensors):
 //  - bwd_prep_kernel: per token, INT8 V' and dO with their scales, D', the log-sum-exp in
 //    base 2, K' in fp16, and per 64-row block the largest |dO_i| and |V'_j| (for sigma);
-//  - bwd_dkdv_kernel: a workgroup owns 128 keys (32 per wave) and walks 64-row query
-//    tiles.  S = Qhat Khat^T and dP = dOhat V'hat^T come out of v_mfma_i32_32x32x32_i8
+//  - bwd_dkdv_kernel: a workgroup owns 32 keys per wave (8 waves at d = 128, 4 at d = 64)
+//    and walks 64-row query tiles through two LDS slots.  S = Qhat Khat^T and dP = dOhat V'hat^T come out of v_mfma_i32_32x32x32_i8
 //    with the query tile as the A operand (rows in the k_perm order of the forward's K
 //    tile), so each lane holds one key and 16 consecutive rows of each 32-row block; P
 //    and dS are then packed as fp16 pairs in exactly the layout of the forward's P~, and
 //    dV^T = dO^T P and dK^T = Q^T dS run as the forward's P~ V product with the dO and Q
 //    fp16 tiles in place of V;
-//  - bwd_dq_kernel: the forward's layout (a workgroup owns 128 query rows): S^T and dP^T
-//    per 64-key tile, dS packed as the forward's P~, and dQ^T = K'^T dS^T as its P~ V
-//    product with the K' fp16 tile in place of V.
+//  - bwd_dq_kernel: the forward's layout (a workgroup owns 128 query rows, their Qhat and
+//    dOhat rows held as register operands): S^T and dP^T per 64-key tile through two LDS
+//    slots, dS packed as the forward's P~, and dQ^T = K'^T dS^T as its P~ V product with
+//    the K' fp16 tile in place of V.
+// Both number their workgroups so that each XCD walks a contiguous range of heads.
 // No atomics: dK and dV are written by the key blocks' owners, dQ by the query blocks'
 // owners, so the results are deterministic.
 #include "sage_device.h"
