@@ -93,32 +93,39 @@ def test_bwd_matches_oracle(sage, orc, name, cfg, shape, causal, blk_q, blk_k):
     check(name, g, r)
 
 
+FULL = [
+    # recipe cfg (its full shape), heads compared (every element), causal
+    (2, [0, 17, 34, 51, 68, 85, 102, 127], 1),   # LLM prefill: B=4 H=32 N=4096 d=128
+    (3, [0, 23, 47], 0),                          # image generation: B=2 H=24 N=8192 d=64
+]
+
+
 @pytest.mark.slow
-def test_bwd_full_size_llm_prefill(sage, orc):
-    """The LLM-prefill workload's shape (B=4, H=32, N=4096, d=128, causal): the GPU backward over
-    all 128 heads; every element of eight heads (including the first and the last) against
-    the oracle."""
-    x = workloads.make_inputs(2)
+@pytest.mark.parametrize("cfg,heads,causal", FULL, ids=[f"cfg{c[0]}" for c in FULL])
+def test_bwd_full_size(sage, orc, cfg, heads, causal):
+    """A workload's full shape: the GPU backward over all heads; every element of the listed
+    heads (including the first and the last) against the oracle."""
+    x = workloads.make_inputs(cfg)
     B, H, N, d = x["q"].shape
+    assert heads[-1] == B * H - 1
     rng = np.random.default_rng(12)
     dout = rng.standard_normal(x["q"].shape).astype(np.float16)
-    heads = [0, 17, 34, 51, 68, 85, 102, B * H - 1]
-    say(f"bwd full size {x['q'].shape}: oracle forward of heads {heads}")
+    say(f"bwd full size cfg{cfg} {x['q'].shape} causal={causal}: oracle forward of heads {heads}")
     sel = lambda a: np.ascontiguousarray(a.reshape(B * H, N, d)[heads].reshape(1, len(heads), N, d))
     qs, ks, vs, gs = sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(dout)
-    o16 = orc.attn(qs, ks, vs, causal=1, variant=0, blk_q=128, blk_k=64, bkv=64).astype(np.float16)
+    o16 = orc.attn(qs, ks, vs, causal=causal, variant=0, blk_q=128, blk_k=64, bkv=64).astype(np.float16)
     # the GPU runs every head; o of the other heads comes from the GPU forward (their
     # gradients are not compared)
     qd, kd, vd = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    o, lse = sage.attn_fwd_train(qd, kd, vd, causal=True)
+    o, lse = sage.attn_fwd_train(qd, kd, vd, causal=bool(causal))
     o.view(B * H, N, d)[heads] = dev(o16.reshape(len(heads), N, d))
-    g = sage.attn_bwd(qd, kd, vd, o, dev(dout), lse, causal=True)
+    g = sage.attn_bwd(qd, kd, vd, o, dev(dout), lse, causal=bool(causal))
     torch.cuda.synchronize()
     g = {n: t.view(B * H, N, d)[heads].cpu().numpy().astype(np.float64).reshape(1, len(heads), N, d)
          for n, t in g.items()}
     say(f"  oracle backward of heads {heads}")
-    r = orc.attn_bwd(qs, ks, vs, o16, gs, causal=1, blk_q=128, blk_k=64, smooth_k=1, smooth_v=1)
-    check("llm-prefill full size", g, r)
+    r = orc.attn_bwd(qs, ks, vs, o16, gs, causal=causal, blk_q=128, blk_k=64, smooth_k=1, smooth_v=1)
+    check(f"cfg{cfg} full size", g, r)
 
 
 def test_bwd_is_deterministic(sage):
