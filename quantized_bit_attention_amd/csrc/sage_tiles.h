@@ -183,6 +183,11 @@ __device__ __forceinline__ void tile_kscales(const float* ksc, int t, unsigned l
   // address space, which allows scalar loads
   typedef const __attribute__((address_space(4))) float* const_ptr;
   const const_ptr kc = (const_ptr)ksc;
+  if (kshift >= 6) {  // blocks of 64 keys or more: one K block covers the tile (one load)
+    const float v = kc[min((unsigned)(t * kTileKV), last_key) >> kshift];
+    kq[0] = kq[1] = kq[2] = kq[3] = v;
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) kq[j] = kc[min((unsigned)(t * kTileKV + 16 * j), last_key) >> kshift];
 }
