@@ -389,8 +389,11 @@ __device__ __forceinline__ void interleave_schedule() {
 // 1 .. 128 rows (the workgroup's 128 rows are whole groups; with Q smoothing the exact
 // mean of each Q block of blk_q rows is taken out first), or MXFP4 per 32-channel block
 // (one lane's operand per block).
+// Two workgroups per CU; at d = 64 the 8-bit P~V variants are held to 168 VGPRs, which
+// gives a third (their LDS is small): variant 3 and variant 1 with causal Q smoothing sat
+// at 169-171 VGPRs and run 10-14 % faster with the third wave (a spill or two).
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void attn_kernel(AttnArgs a) {
   static_assert(!FUSEQ || VARIANT <= 1 || !SMOOTHQ, "in-kernel Q quantisation with Q smoothing: INT8 Q only");
   static_assert(VARIANT < 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
