@@ -342,6 +342,8 @@ EDGE = [
     ("n65_d128", 2, dict(N=65, B=1, H=2), dict(causal=0, variant=0)),
     ("n129_causal_d128", 2, dict(N=129, B=2, H=1), dict(causal=1, variant=0)),
     ("n200_v1_d64", 1, dict(N=200, B=1, H=2), dict(causal=0, variant=1)),
+    ("n300_v1_causal_d64", 3, dict(N=300, B=1, H=2), dict(causal=1, variant=1)),
+    ("n520_v1_causal_d64_smoothv", 4, dict(N=520, B=1, H=2), dict(causal=1, variant=1, smooth_v=1)),
     ("n333_v1_causal", 5, dict(N=333, B=1, H=2), dict(causal=1, variant=1)),
     ("blk32_16", 2, dict(N=300, B=1, H=2), dict(causal=1, variant=0, blk_q=32, blk_k=16)),
     ("blk64_128", 3, dict(N=520, B=1, H=2), dict(causal=0, variant=0, blk_q=64, blk_k=128)),
