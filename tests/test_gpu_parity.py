@@ -610,6 +610,24 @@ def test_attn_rising_scores_interior_tiles(sage, orc, d, causal):
     check_o(f"rising d{d} c{causal}", g, o)
 
 
+@pytest.mark.parametrize("d,sigma,causal", [(128, 74.0, 0), (128, 251.0, 1), (64, 74.0, 1), (64, 251.0, 0)])
+def test_attn_large_logit_scale(sage, orc, d, sigma, causal):
+    """Logit scales far past the workloads': Q and K with standard deviation 74 or 251 give
+    c = dQ dK sm_scale log2(e) of about 0.9 to 15 per unit of the INT8 score, row maxima
+    of about 3e4 and 4e5 (base 2) and a softmax that is close to a hard maximum.  Every
+    fp32 step of the exponent (c S - m) has to hold here, since differences of a few
+    units decide the weights; variant 0 against the oracle on every element."""
+    rng = np.random.default_rng(31)
+    N = 700
+    q = (sigma * rng.standard_normal((1, 2, N, d))).astype(np.float16)
+    k = (sigma * rng.standard_normal((1, 2, N, d))).astype(np.float16)
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float16)
+    say(f"attn large logit scale d={d} sigma={sigma} causal={causal}")
+    g = host(sage.attn(dev(q), dev(k), dev(v), causal=bool(causal), variant=0))
+    o = orc.attn(q, k, v, causal=causal, variant=0, bkv=sage.kv_tile(0, d))
+    check_o(f"large logits d{d} s{sigma:g} c{causal}", g, o)
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 0, 64), (0, 2, 16, 128), (2, 0, 8, 64)])
 @pytest.mark.parametrize("variant", [0, 1, 2])
 def test_attn_empty_inputs(sage, shape, variant):
