@@ -257,8 +257,10 @@ int sage_attn_fwd_qf16(const void* q, const int8_t* k_i8, const float* k_scale, 
 /*
  * Training forward of the 8-bit backward (SageAttention3 abstract: 8-bit attention for
  * training; FlashAttention-2 "Backward pass": the backward recomputes P from the row
- * log-sum-exp).  Exactly sage_attn_fwd_ex with variant SAGE_VARIANT_INT8QK_FP16PV
- * (same kernels, same o), and additionally
+ * log-sum-exp).  sage_attn_fwd_ex with variant SAGE_VARIANT_INT8QK_FP16PV (same passes,
+ * same scores and fp16 weights), except that o is divided by the row sum of the unrounded
+ * weights, the sum lse is defined on, where sage_attn_fwd_ex divides by the sum of the fp16
+ * weights P~ V multiplies; the two o differ in their last fp16 bits.  Additionally
  *   lse[B,H,N] fp32 (16-byte aligned, device) = ln of the row sum of exp(sm_scale * S)
  *   over the visible keys, S the dequantised INT8 scores of the smoothed K (the shift by
  *   K's mean drops out of the softmax), i.e. ln(l) + the running maximum, per row.

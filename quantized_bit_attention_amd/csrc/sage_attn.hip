@@ -110,7 +110,10 @@ constexpr float kLazyLog2 = 8.0f;
 // DEFER0 (variant 3, unmasked interior tiles): leave the packed weights of a P~ block with
 // scale code 0 for fp4_code0_fix after the interleaved block, so that block stays one
 // basic block.
-template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, bool DEFER0 = false, typename SV>
+// RSUM (variant 0): l sums the fp16 weights the P~ V product uses, so the fp16 rounding of a
+// dominant weight cancels in O / l; without it (training forward) l sums the unrounded P~,
+// the sum the row log-sum-exp is defined on.
+template <int VARIANT, bool CAUSAL, bool SMOOTHQ, bool MASK, bool DEFER0 = false, bool RSUM = true, typename SV>
 __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const float* bias, int kl, int N,
                                              int qi, float& m, float& l, uint32_t* pk, float& alpha,
                                              bool& rescale, float lazy = kLazyLog2, uint32_t* pscale = nullptr) {
@@ -233,7 +236,12 @@ __device__ __forceinline__ void softmax_tile(const SV* s, const float* c, const 
       } else {
         pk[st * 4 + i / 4] = cvt_pk_fp8(pv[2], pv[3], cvt_pk_fp8(pv[0], pv[1], 0u, false), true);
       }
-      psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+      if (VARIANT == 0 && RSUM) {
+        psum[st] = sum_f16x2(pk[st * 8 + i / 2], psum[st]);
+        psum[st] = sum_f16x2(pk[st * 8 + i / 2 + 1], psum[st]);
+      } else {
+        psum[st] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+      }
     }
   l += psum[0] + psum[1];
 }
@@ -268,7 +276,9 @@ __device__ __forceinline__ void fp4_code0_fix(const f32x16* s, const float* c, f
 // returns false.  Otherwise (a key far above m, or m = -inf on a row's first tile) it
 // returns true for the whole wave, leaves m and l untouched, and the caller recomputes
 // the tile with softmax_tile, which moves m to the running maximum.
+// RSUM: as in softmax_tile.
 constexpr float kFastSum = 1024.0f;  // 2^10
+template <bool RSUM = true>
 __device__ __forceinline__ bool softmax_tile_fast(const i32x16* s, const float* c, float m, float& l,
                                                   uint32_t* pk) {
   const float shift = -m;
@@ -283,7 +293,12 @@ __device__ __forceinline__ bool softmax_tile_fast(const i32x16* s, const float* 
       pk[st * 8 + i / 2] = pack_f16x2(p[0], p[1]);
       pk[st * 8 + i / 2 + 1] = pack_f16x2(p[2], p[3]);
       asm volatile("" ::"v"(pk[st * 8 + i / 2]), "v"(pk[st * 8 + i / 2 + 1]));  // as in softmax_tile
-      psum[st] += (p[0] + p[1]) + (p[2] + p[3]);
+      if (RSUM) {
+        psum[st] = sum_f16x2(pk[st * 8 + i / 2], psum[st]);
+        psum[st] = sum_f16x2(pk[st * 8 + i / 2 + 1], psum[st]);
+      } else {
+        psum[st] += (p[0] + p[1]) + (p[2] + p[3]);
+      }
     }
   const float t = psum[0] + psum[1];
   // also true for inf and NaN sums
@@ -392,8 +407,12 @@ __device__ __forceinline__ void interleave_schedule() {
 // Two workgroups per CU; at d = 64 the 8-bit P~V variants are held to 168 VGPRs, which
 // gives a third (their LDS is small): variant 3 and variant 1 with causal Q smoothing sat
 // at 169-171 VGPRs and run 10-14 % faster with the third wave (a spill or two).
-template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ>
+// TRAIN (training forward, variant 0): l sums the unrounded P~ (RSUM off), so the row
+// log-sum-exp is that of the weights themselves; O can then differ from the inference
+// forward's in its last fp16 bits.
+template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ, bool TRAIN = false>
 __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void attn_kernel(AttnArgs a) {
+  static_assert(!TRAIN || (VARIANT == 0 && !SMOOTHQ), "training forward: variant 0 without Q smoothing");
   static_assert(!FUSEQ || VARIANT <= 1 || !SMOOTHQ, "in-kernel Q quantisation with Q smoothing: INT8 Q only");
   static_assert(VARIANT < 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
@@ -827,11 +846,13 @@ __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void
         // than the general softmax at three waves, which would spill under a 168 cap)
         score_tile(sKn, sn);
         pv_tile(sVp, pkp);
-        const bool slow = softmax_tile_fast(s, c, m, l, pk);
+        const bool slow = softmax_tile_fast<!TRAIN>(s, c, m, l, pk);
         interleave_schedule<D, VARIANT, SMOOTHQ>();
         __builtin_amdgcn_s_setprio(0);
         // the reference moves to the row maximum (rare after a row's first tiles)
-        if (slow) softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, 0.0f);
+        if (slow)
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false, false, !TRAIN>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale,
+                                                                      0.0f);
       } else {
         score_tile(sKn, sn);
         pv_tile(sVp, pkp);
@@ -844,11 +865,11 @@ __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void
       if (pv_prev) pv_tile(sVp, pkp, psp, vsc[cur ^ 1]);
       if (compute) {
         if (full)
-          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, kLazyLog2,
-                                                        psc);
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, false, false, !TRAIN>(s, c, bias, kl, N, qi, m, l, pk, alpha,
+                                                                       rescale, kLazyLog2, psc);
         else
-          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true>(s, c, bias, kl, N, qi, m, l, pk, alpha, rescale, kLazyLog2,
-                                                       psc);
+          softmax_tile<VARIANT, CAUSAL, SMOOTHQ, true, false, !TRAIN>(s, c, bias, kl, N, qi, m, l, pk, alpha,
+                                                                      rescale, kLazyLog2, psc);
       }
     }
     if (rescale) {  // O already holds P~(t-1) V(t-1)
@@ -947,10 +968,10 @@ __global__ __launch_bounds__(64 * kDbgWaves) void debug_qk_kernel(const int8_t* 
 // ---------------------------------------------------------------------------
 // launchers
 
-template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ = false>
+template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ = false, bool TRAIN = false>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
   const int grid = a.G * ((a.Np + kAttnRows - 1) / kAttnRows);
-  attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ, FUSEQ><<<grid, kAttnThreads, 0, st>>>(a);
+  attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ, FUSEQ, TRAIN><<<grid, kAttnThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -966,6 +987,11 @@ hipError_t launch_attn(int d, int variant, int causal, int smooth_q, const AttnA
     if (variant <= 1) {
       auto one = [&](auto dc, auto vc) -> hipError_t {
         constexpr int DD = decltype(dc)::value, VV = decltype(vc)::value;
+        if constexpr (VV == 0) {
+          if (a.lse && !smooth_q)  // the training forward
+            return causal ? launch_one<DD, 0, true, false, true, true>(a, st)
+                          : launch_one<DD, 0, false, false, true, true>(a, st);
+        }
         if (causal)
           return smooth_q ? launch_one<DD, VV, true, true, true>(a, st) : launch_one<DD, VV, true, false, true>(a, st);
         return smooth_q ? launch_one<DD, VV, false, true, true>(a, st) : launch_one<DD, VV, false, false, true>(a, st);

@@ -143,6 +143,12 @@ __device__ __forceinline__ uint32_t mx_block_fp4(const float* v, uint4& packed) 
   return code;
 }
 
+// acc + the two fp16 values of a packed word (v_dot2_f32_f16 against ones: the products are
+// exact, the sum is in fp32).
+__device__ __forceinline__ float sum_f16x2(uint32_t packed, float acc) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
+}
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   f32x2 v = {a, b};
   f16x2 h = __builtin_convertvector(v, f16x2);  // v_cvt_pk_f16_f32, round to nearest even

@@ -142,13 +142,18 @@ def test_bwd_is_deterministic(sage):
 
 
 def test_train_forward_output_and_lse(sage, orc):
-    """attn_fwd_train's output is attn's, and its lse is the log-sum-exp of the oracle's scores."""
+    """attn_fwd_train's output is attn's up to the divisor (the sum of the unrounded weights
+    instead of the fp16 ones: each fp16 weight is within 2^-11 of its value relative, so the
+    divisors differ by at most 2^-11 relative; the fp16 outputs then differ by that plus at most
+    one fp16 step, 2^-10 relative),
+    and its lse is the log-sum-exp of the oracle's scores."""
     x = workloads.make_inputs(2, N=300, B=1, H=2)
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     o, lse = sage.attn_fwd_train(q, k, v, causal=True)
     o2 = sage.attn(q, k, v, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(o, o2)
+    a, b = o.float(), o2.float()
+    assert float((a - b).abs().max()) <= 3 * 2.0 ** -11 * float(b.abs().max())
     # lse against the oracle: the textbook log-sum-exp of the dequantised INT8 scores
     r = orc.quant(x["q"], x["k"], blk_q=128, blk_k=64, smooth_k=1)
     qi = r["q_i8"][0, :, :300].astype(np.int64)
