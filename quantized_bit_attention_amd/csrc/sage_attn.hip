@@ -410,9 +410,12 @@ __device__ __forceinline__ void interleave_schedule() {
 // TRAIN (training forward, variant 0): l sums the unrounded P~ (RSUM off), so the row
 // log-sum-exp is that of the weights themselves; O can then differ from the inference
 // forward's in its last fp16 bits.
-template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ, bool TRAIN = false>
+// KT (blk_k >= 64): one K block covers each key tile, so a tile has one K scale and every
+// lane the same c (a scalar operand), instead of one scale per 16-key quarter.
+template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ, bool TRAIN = false, bool KT = false>
 __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void attn_kernel(AttnArgs a) {
   static_assert(!TRAIN || (VARIANT == 0 && !SMOOTHQ), "training forward: variant 0 without Q smoothing");
+  static_assert(!KT || (VARIANT == 0 && !SMOOTHQ), "one K scale per tile: variant 0 without Q smoothing");
   static_assert(!FUSEQ || VARIANT <= 1 || !SMOOTHQ, "in-kernel Q quantisation with Q smoothing: INT8 Q only");
   static_assert(VARIANT < 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
@@ -725,12 +728,12 @@ __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void
     if constexpr (VARIANT == 3) vsc[0] = v_scales(0);
   } else {
     if (wave_active) score_tile(sK0, sA);  // tile 0 is visible to every row
-    tile_kscales(ksc, 0, last_key, kshift, kq);
-    cA[0] = dqs * kscale_of(kq, 0, h);
-    cA[1] = dqs * kscale_of(kq, 1, h);
+    tile_kscales_for<KT>(ksc, 0, last_key, kshift, kq);
+    cA[0] = dqs * (KT ? kq[0] : kscale_of(kq, 0, h));
+    cA[1] = dqs * (KT ? kq[0] : kscale_of(kq, 1, h));
     if (SMOOTHQ)
       smooth_q_bias<D>(sK0, sQl, sQs, a.kscale * kscale_quarter(ksc, 0, wave_id(), last_key, kshift), sBias0);
-    tile_kscales(ksc, 1, last_key, kshift, kq);
+    tile_kscales_for<KT>(ksc, 1, last_key, kshift, kq);
   }
   __syncthreads();
   // V(1) is copied by iteration 0, after its barrier.  Nothing is in flight when the
@@ -814,8 +817,8 @@ __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void
     if constexpr (VARIANT >= 2) {
       cn[0] = cn[1] = a.kscale;
     } else {
-      cn[0] = dqs * kscale_of(kq, 0, h);  // tile t+1
-      cn[1] = dqs * kscale_of(kq, 1, h);
+      cn[0] = dqs * (KT ? kq[0] : kscale_of(kq, 0, h));  // tile t+1
+      cn[1] = dqs * (KT ? kq[0] : kscale_of(kq, 1, h));
     }
     if (t + 2 < T) copy.k_tile(krs, t + 2, sKc);
     if (SMOOTHQ && t + 1 < T)
@@ -882,7 +885,7 @@ __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void
     if constexpr (VARIANT >= 2)
       mx_kscales(t + 2, kw);
     else
-      tile_kscales(ksc, t + 2, last_key, kshift, kq);
+      tile_kscales_for<KT>(ksc, t + 2, last_key, kshift, kq);
     if (t < T) {
       wait_copies();
       __syncthreads();
@@ -971,6 +974,12 @@ __global__ __launch_bounds__(64 * kDbgWaves) void debug_qk_kernel(const int8_t* 
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ = false, bool TRAIN = false>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
   const int grid = a.G * ((a.Np + kAttnRows - 1) / kAttnRows);
+  if constexpr (VARIANT == 0 && !SMOOTHQ && FUSEQ) {
+    if (a.blk_k >= kTileKV) {
+      attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ, FUSEQ, TRAIN, true><<<grid, kAttnThreads, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
   attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ, FUSEQ, TRAIN><<<grid, kAttnThreads, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -192,6 +192,16 @@ __device__ __forceinline__ void tile_kscales(const float* ksc, int t, unsigned l
   for (int j = 0; j < 4; ++j) kq[j] = kc[min((unsigned)(t * kTileKV + 16 * j), last_key) >> kshift];
 }
 __device__ __forceinline__ float kscale_of(const float* kq, int st, int h) { return h ? kq[2 * st + 1] : kq[2 * st]; }
+// KT (blk_k >= 64, known at compile time): the tile's one K scale, in kq[0] only.
+template <bool KT>
+__device__ __forceinline__ void tile_kscales_for(const float* ksc, int t, unsigned last_key, int kshift, float* kq) {
+  if constexpr (KT) {
+    typedef const __attribute__((address_space(4))) float* const_ptr;
+    kq[0] = ((const_ptr)ksc)[min((unsigned)(t * kTileKV), last_key) >> kshift];
+  } else {
+    tile_kscales(ksc, t, last_key, kshift, kq);
+  }
+}
 // K scale of the 16 keys 16*w .. of tile t (w uniform: a scalar load).
 __device__ __forceinline__ float kscale_quarter(const float* ksc, int t, int w, unsigned last_key, int kshift) {
   typedef const __attribute__((address_space(4))) float* const_ptr;
