@@ -411,11 +411,11 @@ __device__ __forceinline__ void interleave_schedule() {
 // log-sum-exp is that of the weights themselves; O can then differ from the inference
 // forward's in its last fp16 bits.
 // KT (blk_k >= 64): one K block covers each key tile, so a tile has one K scale and every
-// lane the same c (a scalar operand), instead of one scale per 16-key quarter.
+// lane the same K factor of c (a scalar operand), instead of one scale per 16-key quarter.
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ, bool TRAIN = false, bool KT = false>
 __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void attn_kernel(AttnArgs a) {
   static_assert(!TRAIN || (VARIANT == 0 && !SMOOTHQ), "training forward: variant 0 without Q smoothing");
-  static_assert(!KT || (VARIANT == 0 && !SMOOTHQ), "one K scale per tile: variant 0 without Q smoothing");
+  static_assert(!KT || VARIANT <= 1, "one K scale per tile: INT8 scores");
   static_assert(!FUSEQ || VARIANT <= 1 || !SMOOTHQ, "in-kernel Q quantisation with Q smoothing: INT8 Q only");
   static_assert(VARIANT < 2 || !SMOOTHQ, "MXFP4 scores: no Q smoothing");
   using L = Lds<D, VARIANT>;
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(64 * kDbgWaves) void debug_qk_kernel(const int8_t* 
 template <int D, int VARIANT, bool CAUSAL, bool SMOOTHQ, bool FUSEQ = false, bool TRAIN = false>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
   const int grid = a.G * ((a.Np + kAttnRows - 1) / kAttnRows);
-  if constexpr (VARIANT == 0 && !SMOOTHQ && FUSEQ) {
+  if constexpr (VARIANT <= 1 && FUSEQ) {
     if (a.blk_k >= kTileKV) {
       attn_kernel<D, VARIANT, CAUSAL, SMOOTHQ, FUSEQ, TRAIN, true><<<grid, kAttnThreads, 0, st>>>(a);
       return hipGetLastError();
