@@ -444,13 +444,29 @@ __global__ __launch_bounds__(kAttnThreads, D == 64 && VARIANT >= 1 ? 3 : 2) void
 
   // workgroup -> (head, query tile).  Consecutive workgroup ids go round-robin over the
   // 8 XCDs; remap so each XCD walks a contiguous range of (head, tile) pairs, heads
-  // one after another, and for causal the longest tiles of a head first.
+  // one after another.  Causal query tiles differ in length (tile qt sees qt + 1 key
+  // blocks), so they go longest first across each pair of heads: walking one head's
+  // tiles after another's would start the last head's longest tiles late and leave the
+  // XCD's other workgroup slots idle at the end (about a tenth of the kernel at
+  // B=4 H=32 N=4096).  Two heads at a time keep the K/V working set of an XCD small.
   const int nqt = (a.Np + kAttnRows - 1) / kAttnRows;
   const int total = a.G * nqt;
   int vid = blockIdx.x;
   if ((total & 7) == 0) vid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int g = vid / nqt;
-  const int qt = CAUSAL ? nqt - 1 - vid % nqt : vid % nqt;
+  int g, qt;
+  if constexpr (CAUSAL) {
+    const int pair = vid / (2 * nqt), r = vid - pair * 2 * nqt;
+    if (2 * pair + 1 < a.G) {
+      g = 2 * pair + (r & 1);
+      qt = nqt - 1 - (r >> 1);
+    } else {  // odd head count: the last head alone
+      g = 2 * pair;
+      qt = nqt - 1 - r;
+    }
+  } else {
+    g = vid / nqt;
+    qt = vid % nqt;
+  }
   const int q0 = qt * kAttnRows;
   const int qw = q0 + 32 * wave;  // first row of this wave
   const int qi = qw + ql;         // this lane's query row

@@ -64,6 +64,29 @@ __device__ __forceinline__ int xcd_block(int total) {
   return (total & 7) == 0 ? (b & 7) * (total >> 3) + (b >> 3) : b;
 }
 
+// Head g and length rank of this workgroup among the nb blocks of a head (rank 0: the
+// block with the most work).  Causal blocks differ in length, so they go longest first
+// across each pair of heads: one head's blocks after another's would start the last
+// head's longest blocks late and leave the XCD's other workgroup slots idle at the end.
+// Without the mask every block is as long as the others and heads go one after another.
+template <bool CAUSAL>
+__device__ __forceinline__ void head_rank(int G, int nb, int& g, int& rank) {
+  const int vid = xcd_block(G * nb);
+  if (CAUSAL) {
+    const int pair = vid / (2 * nb), r = vid - pair * 2 * nb;
+    if (2 * pair + 1 < G) {
+      g = 2 * pair + (r & 1);
+      rank = r >> 1;
+    } else {  // odd head count: the last head alone
+      g = 2 * pair;
+      rank = r;
+    }
+  } else {
+    g = vid / nb;
+    rank = vid % nb;
+  }
+}
+
 // sigma = 2^(14 - e), 2^e the first power of two above 2 max|dO_i| max|V'_j| (1 when the bound is 0),
 // from the per-block maxima the preparation pass wrote ([nblk][2]).  Every thread of the
 // workgroup gets the same value.
@@ -276,7 +299,8 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), D == 128 ? 1 : 3) void bwd_dkdv
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int nkb = (a.Np + kKvKeys - 1) / kKvKeys;
-  const int g = xcd_block(a.G * nkb) / nkb, kb = xcd_block(a.G * nkb) % nkb;
+  int g, kb;  // causal: key block kb meets the queries from kb on, so rank order is kb order
+  head_rank<CAUSAL>(a.G, nkb, g, kb);
   const int k0 = kb * kKvKeys, kw = k0 + 32 * wave, key = kw + (lane & 31);
   const int N = a.N, Np = a.Np;
   const bool has_keys = kw < Np;  // kw and Np are multiples of 32
@@ -452,7 +476,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, ql = lane & 31;
   const int nqt = a.Np / kBwdRows;
-  const int g = xcd_block(a.G * nqt) / nqt, qt = xcd_block(a.G * nqt) % nqt;
+  int g, qt;  // causal: query tile qt meets the keys up to its own, so the longest is the last
+  head_rank<CAUSAL>(a.G, nqt, g, qt);
+  if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBwdRows, qw = q0 + 32 * wave, qi = qw + ql;
   const int N = a.N, Np = a.Np;
 
