@@ -83,6 +83,8 @@ CASES = [
     ("n1000_causal_d128", 5, dict(N=1000, B=1, H=2), 1, 128, 64),
     ("n1_d128", 2, dict(N=1, B=1, H=2), 0, 128, 64),
     ("n777_d64_blk128", 4, dict(N=777, B=2, H=1), 0, 128, 128),
+    # causal blocks go longest first across pairs of heads; the third head goes alone
+    ("odd_heads_causal_d128", 2, dict(N=1000, B=1, H=3), 1, 128, 64),
 ]
 
 

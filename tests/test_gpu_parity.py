@@ -371,6 +371,10 @@ EDGE = [
     ("peaked_n2100_d64", 3, dict(N=2100, B=1, H=2), dict(causal=0, variant=0)),
     ("peaked_n2100_d64_seed2", 3, dict(N=2100, B=1, H=2, seed=2), dict(causal=0, variant=0)),
     ("peaked_n3000_causal_d64", 3, dict(N=3000, B=1, H=2, seed=1), dict(causal=1, variant=0)),
+    # causal query tiles go longest first across pairs of heads; an odd head count leaves
+    # the last head alone (24 workgroups: also through the XCD remap; 27: without it)
+    ("odd_heads_causal_d128", 2, dict(N=1000, B=1, H=3), dict(causal=1, variant=0)),
+    ("odd_heads_causal_d64_v1", 3, dict(N=1100, B=1, H=3), dict(causal=1, variant=1)),
     # MXFP4 scores (variant 2)
     ("mx_n1_causal", 5, dict(N=1, B=1, H=1), dict(causal=1, variant=2, smooth_q=0)),
     ("mx_n17_d64", 1, dict(N=17, B=1, H=2), dict(causal=0, variant=2, smooth_q=0)),
